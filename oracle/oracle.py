@@ -1,0 +1,183 @@
+"""Python face of the fp64 CPU oracle (gqa_oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the
+benchmark's CPU-baseline leg are the only callers allowed; the HIP library
+and its Python binding never import this module, and this module imports
+nothing from them.
+
+The oracle computes the dense softmax attention of the unified formula
+o_a = softmax(Q_a K_{g(a)}^T * scale + M) V_{g(a)} ("Attention variants"
+page, unified-notation section), row by row in fp64, with the query position
+offset Tk - Tq of that page's minimal semantic implementation.  See the header
+of gqa_oracle.c for the step list.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "gqa_oracle.c")
+_LIB = os.path.join(_HERE, "libgqa_oracle.so")
+
+BF16, F32, F64 = 0, 1, 2
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile gqa_oracle.c with gcc (plain -O2, IEEE semantics, OpenMP)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall", _SRC, "-o", tmp, "-lm"],
+            check=True,
+        )
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        LLP = ctypes.POINTER(ctypes.c_longlong)
+        I = ctypes.c_int
+        lib.oracle_attention.restype = I
+        lib.oracle_attention.argtypes = [
+            P, LLP, I, P, LLP, I, P, LLP, I, P,
+            I, I, I, I, I, I, I, ctypes.c_double, I, P, ctypes.c_longlong, P, P, I,
+        ]
+        lib.oracle_probs.restype = I
+        lib.oracle_probs.argtypes = [
+            P, LLP, I, P, LLP, I, P, LLP, I, P,
+            I, I, I, I, I, I, I, ctypes.c_double, I, I, I, I, P, P,
+        ]
+        lib.oracle_lse_merge.restype = None
+        lib.oracle_lse_merge.argtypes = [P, P, I, ctypes.c_longlong, I, P, P]
+        lib.oracle_max_threads.restype = I
+        lib.oracle_max_threads.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+class _Operand:
+    """A 4-D input seen as (pointer, element strides, storage code)."""
+
+    def __init__(self, x):
+        self.keep = x
+        try:
+            import torch
+        except ImportError:  # pragma: no cover
+            torch = None
+        if torch is not None and isinstance(x, torch.Tensor):
+            if x.device.type != "cpu":
+                raise ValueError("oracle operands must live in host memory")
+            if x.dim() != 4:
+                raise ValueError("oracle operands are 4-D (b, h, t, d)")
+            codes = {torch.bfloat16: BF16, torch.float32: F32, torch.float64: F64}
+            if x.dtype not in codes:
+                raise ValueError(f"unsupported oracle dtype {x.dtype}")
+            self.code = codes[x.dtype]
+            self.ptr = x.data_ptr()
+            self.strides = (ctypes.c_longlong * 4)(*x.stride())
+            self.shape = tuple(x.shape)
+            return
+        a = np.asarray(x)
+        if a.ndim != 4:
+            raise ValueError("oracle operands are 4-D (b, h, t, d)")
+        codes = {np.dtype(np.float32): F32, np.dtype(np.float64): F64}
+        if a.dtype not in codes:
+            raise ValueError(f"unsupported oracle dtype {a.dtype}")
+        self.keep = a
+        self.code = codes[a.dtype]
+        self.ptr = a.ctypes.data
+        self.strides = (ctypes.c_longlong * 4)(*(s // a.itemsize for s in a.strides))
+        self.shape = a.shape
+
+
+def _lens_arg(kv_lens, B):
+    if kv_lens is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(kv_lens, dtype=np.int32))
+    if arr.shape != (B,):
+        raise ValueError("kv_lens must have one entry per sequence")
+    return arr, arr.ctypes.data
+
+
+def attention(q, k, v, scale: float, causal: bool, kv_lens=None, rows=None, threads: int = 0,
+              with_lse: bool = False):
+    """fp64 attention.  q [B,Hq,Tq,Dk], k [B,Hkv,Tk,Dk], v [B,Hkv,Tk,Dv].
+
+    kv_lens: optional per-sequence key counts (a decode cache of capacity Tk);
+    rows: optional flat row ids ((b*Hq)+a)*Tq+i to compute only those rows.
+    Returns out [B,Hq,Tq,Dv] (or [len(rows), Dv]) in fp64, plus lse if asked.
+    """
+    Q, K, V = _Operand(q), _Operand(k), _Operand(v)
+    B, Hq, Tq, Dk = Q.shape
+    Bk, Hkv, Tk, Dk2 = K.shape
+    Bv, Hkv2, Tk2, Dv = V.shape
+    if not (B == Bk == Bv and Hkv == Hkv2 and Tk == Tk2 and Dk == Dk2):
+        raise ValueError("inconsistent q/k/v shapes")
+    lens, lens_ptr = _lens_arg(kv_lens, B)
+    if rows is None:
+        out = np.empty((B, Hq, Tq, Dv), dtype=np.float64)
+        lse = np.empty((B, Hq, Tq), dtype=np.float64)
+        rows_arr, rows_ptr, nrows = None, None, 0
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows_arr.size
+        out = np.empty((nrows, Dv), dtype=np.float64)
+        lse = np.empty((nrows,), dtype=np.float64)
+        rows_ptr = rows_arr.ctypes.data
+    rc = _load().oracle_attention(
+        Q.ptr, Q.strides, Q.code, K.ptr, K.strides, K.code, V.ptr, V.strides, V.code, lens_ptr,
+        B, Hq, Hkv, Tq, Tk, Dk, Dv, float(scale), int(bool(causal)), rows_ptr, nrows,
+        out.ctypes.data, lse.ctypes.data, int(threads),
+    )
+    if rc != 0:
+        raise ValueError("oracle rejected the problem (shapes, head grouping or Tq > Tk with causal)")
+    return (out, lse) if with_lse else out
+
+
+def probs(q, k, v, scale: float, causal: bool, b: int, a: int, i: int, kv_lens=None):
+    """The probability row P_j over all Tk keys (zeros where masked) and the output row."""
+    Q, K, V = _Operand(q), _Operand(k), _Operand(v)
+    B, Hq, Tq, Dk = Q.shape
+    _, Hkv, Tk, _ = K.shape
+    Dv = V.shape[3]
+    lens, lens_ptr = _lens_arg(kv_lens, B)
+    p = np.empty((Tk,), dtype=np.float64)
+    o = np.empty((Dv,), dtype=np.float64)
+    rc = _load().oracle_probs(
+        Q.ptr, Q.strides, Q.code, K.ptr, K.strides, K.code, V.ptr, V.strides, V.code, lens_ptr,
+        B, Hq, Hkv, Tq, Tk, Dk, Dv, float(scale), int(bool(causal)), b, a, i,
+        p.ctypes.data, o.ctypes.data,
+    )
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+    return p, o
+
+
+def lse_merge(o_parts, lse_parts):
+    """Exact merge of partial results over disjoint key ranges.
+
+    o_parts [S, R, Dv], lse_parts [S, R] (natural log, -inf for empty parts).
+    """
+    o_parts = np.ascontiguousarray(o_parts, dtype=np.float64)
+    lse_parts = np.ascontiguousarray(lse_parts, dtype=np.float64)
+    S, R, Dv = o_parts.shape
+    out = np.empty((R, Dv), dtype=np.float64)
+    lse = np.empty((R,), dtype=np.float64)
+    _load().oracle_lse_merge(o_parts.ctypes.data, lse_parts.ctypes.data, S, R, Dv,
+                             out.ctypes.data, lse.ctypes.data)
+    return out, lse

@@ -1,0 +1,355 @@
+"""Pins for the fp64 oracle: facts fixed by the pages and by mathematics.
+
+Each test checks the oracle against something other than its own formula:
+the worked example the "Attention variants" page prints, invariants the
+pages state (decode equals the last row of the causal prefill, softmax rows
+sum to one, future keys get no weight, MHA/MQA are limits of GQA), closed
+forms, and PyTorch's own scaled-dot-product attention run on the CPU in
+float64 as an independent library routine.  A plausible slip anywhere in the
+oracle (dropped scale, wrong head index, square mask on a suffix, a
+transposed operand, a missing normaliser) fails at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *rest = line.split()
+            vals[key] = [float(x) for x in rest]
+    return vals
+
+
+def _rand(shape, seed, dtype=torch.float64):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return torch.randn(*shape, generator=g, dtype=torch.float64).to(dtype)
+
+
+# ---------------------------------------------------------------- worked example
+
+def test_head_mapping_worked_example():
+    """The page's head-mapping self-test: q=k=0, v=[1,7] per KV head -> [1,1,7,7]."""
+    g = _read_golden("head_mapping_attention_variants.txt")
+    q = np.array(g["q_values"]).reshape([int(x) for x in g["q_shape"]])
+    k = np.array(g["k_values"]).reshape([int(x) for x in g["k_shape"]])
+    v = np.array(g["v_values"]).reshape([int(x) for x in g["v_shape"]])
+    out = O.attention(q, k, v, 1.0 / math.sqrt(q.shape[-1]), True)
+    assert out.ravel().tolist() == g["expected"]
+
+
+@pytest.mark.parametrize("Hq,vals,expected", [
+    (8, [1.0, 7.0], [1, 1, 1, 1, 7, 7, 7, 7]),
+    (8, [1.0, 3.0, 5.0, 7.0], [1, 1, 3, 3, 5, 5, 7, 7]),
+    (4, [1.0, 3.0, 5.0, 7.0], [1, 3, 5, 7]),
+    (4, [2.0], [2, 2, 2, 2]),
+])
+def test_head_mapping_extensions(Hq, vals, expected):
+    Hkv = len(vals)
+    q = np.zeros((1, Hq, 1, 1))
+    k = np.zeros((1, Hkv, 1, 1))
+    v = np.array(vals).reshape(1, Hkv, 1, 1)
+    assert O.attention(q, k, v, 1.0, True).ravel().tolist() == [float(x) for x in expected]
+
+
+# ---------------------------------------------------------------- stated invariants
+
+def test_decode_is_last_row_pages_self_test_shapes():
+    """The page's self-test: q (2,4,5,8), k,v (2,2,5,8) from seed 0; one-step decode
+    equals the last row of the full causal output, and the output has q's shape."""
+    torch.manual_seed(0)
+    q = torch.randn(2, 4, 5, 8).double()
+    k, v = torch.randn(2, 2, 5, 8).double(), torch.randn(2, 2, 5, 8).double()
+    full = O.attention(q, k, v, 1 / math.sqrt(8), True)
+    step = O.attention(q[:, :, -1:].contiguous(), k, v, 1 / math.sqrt(8), True)
+    assert full.shape == tuple(q.shape)
+    np.testing.assert_allclose(step, full[:, :, -1:], rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("Tq", [1, 2, 7, 16, 33])
+def test_suffix_queries_match_rows_of_full_prefill(Tq):
+    """Queries at positions Tk-Tq..Tk-1 see the same keys as those rows of the full
+    causal prefill (a square mask applied to a suffix would fail this)."""
+    Tk = 33
+    q = _rand((2, 6, Tk, 16), 1)
+    k = _rand((2, 3, Tk, 16), 2)
+    v = _rand((2, 3, Tk, 12), 3)
+    full = O.attention(q, k, v, 0.25, True)
+    suf = O.attention(q[:, :, Tk - Tq:].contiguous(), k, v, 0.25, True)
+    np.testing.assert_allclose(suf, full[:, :, Tk - Tq:], rtol=0, atol=1e-14)
+
+
+def test_probabilities_sum_to_one_and_future_is_zero():
+    Tq, Tk = 9, 20
+    q = _rand((1, 4, Tq, 8), 4)
+    k = _rand((1, 2, Tk, 8), 5)
+    v = _rand((1, 2, Tk, 8), 6)
+    for a in range(4):
+        for i in range(Tq):
+            p, o = O.probs(q, k, v, 0.5, True, 0, a, i)
+            pos = Tk - Tq + i
+            assert abs(p.sum() - 1.0) < 1e-12
+            assert np.all(p[pos + 1:] == 0.0)
+            assert np.all(p[: pos + 1] > 0.0)
+            # the output row is the probability-weighted sum of the KV head's values
+            g = a // 2
+            np.testing.assert_allclose(o, p @ v[0, g].numpy(), rtol=0, atol=1e-12)
+
+
+def test_future_keys_and_values_have_no_effect():
+    Tq = Tk = 24
+    q = _rand((2, 4, Tq, 8), 7)
+    k = _rand((2, 2, Tk, 8), 8)
+    v = _rand((2, 2, Tk, 8), 9)
+    base = O.attention(q, k, v, 0.3, True)
+    for i in [0, 5, 17]:
+        k2, v2 = k.clone(), v.clone()
+        k2[:, :, i + 1:] = _rand(k2[:, :, i + 1:].shape, 10 + i) * 50
+        v2[:, :, i + 1:] = _rand(v2[:, :, i + 1:].shape, 20 + i) * 50
+        out = O.attention(q, k2, v2, 0.3, True)
+        np.testing.assert_array_equal(out[:, :, : i + 1], base[:, :, : i + 1])
+
+
+def test_decode_lengths_ignore_cache_tail():
+    """A decode cache of capacity Tmax with len_b valid keys: the slots past len_b
+    (here NaN) never reach the output, and the result equals a fresh forward over
+    exactly len_b keys with the query at position len_b - 1."""
+    B, Hq, Hkv, Tmax, D = 3, 4, 2, 40, 8
+    q = _rand((B, Hq, 1, D), 11)
+    k = _rand((B, Hkv, Tmax, D), 12)
+    v = _rand((B, Hkv, Tmax, D), 13)
+    lens = [1, 17, 40]
+    for b, n in enumerate(lens):
+        k[b, :, n:] = float("nan")
+        v[b, :, n:] = float("nan")
+    out = O.attention(q, k, v, 0.4, True, kv_lens=lens)
+    assert np.isfinite(out).all()
+    for b, n in enumerate(lens):
+        ref = O.attention(q[b:b + 1], k[b:b + 1, :, :n].contiguous(), v[b:b + 1, :, :n].contiguous(),
+                          0.4, True)
+        np.testing.assert_array_equal(out[b:b + 1], ref)
+
+
+def test_gqa_equals_mha_on_expanded_kv_and_mqa_limit():
+    """GQA is MHA run on K/V whose heads are repeated G times (the expansion is a
+    copy, not arithmetic); MQA is the Hkv=1 limit."""
+    B, Hq, T, D = 2, 8, 13, 8
+    q = _rand((B, Hq, T, D), 14)
+    for Hkv in [1, 2, 4, 8]:
+        k = _rand((B, Hkv, T, D), 15 + Hkv)
+        v = _rand((B, Hkv, T, D), 25 + Hkv)
+        G = Hq // Hkv
+        ke = k.repeat_interleave(G, dim=1).contiguous()
+        ve = v.repeat_interleave(G, dim=1).contiguous()
+        np.testing.assert_array_equal(O.attention(q, k, v, 0.35, True), O.attention(q, ke, ve, 0.35, True))
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_zero_query_gives_prefix_mean():
+    """q = 0 makes every visible key equally likely: o_i = mean(v[0..p_i])."""
+    Tq, Tk = 7, 19
+    q = torch.zeros((1, 2, Tq, 4), dtype=torch.float64)
+    k = _rand((1, 1, Tk, 4), 30)
+    v = _rand((1, 1, Tk, 5), 31)
+    out = O.attention(q, k, v, 1.0, True)
+    csum = np.cumsum(v[0, 0].numpy(), axis=0)
+    for i in range(Tq):
+        pos = Tk - Tq + i
+        np.testing.assert_allclose(out[0, 0, i], csum[pos] / (pos + 1), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(out[0, 1, i], csum[pos] / (pos + 1), rtol=0, atol=1e-13)
+
+
+def test_single_key_and_constant_values():
+    q = _rand((2, 4, 1, 6), 32)
+    k = _rand((2, 2, 1, 6), 33)
+    v = _rand((2, 2, 1, 3), 34)
+    out = O.attention(q, k, v, 0.7, True)
+    np.testing.assert_array_equal(out, v.repeat_interleave(2, dim=1).numpy())
+    # V == 1 everywhere gives an all-ones output for any scores
+    q = _rand((2, 4, 11, 6), 35)
+    k = _rand((2, 2, 11, 6), 36)
+    ones = torch.ones((2, 2, 11, 3), dtype=torch.float64)
+    np.testing.assert_allclose(O.attention(q, k, ones, 0.9, True), 1.0, rtol=0, atol=1e-14)
+
+
+def test_identical_keys_noncausal_is_mean_of_values():
+    k = _rand((1, 1, 1, 6), 37).repeat(1, 1, 10, 1).contiguous()
+    q = _rand((1, 3, 4, 6), 38)
+    v = _rand((1, 1, 10, 7), 39)
+    out = O.attention(q, k, v, 0.5, False)
+    np.testing.assert_allclose(out, np.broadcast_to(v.numpy().mean(axis=2, keepdims=True), out.shape),
+                               rtol=0, atol=1e-13)
+
+
+def test_dominant_key_selects_its_value():
+    """One key aligned with the query and scaled far above the rest takes all the
+    weight; a dropped scale or sign error would not."""
+    D, Tk = 8, 12
+    q = torch.zeros((1, 1, 1, D), dtype=torch.float64)
+    q[..., 0] = 1.0
+    k = _rand((1, 1, Tk, D), 40) * 0.1
+    k[0, 0, 5, 0] = 400.0
+    v = _rand((1, 1, Tk, 4), 41)
+    out = O.attention(q, k, v, 0.5, False)
+    np.testing.assert_allclose(out[0, 0, 0], v[0, 0, 5].numpy(), rtol=0, atol=1e-12)
+    # with a negative alignment the same key gets no weight at all
+    k[0, 0, 5, 0] = -400.0
+    p, _ = O.probs(q, k, v, 0.5, False, 0, 0, 0)
+    assert p[5] < 1e-80
+
+
+def test_scale_enters_only_as_product_with_scores():
+    q = _rand((1, 2, 5, 8), 42)
+    k = _rand((1, 1, 9, 8), 43)
+    v = _rand((1, 1, 9, 8), 44)
+    a = O.attention(q, k, v, 0.5, True)
+    b = O.attention(q * 2.0, k, v, 0.25, True)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
+
+
+def test_linearity_in_values():
+    q = _rand((1, 4, 6, 8), 45)
+    k = _rand((1, 2, 10, 8), 46)
+    v = _rand((1, 2, 10, 8), 47)
+    w = _rand((1, 2, 10, 8), 48)
+    lhs = O.attention(q, k, 2.0 * v - 3.0 * w, 0.3, True)
+    rhs = 2.0 * O.attention(q, k, v, 0.3, True) - 3.0 * O.attention(q, k, w, 0.3, True)
+    np.testing.assert_allclose(lhs, rhs, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- library routine
+
+def _sdpa_reference(q, k, v, scale, causal):
+    """torch's scaled_dot_product_attention, CPU float64, with the query offset
+    Tk - Tq expressed as an explicit boolean mask."""
+    Tq, Tk = q.shape[2], k.shape[2]
+    mask = None
+    if causal:
+        qpos = torch.arange(Tk - Tq, Tk)[:, None]
+        kpos = torch.arange(Tk)[None, :]
+        mask = kpos <= qpos
+    return F.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=scale,
+                                          enable_gqa=(q.shape[1] != k.shape[1]))
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Tq,Tk,Dk,Dv,causal", [
+    (1, 4, 2, 17, 17, 16, 16, True),     # square causal GQA, ragged length
+    (2, 8, 2, 5, 29, 16, 16, True),      # suffix queries (decode-like chunk)
+    (2, 6, 6, 1, 31, 8, 8, True),        # MHA single-step decode
+    (1, 8, 1, 9, 40, 32, 32, True),      # MQA suffix
+    (2, 4, 2, 12, 7, 16, 16, False),     # cross attention, Tq > Tk
+    (1, 8, 1, 1, 23, 72, 64, True),      # absorbed-MLA shape family: Dk != Dv
+])
+def test_matches_torch_sdpa_float64(B, Hq, Hkv, Tq, Tk, Dk, Dv, causal):
+    q = _rand((B, Hq, Tq, Dk), 50)
+    k = _rand((B, Hkv, Tk, Dk), 51)
+    v = _rand((B, Hkv, Tk, Dv), 52)
+    scale = 1.0 / math.sqrt(Dk) * 1.3
+    ours = O.attention(q, k, v, scale, causal)
+    ref = _sdpa_reference(q, k, v, scale, causal).numpy()
+    np.testing.assert_allclose(ours, ref, rtol=0, atol=1e-12)
+
+
+def test_mla_value_is_latent_view_of_key():
+    """Absorbed MLA decode: one 576-wide key = [512 latent | 64 rope]; the value is the
+    latent part.  The score is the latent dot plus the rope dot, so splitting the
+    query/key into the two parts and summing the two score matrices must give the
+    same attention as the single wide dot."""
+    B, Hq, T = 2, 8, 19
+    q = _rand((B, Hq, 1, 576), 53)
+    kc = _rand((B, 1, T, 576), 54)
+    v = kc[..., :512]
+    scale = 1.0 / math.sqrt(192)
+    ours = O.attention(q, kc, v, scale, True)
+    # independent route: scores as latent-dot + rope-dot, softmax via torch, sum via matmul
+    s_lat = torch.einsum("bhqd,bkd->bhqk", q[..., :512], kc[:, 0, :, :512])
+    s_rope = torch.einsum("bhqd,bkd->bhqk", q[..., 512:], kc[:, 0, :, 512:])
+    p = torch.softmax((s_lat + s_rope) * scale, dim=-1)
+    ref = torch.einsum("bhqk,bkd->bhqd", p, kc[:, 0, :, :512]).numpy()
+    np.testing.assert_allclose(ours, ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- split-KV merge
+
+@pytest.mark.parametrize("cuts", [[0, 64], [0, 1, 64], [0, 20, 21, 50, 64], list(range(0, 65, 8))])
+def test_lse_merge_of_partitions_equals_full(cuts):
+    """Attention over all keys equals the log-sum-exp merge of attention over any
+    partition of the keys (non-causal, so each part is a plain slice)."""
+    q = _rand((1, 4, 3, 16), 60)
+    k = _rand((1, 2, 64, 16), 61)
+    v = _rand((1, 2, 64, 16), 62)
+    full, full_lse = O.attention(q, k, v, 0.25, False, with_lse=True)
+    parts, lses = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        o, l = O.attention(q, k[:, :, a:b].contiguous(), v[:, :, a:b].contiguous(), 0.25, False,
+                           with_lse=True)
+        parts.append(o.reshape(-1, 16))
+        lses.append(l.reshape(-1))
+    merged, merged_lse = O.lse_merge(np.stack(parts), np.stack(lses))
+    np.testing.assert_allclose(merged, full.reshape(-1, 16), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(merged_lse, full_lse.reshape(-1), rtol=0, atol=1e-13)
+
+
+def test_lse_is_log_of_partition_function():
+    q = _rand((1, 2, 1, 8), 63)
+    k = _rand((1, 1, 10, 8), 64)
+    v = _rand((1, 1, 10, 8), 65)
+    _, lse = O.attention(q, k, v, 0.5, False, with_lse=True)
+    s = (q[0, :, 0] @ k[0, 0].T) * 0.5
+    np.testing.assert_allclose(lse.ravel(), torch.logsumexp(s, dim=-1).numpy(), rtol=0, atol=1e-13)
+    # an empty part merges as nothing
+    merged, _ = O.lse_merge(np.stack([np.ones((1, 3)), np.full((1, 3), 5.0)]),
+                            np.stack([np.array([0.0]), np.array([-np.inf])]))
+    np.testing.assert_array_equal(merged, np.ones((1, 3)))
+
+
+def test_empty_visible_set_is_zero_row():
+    q = _rand((2, 2, 1, 4), 66)
+    k = _rand((2, 1, 5, 4), 67)
+    v = _rand((2, 1, 5, 4), 68)
+    out, lse = O.attention(q, k, v, 1.0, True, kv_lens=[0, 3], with_lse=True)
+    assert np.all(out[0] == 0.0) and np.all(np.isneginf(lse[0]))
+    assert np.all(np.isfinite(out[1]))
+
+
+def test_bf16_inputs_are_widened_exactly():
+    x = _rand((1, 2, 6, 8), 69, torch.float32).to(torch.bfloat16)
+    k = _rand((1, 1, 6, 8), 70, torch.float32).to(torch.bfloat16)
+    v = _rand((1, 1, 6, 8), 71, torch.float32).to(torch.bfloat16)
+    a = O.attention(x, k, v, 0.3, True)
+    b = O.attention(x.double(), k.double(), v.double(), 0.3, True)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_rows_subset_matches_full():
+    q = _rand((2, 4, 9, 8), 72)
+    k = _rand((2, 2, 12, 8), 73)
+    v = _rand((2, 2, 12, 8), 74)
+    full = O.attention(q, k, v, 0.4, True).reshape(-1, 8)
+    rows = [0, 5, 17, 35, 71]
+    np.testing.assert_array_equal(O.attention(q, k, v, 0.4, True, rows=rows), full[rows])
+
+
+def test_rejects_bad_problems():
+    q = np.zeros((1, 3, 2, 4))
+    k = np.zeros((1, 2, 2, 4))
+    with pytest.raises(ValueError):
+        O.attention(q, k, k, 1.0, True)  # Hq % Hkv != 0
+    q = np.zeros((1, 2, 5, 4))
+    k = np.zeros((1, 1, 3, 4))
+    with pytest.raises(ValueError):
+        O.attention(q, k, k, 1.0, True)  # causal with Tq > Tk

@@ -1,0 +1,109 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module only draws inputs: it holds none of the attention arithmetic, so
+that the HIP path and the fp64 oracle can both be fed from it without sharing
+any computation.
+
+Recipe (the same for every workload and size):
+  * a CPU ``torch.Generator`` seeded with the workload's seed draws q, then k,
+    then v with ``randn`` in fp32 (N(0,1)), each cast by round-to-nearest-even
+    to the workload's storage type (bf16 or fp32);
+  * decode lengths come from a second CPU generator seeded with seed + 1000:
+    ``randint(lo, hi + 1, (B,))``, i.e. uniform on [lo, hi] inclusive;
+  * decode caches have capacity Tmax; for parity runs every cache slot at a
+    position >= len_b is overwritten with NaN, because those slots are not
+    part of the input and must not reach the output;
+  * the weight-absorbed MLA shape draws only q and k: the value is the first
+    512 columns of the 576-wide key (latent 512 + rope 64), taken as a view.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field, replace
+
+import torch
+
+_DT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str  # "fwd", "decode", "mla_decode", "fwd+decode"
+    B: int
+    Hq: int
+    Hkv: int
+    Tq: int
+    Tk: int  # forward: key length; decode: cache capacity Tmax
+    Dk: int
+    Dv: int
+    dtype: str
+    seed: int
+    scale: float
+    causal: bool = True
+    len_lo: int = 0  # decode lengths, inclusive range
+    len_hi: int = 0
+    extra: dict = field(default_factory=dict)
+
+    def scaled(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+# The five workloads of the headline comparison.
+TINY_F32 = Workload("tiny_fp32_gqa_b1_hq4_hkv2_t128_d64", "fwd+decode", 1, 4, 2, 128, 128, 64, 64,
+                    "f32", 0, 1.0 / 8.0, len_lo=128, len_hi=128)
+GQA_PREFILL = Workload("gqa_prefill_b4_hq32_hkv8_t4096_d128", "fwd", 4, 32, 8, 4096, 4096, 128, 128,
+                       "bf16", 1, 1.0 / math.sqrt(128))
+GQA_DECODE = Workload("gqa_decode_b64_hq32_hkv8_tmax8192_d128", "decode", 64, 32, 8, 1, 8192, 128, 128,
+                      "bf16", 2, 1.0 / math.sqrt(128), len_lo=1024, len_hi=8192)
+MQA_SUFFIX = Workload("mqa_suffix_prefill_b8_hq64_hkv1_tq512_tk16384_d128", "fwd", 8, 64, 1, 512, 16384,
+                      128, 128, "bf16", 3, 1.0 / math.sqrt(128))
+MLA_DECODE = Workload("mla_absorbed_decode_b16_hq128_tk32768_dk576_dv512", "mla_decode", 16, 128, 1, 1,
+                      32768, 576, 512, "bf16", 4, 1.0 / math.sqrt(192), len_lo=32768, len_hi=32768)
+
+ALL = [TINY_F32, GQA_PREFILL, GQA_DECODE, MQA_SUFFIX, MLA_DECODE]
+
+
+def _randn(gen: torch.Generator, shape, dtype: str) -> torch.Tensor:
+    return torch.randn(*shape, generator=gen, dtype=torch.float32).to(_DT[dtype])
+
+
+def fwd_inputs(w: Workload):
+    """q [B,Hq,Tq,Dk], k [B,Hkv,Tk,Dk], v [B,Hkv,Tk,Dv] on the CPU."""
+    g = torch.Generator("cpu").manual_seed(w.seed)
+    q = _randn(g, (w.B, w.Hq, w.Tq, w.Dk), w.dtype)
+    k = _randn(g, (w.B, w.Hkv, w.Tk, w.Dk), w.dtype)
+    v = _randn(g, (w.B, w.Hkv, w.Tk, w.Dv), w.dtype)
+    return q, k, v
+
+
+def decode_lengths(w: Workload) -> torch.Tensor:
+    g = torch.Generator("cpu").manual_seed(w.seed + 1000)
+    return torch.randint(w.len_lo, w.len_hi + 1, (w.B,), generator=g, dtype=torch.int32)
+
+
+def _nan_tail(cache: torch.Tensor, lens: torch.Tensor) -> None:
+    for b, n in enumerate(lens.tolist()):
+        cache[b, :, n:, :] = float("nan")
+
+
+def decode_inputs(w: Workload, nan_tail: bool = True):
+    """q [B,Hq,1,Dk], k/v caches [B,Hkv,Tmax,D], lengths int32 [B] (CPU).
+
+    For the MLA shape, v is the view k[..., :Dv] of the shared latent.
+    """
+    g = torch.Generator("cpu").manual_seed(w.seed)
+    q = _randn(g, (w.B, w.Hq, 1, w.Dk), w.dtype)
+    k = _randn(g, (w.B, w.Hkv, w.Tk, w.Dk), w.dtype)
+    if w.kind == "mla_decode":
+        v = None
+    else:
+        v = _randn(g, (w.B, w.Hkv, w.Tk, w.Dv), w.dtype)
+    lens = decode_lengths(w)
+    if nan_tail:
+        _nan_tail(k, lens)
+        if v is not None:
+            _nan_tail(v, lens)
+    if v is None:
+        v = k[..., : w.Dv]
+    return q, k, v, lens
