@@ -1,0 +1,177 @@
+"""Python binding of libgqa_attn.so: causal grouped-query attention on MI355X.
+
+Argument marshalling only: every step of the attention runs in the HIP
+kernels of the library.  PyTorch supplies device memory and the current
+stream.  There is no fallback: if the library is missing, every call raises.
+
+    attention(q, k, v, scale=None, causal=True)       prefill / suffix forward
+    decode(q, k_cache, v_cache, seq_lens, scale=None) split-KV single-token decode
+
+Shapes follow the C header include/gqa_attn.h: q [B,Hq,Tq,Dk], k [B,Hkv,Tk,Dk],
+v [B,Hkv,Tk,Dv]; decode caches [B,Hkv,Tmax,D] with any element strides whose
+last dim is unit-stride (for the absorbed-MLA shape pass v_cache = k_cache[..., :512]).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "LIB_PATH", "GQA_BF16", "GQA_F32", "GQAError", "lib", "attention", "decode", "decode_splits",
+    "decode_workspace_size", "strerror",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_attn.so")
+GQA_BF16, GQA_F32 = 0, 1
+GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP = 0, -1, -2, -3, -4
+
+EXPORTS = ("gqa_attn_fwd", "gqa_attn_decode", "gqa_attn_decode_splits", "gqa_attn_decode_workspace_size",
+           "gqa_attn_strerror")
+
+_lib = None
+
+
+class GQAError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree HIP library (built by causal_grouped_query_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m causal_grouped_query_amd.build` "
+                "(there is no CPU fallback)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, LL, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.c_size_t
+        L.gqa_attn_fwd.restype = I
+        L.gqa_attn_fwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, F, I, I, P]
+        L.gqa_attn_decode_splits.restype = I
+        L.gqa_attn_decode_splits.argtypes = [I, I, I, I, I, I, I]
+        L.gqa_attn_decode_workspace_size.restype = SZ
+        L.gqa_attn_decode_workspace_size.argtypes = [I, I, I, I]
+        L.gqa_attn_decode.restype = I
+        L.gqa_attn_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, LL, LL, LL, LL, LL, LL, F, I, P, SZ,
+                                      I, P]
+        L.gqa_attn_strerror.restype = ctypes.c_char_p
+        L.gqa_attn_strerror.argtypes = [I]
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().gqa_attn_strerror(int(code)).decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return GQA_BF16
+    if t.dtype == torch.float32:
+        return GQA_F32
+    raise ValueError(f"unsupported dtype {t.dtype}: use bfloat16 or float32")
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on a HIP device (torch 'cuda')")
+
+
+def attention(q, k, v, scale: float | None = None, causal: bool = True, out=None):
+    """o = softmax(q k^T * scale + causal mask) v, KV head g(a) = a // (Hq // Hkv).
+
+    q [B,Hq,Tq,Dk], k [B,Hkv,Tk,Dk], v [B,Hkv,Tk,Dv]: contiguous, same dtype
+    (bfloat16 or float32) on one device.  Queries sit at positions Tk-Tq..Tk-1.
+    """
+    import torch
+    _check_cuda(q, k, v)
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, T, D]")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    B, Hq, Tq, Dk = q.shape
+    Bk, Hkv, Tk, Dk2 = k.shape
+    Bv, Hkv2, Tk2, Dv = v.shape
+    if not (B == Bk == Bv and Hkv == Hkv2 and Tk == Tk2 and Dk == Dk2):
+        raise ValueError("inconsistent q/k/v shapes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dk)
+    if out is None:
+        out = torch.empty((B, Hq, Tq, Dv), dtype=q.dtype, device=q.device)
+    elif out.shape != (B, Hq, Tq, Dv) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B,Hq,Tq,Dv] tensor of q's dtype")
+    rc = lib().gqa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, Tq, Tk,
+                            Dk, Dv, float(scale), int(bool(causal)), _dtype_code(q), _stream())
+    if rc != GQA_OK:
+        raise GQAError(rc, "gqa_attn_fwd")
+    return out
+
+
+def decode_splits(B: int, Hq: int, Hkv: int, Tmax: int, Dk: int, Dv: int, dtype_code: int) -> int:
+    s = lib().gqa_attn_decode_splits(B, Hq, Hkv, Tmax, Dk, Dv, dtype_code)
+    if s < 0:
+        raise GQAError(s, "gqa_attn_decode_splits")
+    return s
+
+
+def decode_workspace_size(B: int, Hq: int, Dv: int, num_splits: int) -> int:
+    return int(lib().gqa_attn_decode_workspace_size(B, Hq, Dv, num_splits))
+
+
+def decode(q, k_cache, v_cache, seq_lens, scale: float | None = None, num_splits: int = 0, out=None,
+           workspace=None):
+    """Single-token decode: q [B,Hq,1,Dk] over caches [B,Hkv,Tmax,D] holding seq_lens[b] keys.
+
+    seq_lens: int32 device tensor [B].  Cache slots at or past seq_lens[b] are
+    never read into the result.  num_splits = 0 lets the library choose.
+    """
+    import torch
+    _check_cuda(q, k_cache, v_cache, seq_lens)
+    if q.dim() != 4 or q.shape[2] != 1 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Hq, 1, Dk] tensor")
+    if k_cache.dim() != 4 or v_cache.dim() != 4:
+        raise ValueError("caches must be 4-D [B, Hkv, Tmax, D]")
+    if k_cache.stride(3) != 1 or v_cache.stride(3) != 1:
+        raise ValueError("the head dim of each cache must be unit-stride")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise ValueError("q and caches must share a dtype")
+    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 tensor [B]")
+    B, Hq, _, Dk = q.shape
+    Bk, Hkv, Tmax, Dk2 = k_cache.shape
+    Bv, Hkv2, Tmax2, Dv = v_cache.shape
+    if not (B == Bk == Bv == seq_lens.shape[0] and Hkv == Hkv2 and Tmax == Tmax2 and Dk == Dk2):
+        raise ValueError("inconsistent q / cache / seq_lens shapes")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dk)
+    S = num_splits if num_splits else decode_splits(B, Hq, Hkv, Tmax, Dk, Dv, code)
+    need = decode_workspace_size(B, Hq, Dv, S)
+    if need == 0:
+        raise GQAError(GQA_ERR_INVALID_ARG, "gqa_attn_decode_workspace_size")
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, 1, Dv), dtype=q.dtype, device=q.device)
+    elif out.shape != (B, Hq, 1, Dv) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B,Hq,1,Dv] tensor of q's dtype")
+    ks, vs = k_cache.stride(), v_cache.stride()
+    rc = lib().gqa_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                               seq_lens.data_ptr(), B, Hq, Hkv, Tmax, Dk, Dv, ks[0], ks[1], ks[2], vs[0],
+                               vs[1], vs[2], float(scale), int(S), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), code, _stream())
+    if rc != GQA_OK:
+        raise GQAError(rc, "gqa_attn_decode")
+    return out

@@ -1,0 +1,258 @@
+// api.hip -- exported C ABI of libgqa_attn.so (declared in include/gqa_attn.h).
+//
+// Every argument is validated here, on the host, before anything is
+// launched; a rejected call touches no device memory and makes no HIP call.
+#include <math.h>
+#include <stdint.h>
+
+#include "gqa_attn.h"
+#include "launch.h"
+
+#define GQA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxSplits = 1024;
+
+bool finite_nonneg(float x) { return isfinite(x) && x >= 0.f; }
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// scale * log2(e), kept strictly positive so that masked (-inf) scores stay
+// -inf after scaling; a zero scale becomes 1e-30, which leaves every weight
+// exactly equal in fp32 (uniform attention, as scale = 0 means).
+float folded_scale(float scale) { return fmaxf(scale * kLog2e, 1e-30f); }
+
+bool head_dims_fwd(int Dk, int Dv) { return Dk == Dv && (Dk == 64 || Dk == 128); }
+
+bool head_dims_decode(int Dk, int Dv, int dtype)
+{
+    if (Dk == Dv && (Dk == 64 || Dk == 128)) return true;
+    return dtype == GQA_BF16 && Dk == 576 && Dv == 512;
+}
+
+int check_common(int B, int Hq, int Hkv, int Dk, int Dv, float scale, int dtype)
+{
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || Dk <= 0 || Dv <= 0) return GQA_ERR_INVALID_ARG;
+    if (Hq % Hkv != 0) return GQA_ERR_INVALID_ARG;
+    if (!finite_nonneg(scale)) return GQA_ERR_INVALID_ARG;
+    if (dtype != GQA_BF16 && dtype != GQA_F32) return GQA_ERR_INVALID_ARG;
+    return GQA_OK;
+}
+
+int launch_status(int rc)
+{
+    if (rc != 0) return GQA_ERR_UNSUPPORTED;
+    return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
+}
+
+// Keys per split when the caller leaves the choice to the library.  The
+// choice depends only on the shape (it assumes the 256 compute units of an
+// MI355X) so that the workspace size is known before any device call.
+int default_splits(int B, int Hq, int Hkv, int Tmax, int Dk)
+{
+    const int G = Hq / Hkv;
+    long long groups;
+    int min_chunk;
+    if (Dk == 576) {
+        // absorbed MLA: a workgroup covers 128 query heads of a sequence
+        groups = (long long)B * Hkv * ((G + 127) / 128);
+        min_chunk = 256;
+        long long s = (512 + groups - 1) / groups;  // at least ~2 workgroups per CU
+        long long cap = (Tmax + min_chunk - 1) / min_chunk;
+        if (s > cap) s = cap;
+        if (s < 1) s = 1;
+        if (s > 64) s = 64;
+        return (int)s;
+    }
+    // small head dims: ~512-key chunks keep thousands of single-wave
+    // workgroups in flight and bound the imbalance of ragged lengths
+    long long s = (Tmax + 511) / 512;
+    if (s < 1) s = 1;
+    if (s > 64) s = 64;
+    return (int)s;
+}
+
+size_t ws_bytes(int B, int Hq, int Dv, int S)
+{
+    const size_t rows = (size_t)B * Hq * S;
+    size_t bytes = rows * Dv * sizeof(float) + rows * sizeof(float);
+    return (bytes + 255) & ~(size_t)255;
+}
+
+} // namespace
+
+GQA_API const char *gqa_attn_strerror(int code)
+{
+    switch (code) {
+    case GQA_OK: return "success";
+    case GQA_ERR_INVALID_ARG: return "invalid argument";
+    case GQA_ERR_UNSUPPORTED: return "unsupported head dimension / dtype combination";
+    case GQA_ERR_WORKSPACE: return "workspace missing or too small";
+    case GQA_ERR_HIP: return "HIP launch error";
+    default: return "unknown error code";
+    }
+}
+
+GQA_API int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out, int B, int Hq,
+                         int Hkv, int Tq, int Tk, int Dk, int Dv, float scale, int causal,
+                         int dtype, void *stream)
+{
+    if (!q || !k || !v || !out) return GQA_ERR_INVALID_ARG;
+    int rc = check_common(B, Hq, Hkv, Dk, Dv, scale, dtype);
+    if (rc != GQA_OK) return rc;
+    if (Tq <= 0 || Tk <= 0) return GQA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return GQA_ERR_INVALID_ARG;
+    if (causal && Tq > Tk) return GQA_ERR_INVALID_ARG;
+    if (!head_dims_fwd(Dk, Dv)) return GQA_ERR_UNSUPPORTED;
+    const int G = Hq / Hkv;
+    hipStream_t st = (hipStream_t)stream;
+
+    if (dtype == GQA_BF16) {
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 8))
+            return GQA_ERR_INVALID_ARG;
+        gqa::FwdArgs a;
+        a.q = (const uint16_t *)q;
+        a.k = (const uint16_t *)k;
+        a.v = (const uint16_t *)v;
+        a.out = (uint16_t *)out;
+        a.B = B;
+        a.Hq = Hq;
+        a.Hkv = Hkv;
+        a.Tq = Tq;
+        a.Tk = Tk;
+        a.G = G;
+        const int rows = gqa::fwd_bf16_rows_per_block();  // 128 = 4 waves x 32 rows
+        int gt = 1;
+        while (gt * 2 <= rows / 32 && G % (gt * 2) == 0) gt *= 2;
+        a.Gt = gt;
+        a.Pt = rows / gt;
+        a.n_hblk = G / gt;
+        a.n_qt = (Tq + a.Pt - 1) / a.Pt;
+        const long long units = (long long)B * Hkv * a.n_hblk;
+        if (units * a.n_qt > 0x7fffffffLL) return GQA_ERR_UNSUPPORTED;
+        a.n_units = (int)units;
+        a.causal = causal;
+        a.c = folded_scale(scale);
+        (void)hipGetLastError();
+        return launch_status(gqa::launch_fwd_bf16(a, Dk, st));
+    }
+    if (!aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(out, 4))
+        return GQA_ERR_INVALID_ARG;
+    if (Hq > 65535 || B > 65535) return GQA_ERR_UNSUPPORTED;
+    gqa::F32FwdArgs a;
+    a.q = (const float *)q;
+    a.k = (const float *)k;
+    a.v = (const float *)v;
+    a.out = (float *)out;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Tq = Tq;
+    a.Tk = Tk;
+    a.G = G;
+    a.causal = causal;
+    a.scale = scale;
+    (void)hipGetLastError();
+    return launch_status(gqa::launch_fwd_f32(a, Dk, st));
+}
+
+GQA_API int gqa_attn_decode_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int Dv, int dtype)
+{
+    int rc = check_common(B, Hq, Hkv, Dk, Dv, 1.f, dtype);
+    if (rc != GQA_OK) return rc;
+    if (Tmax <= 0) return GQA_ERR_INVALID_ARG;
+    if (!head_dims_decode(Dk, Dv, dtype)) return GQA_ERR_UNSUPPORTED;
+    return default_splits(B, Hq, Hkv, Tmax, Dk);
+}
+
+GQA_API size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_splits)
+{
+    if (B <= 0 || Hq <= 0 || Dv <= 0 || num_splits <= 0 || num_splits > kMaxSplits) return 0;
+    return ws_bytes(B, Hq, Dv, num_splits);
+}
+
+GQA_API int gqa_attn_decode(const void *q, const void *k, const void *v, void *out,
+                            const int *seq_lens, int B, int Hq, int Hkv, int Tmax, int Dk, int Dv,
+                            long long k_sb, long long k_sh, long long k_st, long long v_sb,
+                            long long v_sh, long long v_st, float scale, int num_splits,
+                            void *workspace, size_t workspace_bytes, int dtype, void *stream)
+{
+    if (!q || !k || !v || !out || !seq_lens) return GQA_ERR_INVALID_ARG;
+    int rc = check_common(B, Hq, Hkv, Dk, Dv, scale, dtype);
+    if (rc != GQA_OK) return rc;
+    if (Tmax <= 0) return GQA_ERR_INVALID_ARG;
+    if (k_sb <= 0 || k_sh <= 0 || k_st <= 0 || v_sb <= 0 || v_sh <= 0 || v_st <= 0)
+        return GQA_ERR_INVALID_ARG;
+    if (k_st < Dk || v_st < Dv) return GQA_ERR_INVALID_ARG;  // rows may not overlap
+    if (num_splits < 0 || num_splits > kMaxSplits) return GQA_ERR_INVALID_ARG;
+    if (!head_dims_decode(Dk, Dv, dtype)) return GQA_ERR_UNSUPPORTED;
+    if (dtype == GQA_BF16) {
+        if (k_sb % 8 || k_sh % 8 || k_st % 8 || v_sb % 8 || v_sh % 8 || v_st % 8)
+            return GQA_ERR_INVALID_ARG;
+        if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 8))
+            return GQA_ERR_INVALID_ARG;
+    } else {
+        if (!aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(out, 16))
+            return GQA_ERR_INVALID_ARG;
+    }
+    if (!aligned(seq_lens, 4)) return GQA_ERR_INVALID_ARG;
+
+    const int S = num_splits ? num_splits : default_splits(B, Hq, Hkv, Tmax, Dk);
+    const size_t need = ws_bytes(B, Hq, Dv, S);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return GQA_ERR_WORKSPACE;
+
+    const int G = Hq / Hkv;
+    const int tile = dtype == GQA_BF16 ? gqa::decode_bf16_key_tile() : 64;
+    int chunk = (Tmax + S - 1) / S;
+    chunk = (chunk + tile - 1) / tile * tile;
+
+    gqa::DecodeArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.lens = seq_lens;
+    a.part_o = (float *)workspace;
+    a.part_lse = (float *)workspace + (size_t)B * Hq * S * Dv;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Tmax = Tmax;
+    a.G = G;
+    a.k_sb = k_sb;
+    a.k_sh = k_sh;
+    a.k_st = k_st;
+    a.v_sb = v_sb;
+    a.v_sh = v_sh;
+    a.v_st = v_st;
+    a.S = S;
+    a.chunk = chunk;
+    hipStream_t st = (hipStream_t)stream;
+
+    if (dtype == GQA_BF16) {
+        const int hpb = gqa::decode_bf16_heads_per_block(Dk, G);
+        a.n_hblk = (G + hpb - 1) / hpb;
+        if ((long long)B * Hkv > 65535 || a.n_hblk > 65535) return GQA_ERR_UNSUPPORTED;
+        a.c = folded_scale(scale);
+        (void)hipGetLastError();
+        rc = gqa::launch_decode_bf16(a, Dk, Dv, st);
+    } else {
+        if (Hq > 65535 || B > 65535) return GQA_ERR_UNSUPPORTED;
+        a.n_hblk = 1;
+        a.c = scale;  // the fp32 path works in natural-log units
+        (void)hipGetLastError();
+        rc = gqa::launch_decode_f32(a, Dk, st);
+    }
+    if (rc != 0) return GQA_ERR_UNSUPPORTED;
+    gqa::CombineArgs c;
+    c.part_o = a.part_o;
+    c.part_lse = a.part_lse;
+    c.out = out;
+    c.B = B;
+    c.Hq = Hq;
+    c.S = S;
+    c.Dv = Dv;
+    c.out_bf16 = dtype == GQA_BF16;
+    return launch_status(gqa::launch_combine(c, st));
+}

@@ -1,0 +1,96 @@
+// device_common.h -- small gfx950 building blocks shared by the attention
+// kernels of libgqa_attn.so: MFMA wrapper, bf16 packing, the key permutation
+// that lets the score accumulator feed the PV product without a shuffle, and
+// the register transpose that stages V as V^T in LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 32x32x16 bf16 MFMA, fp32 accumulate.  Operand lane layout (both A and B):
+// lane l holds row/column (l & 31) and 8 contraction slots owned by lane
+// half (l >> 5); A and B are always filled with the same slot -> index map,
+// so the hardware's slot order inside a lane never matters.  Accumulator:
+// lane l holds column (l & 31), element e is row 8*(e>>2) + 4*(l>>5) + (e&3).
+__device__ __forceinline__ f32x16 mfma32x32x16(const u32x4 &a, const u32x4 &b, const f32x16 &c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Round-to-nearest-even fp32 -> bf16 for two values, packed lo | hi << 16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    bf16x2 p = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+// acc + sum of the 8 bf16 values packed in p (v_dot2c_f32_bf16 against 1.0).
+// Summing the rounded weights makes the normaliser match the weights the PV
+// product actually applies.
+__device__ __forceinline__ float sum_bf16x8(const u32x4 &p, float acc)
+{
+    // Note: bit-cast the whole vector.  This clang miscompiles
+    // __builtin_bit_cast applied to a single ext-vector element (it reads
+    // element 0 whatever the index).
+    const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+    const bf16x8 v = __builtin_bit_cast(bf16x8, p);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[0], v[1]}, one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[2], v[3]}, one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[4], v[5]}, one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[6], v[7]}, one, acc, false);
+    return acc;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Key permutation inside a 32-key block.  Accumulator row m of a score
+// tile S^T = K Q^T is produced by A-operand row m, which we load from key
+// kperm(m).  With kperm(m) = 16*(m>>4) + 8*((m>>2)&1) + 4*((m>>3)&1) + (m&3)
+// the 8 accumulator elements a lane holds for PV step s are the 8
+// consecutive keys 16*s + 8*(l>>5) + 0..7, i.e. the B operand of P^T V-step
+// s is the lane's own accumulator slice, and the matching A operand (V^T)
+// is one contiguous 16-byte LDS read.
+__device__ __forceinline__ int kperm(int m)
+{
+    return ((m >> 4) << 4) + (((m >> 2) & 1) << 3) + (((m >> 3) & 1) << 2) + (m & 3);
+}
+
+// Key (within a 64-key tile) of accumulator element e of score tile t held
+// by lane half `hi`.
+__device__ __forceinline__ int acc_key(int t, int e, int hi)
+{
+    return 32 * t + 16 * (e >> 3) + 8 * hi + (e & 7);
+}
+
+// Transpose a 4-key x 8-dim block of bf16 (rows r[0..3], 8 dims each) into
+// 8 dim-rows of 4 keys: out[e] holds keys 0..3 of dim e as two packed dwords.
+__device__ __forceinline__ void transpose4x8(const u32x4 r[4], u32x2 out[8])
+{
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        // dims 2w (low halves) and 2w+1 (high halves) of dword w
+        out[2 * w].x = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x05040100u);
+        out[2 * w].y = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x05040100u);
+        out[2 * w + 1].x = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x07060302u);
+        out[2 * w + 1].y = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x07060302u);
+    }
+}
+
+__device__ __forceinline__ float wave_swap_half(float x)
+{
+    // exchange with lane l ^ 32 (the other half of the wave)
+    return __shfl_xor(x, 32, 64);
+}
+
+} // namespace gqa

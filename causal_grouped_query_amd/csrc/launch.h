@@ -1,0 +1,71 @@
+// launch.h -- internal kernel argument blocks and launchers of libgqa_attn.so.
+// Host code in api.hip validates every argument before calling these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gqa {
+
+// Prefill / suffix forward (contiguous [B,H,T,D] tensors).
+struct FwdArgs {
+    const uint16_t *q;  // bf16 bits
+    const uint16_t *k;
+    const uint16_t *v;
+    uint16_t *out;
+    int B, Hq, Hkv, Tq, Tk;
+    int G;       // Hq / Hkv
+    int Gt;      // query heads per workgroup (divides G)
+    int Pt;      // query positions per workgroup (Gt * Pt = rows per workgroup)
+    int n_hblk;  // G / Gt
+    int n_qt;    // ceil(Tq / Pt)
+    int n_units; // B * Hkv * n_hblk
+    int causal;
+    float c;     // scale * log2(e), > 0
+};
+
+int launch_fwd_bf16(const FwdArgs &a, int D, hipStream_t stream);
+int fwd_bf16_rows_per_block();
+
+// Split-KV decode partials over a strided cache.
+struct DecodeArgs {
+    const void *q;       // [B, Hq, 1, Dk] contiguous
+    const void *k;       // cache, element strides below
+    const void *v;
+    const int *lens;     // device int32 [B]
+    float *part_o;       // [B, Hq, S, Dv] fp32, normalised partial outputs
+    float *part_lse;     // [B, Hq, S] fp32, base-2 log-sum-exp of scaled scores
+    int B, Hq, Hkv, Tmax, G;
+    long long k_sb, k_sh, k_st;
+    long long v_sb, v_sh, v_st;
+    int S;               // splits
+    int chunk;           // keys per split (multiple of the key tile)
+    int n_hblk;          // head blocks per KV head
+    float c;             // scale * log2(e)
+};
+
+int launch_decode_bf16(const DecodeArgs &a, int Dk, int Dv, hipStream_t stream);
+int decode_bf16_key_tile();
+int decode_bf16_heads_per_block(int Dk, int G);
+
+// fp32 VALU paths (small head dims; exactness-first).
+struct F32FwdArgs {
+    const float *q, *k, *v;
+    float *out;
+    int B, Hq, Hkv, Tq, Tk, G, causal;
+    float scale;
+};
+int launch_fwd_f32(const F32FwdArgs &a, int D, hipStream_t stream);
+int launch_decode_f32(const DecodeArgs &a, int D, hipStream_t stream);
+
+// Log-sum-exp combine of the decode partials into the output.
+struct CombineArgs {
+    const float *part_o;
+    const float *part_lse;
+    void *out;           // [B, Hq, 1, Dv], bf16 or fp32
+    int B, Hq, S, Dv;
+    int out_bf16;
+};
+int launch_combine(const CombineArgs &a, hipStream_t stream);
+
+} // namespace gqa

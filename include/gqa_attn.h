@@ -1,0 +1,132 @@
+/*
+ * gqa_attn.h -- C ABI of the MI355X (gfx950) causal grouped-query attention
+ * library, libgqa_attn.so.
+ *
+ * The operation is dense softmax attention with grouped KV heads,
+ *
+ *     o_a = softmax( Q_a K_{g(a)}^T * scale + M ) V_{g(a)},
+ *     g(a) = floor(a / (Hq / Hkv)),
+ *
+ * as written in the unified-notation section of the "Attention variants"
+ * page (wineandchord.com, 注意力家族) and, for each of the MHA / MQA / GQA
+ * limits, in the Dense Softmax family section of "Attention Architecture
+ * Evolution".  M is the causal mask: with Tq queries over Tk keys the queries
+ * sit at absolute positions Tk-Tq .. Tk-1 (the suffix-decode convention of the
+ * "Attention variants" minimal semantic implementation and its section on
+ * masks and incremental positions), and query i sees key j iff
+ * j <= Tk - Tq + i.  One entry point covers MHA (Hkv = Hq), MQA (Hkv = 1),
+ * GQA, and the weight-absorbed MLA decode shape of "Attention Architecture
+ * Evolution" (MLA section and the DSA section's absorbed equations), which is
+ * MQA over a 576-wide shared latent key whose first 512 columns are the value.
+ *
+ * Conventions for every entry point
+ *  - Pointers q, k, v, out, seq_lens and workspace are DEVICE pointers
+ *    (hipMalloc'd or torch CUDA tensors).  The caller owns all buffers; the
+ *    library never allocates, frees or synchronises.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *    default stream) and runs asynchronously.
+ *  - dtype selects the element type of q, k, v and out: GQA_BF16 (bfloat16
+ *    storage, fp32 accumulation, fp32 softmax, P rounded to bf16 for the PV
+ *    product, output rounded to nearest-even) or GQA_F32 (fp32 throughout).
+ *  - scale must be finite and >= 0 (1/sqrt(Dk) is the pages' choice; the
+ *    absorbed MLA shape uses 1/sqrt(192)).
+ *  - out must not alias any input.
+ *  - All argument checks run on the host before anything is launched; on
+ *    error nothing is enqueued and no device memory is touched.
+ *
+ * Supported head dims (anything else returns GQA_ERR_UNSUPPORTED):
+ *    gqa_attn_fwd:     (Dk, Dv) = (64, 64) or (128, 128), bf16 or fp32
+ *    gqa_attn_decode:  (64, 64) or (128, 128), bf16 or fp32;
+ *                      (576, 512) bf16 (the absorbed-MLA shape)
+ */
+#ifndef GQA_ATTN_H
+#define GQA_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GQA_BF16 = 0, GQA_F32 = 1 } gqa_dtype;
+
+enum {
+    GQA_OK = 0,
+    GQA_ERR_INVALID_ARG = -1, /* null pointer, dim <= 0, Hq % Hkv != 0, causal with
+                                 Tq > Tk, non-finite or negative scale, bad stride */
+    GQA_ERR_UNSUPPORTED = -2, /* (Dk, Dv, dtype) combination not built */
+    GQA_ERR_WORKSPACE = -3,   /* workspace null or smaller than required */
+    GQA_ERR_HIP = -4          /* a HIP launch reported an error */
+};
+
+/*
+ * Prefill / suffix forward.
+ *
+ *   q   [B, Hq,  Tq, Dk]   contiguous, row-major
+ *   k   [B, Hkv, Tk, Dk]   contiguous
+ *   v   [B, Hkv, Tk, Dv]   contiguous
+ *   out [B, Hq,  Tq, Dv]   contiguous, written in full
+ *
+ * causal = 1: query i (position Tk - Tq + i) attends to keys 0 .. Tk - Tq + i;
+ * requires Tq <= Tk (the pages' semantic implementation asserts it).
+ * causal = 0: every query attends to all Tk keys (cross attention; any Tq).
+ * Returns GQA_OK or a negative GQA_ERR_* code.
+ */
+int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv,
+                 int Tq, int Tk, int Dk, int Dv, float scale, int causal, int dtype, void *stream);
+
+/*
+ * Split count the decode entry point uses when called with num_splits = 0.
+ * It depends on the shape only (not on the device or on seq_lens), so the
+ * workspace can be sized before any device call.  Host-only; returns >= 1,
+ * or a negative GQA_ERR_* code for invalid or unsupported arguments.
+ */
+int gqa_attn_decode_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int Dv, int dtype);
+
+/*
+ * Bytes of device workspace gqa_attn_decode needs for num_splits splits
+ * (num_splits >= 1): fp32 partial outputs [B, Hq, S, Dv] and fp32 partial
+ * log-sum-exp values [B, Hq, S].  Returns 0 for invalid arguments.
+ */
+size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_splits);
+
+/*
+ * Single-token decode over a KV cache, split over the key axis with a
+ * log-sum-exp combine (flash-decoding style; the pages describe decode as
+ * bound by reading the KV stream, and the online-softmax merge of partial
+ * blocks as exact up to rounding).
+ *
+ *   q        [B, Hq, 1, Dk]  contiguous
+ *   k, v     KV cache: element (b, h, t, d) at k[b*k_sb + h*k_sh + t*k_st + d]
+ *            (element strides; d is unit-stride; t < Tmax).  For the
+ *            absorbed-MLA shape pass v = k with the same strides and
+ *            Dv = 512 < Dk = 576: the value is the latent prefix of each key.
+ *            Strides must be multiples of 8 elements and the base pointers
+ *            16-byte aligned.
+ *   out      [B, Hq, 1, Dv]  contiguous
+ *   seq_lens device int32[B]: sequence b has keys 0 .. seq_lens[b]-1 and its
+ *            query sits at position seq_lens[b]-1 (sees all of them).  Values
+ *            are read on the device: 0 gives a zero output row; values above
+ *            Tmax are clamped to Tmax.  Cache slots at t >= seq_lens[b] are
+ *            never read into the result (they may hold anything, NaN included).
+ *   num_splits  number of key-axis splits, 1 .. 1024, or 0 for the value of
+ *            gqa_attn_decode_splits().
+ *   workspace   device buffer of at least
+ *            gqa_attn_decode_workspace_size(B, Hq, Dv, splits) bytes, 256-byte
+ *            aligned; contents on entry are ignored.  Two calls that share a
+ *            workspace must be ordered on one stream.
+ */
+int gqa_attn_decode(const void *q, const void *k, const void *v, void *out, const int *seq_lens,
+                    int B, int Hq, int Hkv, int Tmax, int Dk, int Dv, long long k_sb, long long k_sh,
+                    long long k_st, long long v_sb, long long v_sh, long long v_st, float scale,
+                    int num_splits, void *workspace, size_t workspace_bytes, int dtype,
+                    void *stream);
+
+/* Static, thread-safe description of a GQA_* return code. */
+const char *gqa_attn_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_ATTN_H */

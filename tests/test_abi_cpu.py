@@ -1,0 +1,115 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every entry point include/gqa_attn.h
+declares, and reject bad arguments on the host with the documented codes
+before anything touches the device.  Pointers here are fake but aligned
+addresses: a rejected call never dereferences them, and no call below is a
+valid one (a valid call would launch a kernel).
+"""
+import os
+import re
+
+import pytest
+
+import causal_grouped_query_amd as gqa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gqa_attn.h")
+
+FAKE = 0x10000  # aligned stand-in address; never dereferenced
+BF16, F32 = gqa.GQA_BF16, gqa.GQA_F32
+INVALID, UNSUP, WS = gqa.GQA_ERR_INVALID_ARG, gqa.GQA_ERR_UNSUPPORTED, gqa.GQA_ERR_WORKSPACE
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gqa_attn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    import subprocess
+    declared = _declared_functions()
+    assert set(declared) == set(gqa.EXPORTS)
+    L = gqa.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    nm = subprocess.run(["nm", "-D", "--defined-only", gqa.LIB_PATH], capture_output=True, text=True,
+                        check=True).stdout
+    exported = set(re.findall(r"\bT (gqa_attn_\w+)", nm))
+    assert exported == set(declared)
+
+
+def test_strerror_strings():
+    assert gqa.strerror(0) == "success"
+    for code in (INVALID, UNSUP, WS, gqa.GQA_ERR_HIP):
+        assert gqa.strerror(code) and gqa.strerror(code) != "unknown error code"
+    assert gqa.strerror(-99) == "unknown error code"
+
+
+def _fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, B=1, Hq=4, Hkv=2, Tq=8, Tk=8, Dk=128, Dv=128, scale=0.1,
+             causal=1, dtype=BF16)
+    a.update(kw)
+    return gqa.lib().gqa_attn_fwd(a["q"], a["k"], a["v"], a["out"], a["B"], a["Hq"], a["Hkv"], a["Tq"],
+                                  a["Tk"], a["Dk"], a["Dv"], a["scale"], a["causal"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), INVALID), (dict(k=0), INVALID), (dict(v=0), INVALID), (dict(out=0), INVALID),
+    (dict(B=0), INVALID), (dict(Hq=0), INVALID), (dict(Hkv=-1), INVALID), (dict(Tq=0), INVALID),
+    (dict(Tk=0), INVALID), (dict(Hq=6, Hkv=4), INVALID), (dict(Tq=9, Tk=8), INVALID),
+    (dict(scale=float("nan")), INVALID), (dict(scale=float("inf")), INVALID), (dict(scale=-1.0), INVALID),
+    (dict(causal=2), INVALID), (dict(dtype=7), INVALID), (dict(q=FAKE + 2), INVALID),
+    (dict(Dk=96, Dv=96), UNSUP), (dict(Dk=128, Dv=64), UNSUP), (dict(Dk=576, Dv=512), UNSUP),
+    (dict(Dk=256, Dv=256, dtype=F32), UNSUP),
+])
+def test_fwd_rejects_on_host(kw, code):
+    assert _fwd(**kw) == code
+
+
+def _dec(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lens=FAKE, B=2, Hq=8, Hkv=2, Tmax=64, Dk=128, Dv=128,
+             ksb=2 * 64 * 128, ksh=64 * 128, kst=128, vsb=2 * 64 * 128, vsh=64 * 128, vst=128, scale=0.1,
+             S=0, ws=FAKE, wsb=1 << 30, dtype=BF16)
+    a.update(kw)
+    return gqa.lib().gqa_attn_decode(a["q"], a["k"], a["v"], a["out"], a["lens"], a["B"], a["Hq"], a["Hkv"],
+                                     a["Tmax"], a["Dk"], a["Dv"], a["ksb"], a["ksh"], a["kst"], a["vsb"],
+                                     a["vsh"], a["vst"], a["scale"], a["S"], a["ws"], a["wsb"], a["dtype"],
+                                     None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lens=0), INVALID), (dict(q=0), INVALID), (dict(Tmax=0), INVALID), (dict(Hq=6, Hkv=4), INVALID),
+    (dict(kst=0), INVALID), (dict(kst=100), INVALID), (dict(vst=64), INVALID), (dict(ksh=-8), INVALID),
+    (dict(S=-1), INVALID), (dict(S=1025), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(k=FAKE + 8), INVALID), (dict(lens=FAKE + 2), INVALID),
+    (dict(Dk=96, Dv=96), UNSUP), (dict(Dk=576, Dv=512, dtype=F32, kst=576, vst=576), UNSUP),
+    (dict(ws=0), WS), (dict(wsb=100), WS), (dict(ws=FAKE + 4), WS),
+])
+def test_decode_rejects_on_host(kw, code):
+    assert _dec(**kw) == code
+
+
+def test_workspace_size_and_splits():
+    assert gqa.decode_workspace_size(2, 4, 128, 0) == 0
+    assert gqa.decode_workspace_size(2, 4, 128, 1025) == 0
+    n = gqa.decode_workspace_size(64, 32, 128, 16)
+    assert n >= 64 * 32 * 16 * 129 * 4 and n % 256 == 0
+    # the split choice depends only on the shape
+    s = gqa.decode_splits(64, 32, 8, 8192, 128, 128, BF16)
+    assert 1 <= s <= 1024 and s == gqa.decode_splits(64, 32, 8, 8192, 128, 128, BF16)
+    assert gqa.decode_splits(16, 128, 1, 32768, 576, 512, BF16) >= 1
+    with pytest.raises(gqa.GQAError):
+        gqa.decode_splits(16, 128, 1, 32768, 576, 512, F32)
+    # every default split count fits a workspace the size function accepts
+    for shape in [(1, 4, 2, 128, 64, 64, F32), (64, 32, 8, 8192, 128, 128, BF16), (16, 128, 1, 32768, 576, 512, BF16)]:
+        B, Hq, Hkv, T, Dk, Dv, dt = shape
+        assert gqa.decode_workspace_size(B, Hq, Dv, gqa.decode_splits(*shape)) > 0
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 2, 4, 64)
+    with pytest.raises(ValueError):
+        gqa.attention(q, q[:, :1], q[:, :1])
