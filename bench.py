@@ -1,0 +1,292 @@
+"""Benchmark: causal grouped-query attention on one MI355X.
+
+One step = one pass of the whole hot path on the two GQA 32q/8kv d128
+workloads: the causal prefill (B=4, Hq=32, Hkv=8, T=4096, bf16) through
+gqa_attn_fwd, then the split-KV decode (B=64, Hq=32, Hkv=8, Tmax=8192,
+lengths uniform in [1024, 8192]) through gqa_attn_decode.  Inputs are seeded
+synthetic N(0,1) tensors already resident in HBM.  `value` is the prefill
+throughput in TFLOP/s (algorithmic FLOPs: 2*(Dk+Dv) per visible causal
+(query, key) pair per query head); the decode KV read rate is reported next
+to it.  Per-kernel times come from HIP events recorded on the stream the
+library launches on (torch's current stream).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+METRIC = "prefill attn TFLOP/s & %MFMA peak; decode KV GB/s & %HBM peak (GQA 32q/8kv d128)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "fwd_bf16_kernel": ["causal_grouped_query_amd/csrc/fwd_bf16.hip",
+                        "causal_grouped_query_amd/csrc/device_common.h"],
+    "decode_bf16_kernel": ["causal_grouped_query_amd/csrc/decode_bf16.hip",
+                           "causal_grouped_query_amd/csrc/device_common.h"],
+}
+
+
+def causal_pairs(Tq: int, Tk: int) -> int:
+    off = Tk - Tq
+    return sum(min(Tk, off + i + 1) for i in range(Tq))
+
+
+def fwd_flops(w) -> float:
+    return 2.0 * (w.Dk + w.Dv) * causal_pairs(w.Tq, w.Tk) * w.Hq * w.B
+
+
+def decode_bytes(w, lens) -> float:
+    per_key = w.Dk if w.kind == "mla_decode" else (w.Dk + w.Dv)  # MLA: V is the latent prefix of K
+    return float(sum(lens)) * w.Hkv * per_key * 2
+
+
+def decode_flops(w, lens) -> float:
+    return 2.0 * (w.Dk + w.Dv) * float(sum(lens)) * w.Hq
+
+
+def source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str, launches_per_unit: int = 1):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_sha") != source_sha(kernel):
+        return None
+    return t["bytes_per_launch"]
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extra", action="store_true", help="skip the MQA-suffix / MLA / fp32 workloads")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(see DESIGN.md for how the work would shard).", file=sys.stderr)
+        return 2
+
+    import torch
+    import causal_grouped_query_amd as gqa
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a HIP device", file=sys.stderr)
+        return 2
+    gqa.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+
+    # ---------------- inputs (seeded, synthetic, resident in HBM) ----------------
+    wp, wd = W.GQA_PREFILL, W.GQA_DECODE
+    q, k, v = (t.to(dev) for t in W.fwd_inputs(wp))
+    out = torch.empty((wp.B, wp.Hq, wp.Tq, wp.Dv), dtype=torch.bfloat16, device=dev)
+    dq, dk, dv, lens_cpu = W.decode_inputs(wd, nan_tail=False)
+    dq, dk, dv = dq.to(dev), dk.to(dev), dv.to(dev)
+    lens = lens_cpu.to(dev)
+    dout = torch.empty((wd.B, wd.Hq, 1, wd.Dv), dtype=torch.bfloat16, device=dev)
+    S = gqa.decode_splits(wd.B, wd.Hq, wd.Hkv, wd.Tk, wd.Dk, wd.Dv, gqa.GQA_BF16)
+    ws = torch.empty(gqa.decode_workspace_size(wd.B, wd.Hq, wd.Dv, S), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def prefill():
+        gqa.attention(q, k, v, scale=wp.scale, causal=True, out=out)
+
+    def decode():
+        gqa.decode(dq, dk, dv, lens, scale=wd.scale, num_splits=S, out=dout, workspace=ws)
+
+    for _ in range(args.warmup):
+        prefill()
+        decode()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for i in range(K):
+        ev[i][0].record()
+        prefill()
+        ev[i][1].record()
+        decode()
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_pre = sum(e[0].elapsed_time(e[1]) for e in ev) / K * 1e-3
+    t_dec = sum(e[1].elapsed_time(e[2]) for e in ev) / K * 1e-3
+    ms_step = ev[0][0].elapsed_time(ev[-1][2]) / K
+
+    F = fwd_flops(wp)
+    lens_list = lens_cpu.tolist()
+    DB = decode_bytes(wd, lens_list)
+    pre_tflops = F / t_pre / 1e12
+    dec_gbps = DB / t_dec / 1e9
+
+    tr = traffic_for("fwd_bf16_kernel")
+    roofline = {
+        "kernel": "fwd_bf16_kernel<128> (gqa_attn_fwd, one launch per step)",
+        "bound": "mfma", "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "traffic": tr,
+        "avg_launch_us": round(t_pre * 1e6, 2), "flop_per_launch": F,
+    }
+    trd = traffic_for("decode_bf16_kernel")
+    roofline_decode = {
+        "kernel": f"decode_bf16_kernel<128,128> + combine_kernel (gqa_attn_decode, {S} splits)",
+        "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+        "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": trd,
+        "avg_launch_us": round(t_dec * 1e6, 2), "kv_bytes_per_launch": DB, "sum_len": int(sum(lens_list)),
+    }
+
+    result = {
+        "metric": METRIC,
+        "value": round(pre_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), cast to bf16; decode lengths uniform [1024, 8192])",
+        "config": {
+            "workload": f"{wp.name} + {wd.name}",
+            "prefill": {"B": wp.B, "Hq": wp.Hq, "Hkv": wp.Hkv, "Tq": wp.Tq, "Tk": wp.Tk, "D": wp.Dk,
+                        "causal": True},
+            "decode": {"B": wd.B, "Hq": wd.Hq, "Hkv": wd.Hkv, "Tmax": wd.Tk, "D": wd.Dk, "splits": S},
+        },
+        "prefill_tflops": round(pre_tflops, 2),
+        "prefill_frac_mfma_peak": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
+        "decode_kv_GBps": round(dec_gbps, 1),
+        "decode_frac_hbm_peak": round(dec_gbps / PEAK_HBM_GBPS, 4),
+        "roofline": roofline,
+        "roofline_decode": roofline_decode,
+        "wall_s_timed": round(wall, 4),
+    }
+
+    # free the headline inputs before the extra workloads
+    del q, k, v, out, dq, dk, dv, dout, ws
+    torch.cuda.empty_cache()
+
+    if not args.no_extra:
+        result["extra"] = extra_workloads(torch, gqa, W, dev)
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def _time(torch, fn, reps=10, warm=3):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps * 1e-3
+
+
+def extra_workloads(torch, gqa, W, dev):
+    """The other headline shapes, timed the same way (not part of the step)."""
+    res = {}
+    w = W.MQA_SUFFIX
+    q, k, v = (t.to(dev) for t in W.fwd_inputs(w))
+    out = torch.empty((w.B, w.Hq, w.Tq, w.Dv), dtype=torch.bfloat16, device=dev)
+    sec = _time(torch, lambda: gqa.attention(q, k, v, scale=w.scale, out=out))
+    f = fwd_flops(w)
+    res[w.name] = {"us": round(sec * 1e6, 1), "TFLOP/s": round(f / sec / 1e12, 1),
+                   "frac_mfma_peak": round(f / sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    del q, k, v, out
+
+    w = W.MLA_DECODE
+    q, kc, _, lens = W.decode_inputs(w, nan_tail=False)
+    q, kc, lens_d = q.to(dev), kc.to(dev), lens.to(dev)
+    out = torch.empty((w.B, w.Hq, 1, w.Dv), dtype=torch.bfloat16, device=dev)
+    S = gqa.decode_splits(w.B, w.Hq, w.Hkv, w.Tk, w.Dk, w.Dv, gqa.GQA_BF16)
+    ws = torch.empty(gqa.decode_workspace_size(w.B, w.Hq, w.Dv, S), dtype=torch.uint8, device=dev)
+    sec = _time(torch, lambda: gqa.decode(q, kc, kc[..., : w.Dv], lens_d, scale=w.scale, num_splits=S, out=out,
+                                          workspace=ws))
+    b = decode_bytes(w, lens.tolist())
+    f = decode_flops(w, lens.tolist())
+    res[w.name] = {"us": round(sec * 1e6, 1), "GB/s": round(b / sec / 1e9, 1),
+                   "frac_hbm_peak": round(b / sec / 1e9 / PEAK_HBM_GBPS, 4),
+                   "TFLOP/s": round(f / sec / 1e12, 1), "splits": S}
+    del q, kc, out, ws
+
+    w = W.TINY_F32
+    q, k, v = (t.to(dev) for t in W.fwd_inputs(w))
+    sec = _time(torch, lambda: gqa.attention(q, k, v, scale=w.scale))
+    res[w.name] = {"us": round(sec * 1e6, 1), "note": "parity-only fp32 workload"}
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(target_s: float):
+    """The fp64 oracle as it stands, on this host's cores, over a bounded random
+    sample of the prefill workload's rows; rate scaled to TFLOP/s of the same
+    algorithmic FLOP count."""
+    import numpy as np
+    import workloads as W
+    from oracle import oracle as O
+
+    w = W.GQA_PREFILL
+    q, k, v = W.fwd_inputs(w)
+    threads = O.max_threads()
+    rng = np.random.default_rng(12345)
+    n_rows_total = w.B * w.Hq * w.Tq
+    done_rows, done_flops, elapsed = 0, 0.0, 0.0
+    batch = 2048
+    while elapsed < target_s and done_rows < n_rows_total:
+        rows = rng.integers(0, n_rows_total, size=batch)
+        i = rows % w.Tq
+        flops = float(np.sum(2.0 * (w.Dk + w.Dv) * (i + 1)))  # square causal: row i sees i+1 keys
+        t0 = time.perf_counter()
+        O.attention(q, k, v, w.scale, True, rows=rows, threads=threads)
+        elapsed += time.perf_counter() - t0
+        done_rows += batch
+        done_flops += flops
+        if elapsed < 1.0:
+            batch *= 2
+    return {
+        "value": done_flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done_rows} uniformly drawn query rows (of {n_rows_total}) of {w.name}, fp64, "
+                  f"{elapsed:.1f} s",
+    }
+
+
+if __name__ == "__main__":
+    sys.exit(main())

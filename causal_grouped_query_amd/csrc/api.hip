@@ -59,7 +59,7 @@ int default_splits(int B, int Hq, int Hkv, int Tmax, int Dk)
         // absorbed MLA: a workgroup covers 128 query heads of a sequence
         groups = (long long)B * Hkv * ((G + 127) / 128);
         min_chunk = 256;
-        long long s = (512 + groups - 1) / groups;  // at least ~2 workgroups per CU
+        long long s = (256 + groups - 1) / groups;  // one workgroup per CU, equal chunks
         long long cap = (Tmax + min_chunk - 1) / min_chunk;
         if (s > cap) s = cap;
         if (s < 1) s = 1;
@@ -188,6 +188,8 @@ GQA_API int gqa_attn_decode(const void *q, const void *k, const void *v, void *o
     if (k_st < Dk || v_st < Dv) return GQA_ERR_INVALID_ARG;  // rows may not overlap
     if (num_splits < 0 || num_splits > kMaxSplits) return GQA_ERR_INVALID_ARG;
     if (!head_dims_decode(Dk, Dv, dtype)) return GQA_ERR_UNSUPPORTED;
+    if (Dk == 576 && !(v == k && v_sb == k_sb && v_sh == k_sh && v_st == k_st))
+        return GQA_ERR_UNSUPPORTED;  // absorbed MLA: the value is the key's latent prefix
     if (dtype == GQA_BF16) {
         if (k_sb % 8 || k_sh % 8 || k_st % 8 || v_sb % 8 || v_sh % 8 || v_st % 8)
             return GQA_ERR_INVALID_ARG;

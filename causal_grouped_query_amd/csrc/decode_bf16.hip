@@ -10,15 +10,14 @@
 // kernel (combine.hip) merges the S partials exactly (online-softmax merge,
 // "A Visual Guide to Attention", section on sources and execution).
 //
-// The same kernel serves the weight-absorbed MLA shape of "Attention
-// Architecture Evolution" (MLA section; absorbed score/value equations of its
-// DSA section): MQA with a 576-wide key (512 latent + 64 rope) whose first
-// 512 columns are the value; the caller passes v = k.
-//
 // Layout in a workgroup: NW waves, wave w owns query heads
 // 32*(NW*hblk + w) + (0..31) of the group (columns of the MFMA, zero-padded
 // when the group is smaller).  Scores are S^T = K Q^T (32 keys x 32 heads per
 // v_mfma_f32_32x32x16_bf16), O^T = V^T P^T as in the prefill kernel.
+// K/V tiles of 32 keys stream HBM -> LDS through global_load_lds into a
+// STAGES-deep ring (STAGES-1 tiles in flight while one is computed); V^T
+// comes from ds_read_b64_tr_b16.  (The absorbed-MLA shape has its own kernel,
+// mla_decode.hip, whose register budget needs a different wave layout.)
 #include "device_common.h"
 #include "launch.h"
 
@@ -28,28 +27,26 @@ namespace {
 
 constexpr int kTK = 32;  // keys per tile
 
-template <int DK, int DV>
+template <int DK, int DV, int STAGES>
 struct DecSmem {
-    static constexpr int KP = DK + 8;
-    static constexpr int VP = kTK + 8;
-    uint16_t k[kTK * KP];
-    uint16_t vt[DV * VP];
+    uint16_t k[STAGES][kTK * DK];
+    uint16_t v[STAGES][kTK * DV];
 };
 
-template <int DK, int DV, int NW, bool PREFETCH>
-__global__ __launch_bounds__(64 * NW) void decode_bf16_kernel(DecodeArgs p)
+template <int DK, int DV, int NW, int STAGES>
+__global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kernel(DecodeArgs p)
 {
     constexpr int NT = 64 * NW;
-    constexpr int KP = DecSmem<DK, DV>::KP;
-    constexpr int VP = DecSmem<DK, DV>::VP;
+    constexpr int CPRK = DK / 8, CPRV = DV / 8;
     constexpr int KS = DK / 16;
     constexpr int DT = DV / 32;
-    constexpr int KCH = kTK * DK / 8;
-    constexpr int KPT = (KCH + NT - 1) / NT;
-    constexpr int VBL = (kTK / 4) * (DV / 8);
-    constexpr int VPT = (VBL + NT - 1) / NT;
+    constexpr int KINS = kTK * CPRK / NT;                  // async copies per thread, K tile
+    constexpr int VINS = kTK * CPRV / NT;                  // and V tile
+    constexpr int NI = KINS + VINS;                        // vmem ops per thread per tile
+    static_assert(kTK * CPRK % NT == 0 && kTK * CPRV % NT == 0, "tile must split evenly");
+    static_assert(STAGES >= 2 && (STAGES - 2) * NI < 64, "ring depth");
 
-    __shared__ __attribute__((aligned(16))) DecSmem<DK, DV> sm;
+    __shared__ __attribute__((aligned(1024))) DecSmem<DK, DV, STAGES> sm;
 
     const int split = blockIdx.x;
     const int hblk = blockIdx.y;
@@ -71,6 +68,27 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_kernel(DecodeArgs p)
     const uint16_t *kb = (const uint16_t *)p.k + (size_t)b * p.k_sb + (size_t)kvh * p.k_sh;
     const uint16_t *vb = (const uint16_t *)p.v + (size_t)b * p.v_sb + (size_t)kvh * p.v_sh;
 
+    // Async copy of keys [k0, k0 + 32) into ring slot `slot`; rows past the
+    // chunk end re-read its last key (in bounds; masked below).
+    auto issue_tile = [&](int k0, int slot) {
+#pragma unroll
+        for (int j = 0; j < KINS; ++j) {
+            const int base = (j * NW + w) * 64;
+            const int Lc = base + lane;
+            const int row = Lc / CPRK, sl = Lc % CPRK;
+            const int c = sl ^ swz<CPRK>(row);
+            g2lds16(kb + (size_t)min(k0 + row, kend - 1) * p.k_st + c * 8, &sm.k[slot][base * 8]);
+        }
+#pragma unroll
+        for (int j = 0; j < VINS; ++j) {
+            const int base = (j * NW + w) * 64;
+            const int Lc = base + lane;
+            const int row = Lc / CPRV, sl = Lc % CPRV;
+            const int c = sl ^ swz<CPRV>(row);
+            g2lds16(vb + (size_t)min(k0 + row, kend - 1) * p.v_st + c * 8, &sm.v[slot][base * 8]);
+        }
+    };
+
     u32x4 qreg[KS];
     {
         const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * p.Hq + head) * DK;
@@ -88,71 +106,33 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_kernel(DecodeArgs p)
         for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    u32x4 kpre[KPT];
-    u32x4 vpre[VPT][4];
+    const int krow = kperm(col);
+    const int kswz = swz<CPRK>(krow);
+    const int vg = lane >> 4, vi = lane & 15;
 
-    auto load_tile = [&](int k0) {
+    // prologue: fill all but one ring slot
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int c = tid + i * NT;
-            const int row = c / (DK / 8), cc = c % (DK / 8);
-            u32x4 z = {0u, 0u, 0u, 0u};
-            kpre[i] = (c < KCH && k0 + row < kend)
-                          ? *(const u32x4 *)(kb + (size_t)(k0 + row) * p.k_st + cc * 8)
-                          : z;
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int vbk = tid + i * NT;
-            const int db = vbk % (DV / 8), kq = vbk / (DV / 8);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int key = k0 + 4 * kq + j;
-                u32x4 z = {0u, 0u, 0u, 0u};
-                vpre[i][j] = (vbk < VBL && key < kend)
-                                 ? *(const u32x4 *)(vb + (size_t)key * p.v_st + db * 8)
-                                 : z;
-            }
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int c = tid + i * NT;
-            const int row = c / (DK / 8), cc = c % (DK / 8);
-            if (c < KCH) *(u32x4 *)(&sm.k[row * KP + cc * 8]) = kpre[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int vbk = tid + i * NT;
-            const int db = vbk % (DV / 8), kq = vbk / (DV / 8);
-            if (vbk < VBL) {
-                u32x2 t8[8];
-                transpose4x8(vpre[i], t8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    *(u32x2 *)(&sm.vt[(db * 8 + e) * VP + 4 * kq]) = t8[e];
-            }
-        }
-    };
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < ntiles) issue_tile(kbeg + s * kTK, s);
 
     const float c = p.c;
-    if (PREFETCH && ntiles > 0) load_tile(kbeg);
-
     for (int it = 0; it < ntiles; ++it) {
         const int k0 = kbeg + it * kTK;
-        if (!PREFETCH) load_tile(k0);
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        if (PREFETCH && it + 1 < ntiles) load_tile(k0 + kTK);
+        const int slot = it % STAGES;
+        if (it + STAGES - 2 < ntiles)
+            wait_vmem_le<(STAGES - 2) * NI>();  // tile `it` landed, later ones may fly
+        else
+            wait_vmem();
+        __syncthreads();  // tile visible to all waves; slot of tile it-1 is free
+        if (it + STAGES - 1 < ntiles) issue_tile(k0 + (STAGES - 1) * kTK, (it + STAGES - 1) % STAGES);
 
+        const uint16_t *ks_ = sm.k[slot];
         f32x16 s;
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[e] = 0.f;
-        const uint16_t *krow = &sm.k[kperm(col) * KP + 8 * hi];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) s = mfma32x32x16(*(const u32x4 *)(krow + 16 * ks), qreg[ks], s);
+        for (int ks = 0; ks < KS; ++ks)
+            s = mfma32x32x16(*(const u32x4 *)(ks_ + krow * DK + (((2 * ks + hi) ^ kswz) * 8)), qreg[ks], s);
 
         if (k0 + kTK > kend) {
 #pragma unroll
@@ -164,18 +144,22 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_kernel(DecodeArgs p)
 #pragma unroll
         for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
         mx = fmaxf(mx, wave_swap_half(mx));
-        const float m_new = fmaxf(m_run, mx * c);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
-        l_run *= alpha;
+        const float mt = mx * c;
+        if (__any(mt > m_run + 8.0f)) {
+            // only lanes whose own max crossed the threshold move their
+            // reference, so a row never depends on keys it cannot see
+            const float m_new = (mt > m_run + 8.0f) ? mt : m_run;
+            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < DT; ++i)
+            for (int i = 0; i < DT; ++i)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+                for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
         u32x4 pb[2];
-        float psum = 0.f;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             float pv[8];
@@ -186,15 +170,24 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_kernel(DecodeArgs p)
             pb[h].y = pack_bf16x2(pv[2], pv[3]);
             pb[h].z = pack_bf16x2(pv[4], pv[5]);
             pb[h].w = pack_bf16x2(pv[6], pv[7]);
-            psum = sum_bf16x8(pb[h], psum);
+            l_run = sum_bf16x8(pb[h], l_run);
         }
-        l_run += psum;
 
+        // O^T += V^T P^T; V^T via transpose reads of the row-major V tile
+        const uint16_t *vs_ = sm.v[slot];
+        constexpr int VP = DV;
+        constexpr int VCPR = CPRV;
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
+            const int r0 = 16 * st + 8 * (vg >> 1) + (vi >> 2);
+            const int r1 = r0 + 4;
+            const int sw0 = swz<VCPR>(r0), sw1 = swz<VCPR>(r1);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const u32x4 va = *(const u32x4 *)(&sm.vt[(32 * dt + col) * VP + 16 * st + 8 * hi]);
+                const int cb = 32 * dt + 16 * (vg & 1) + 4 * (vi & 3);
+                const u32x2 lo = lds_read_tr16(vs_ + r0 * VP + (((cb >> 3) ^ sw0) * 8) + (cb & 7));
+                const u32x2 hv = lds_read_tr16(vs_ + r1 * VP + (((cb >> 3) ^ sw1) * 8) + (cb & 7));
+                u32x4 va = {lo.x, lo.y, hv.x, hv.y};
                 o[dt] = mfma32x32x16(va, pb[st], o[dt]);
             }
         }
@@ -204,35 +197,24 @@ __global__ __launch_bounds__(64 * NW) void decode_bf16_kernel(DecodeArgs p)
     const float l_tot = l_run + wave_swap_half(l_run);
     const size_t prow = ((size_t)b * p.Hq + head) * p.S + split;
     float *po = p.part_o + prow * DV;
-    if (l_tot > 0.f) {
-        const float inv = 1.f / l_tot;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                f32x4 v4 = {o[dt][4 * j] * inv, o[dt][4 * j + 1] * inv, o[dt][4 * j + 2] * inv,
-                            o[dt][4 * j + 3] * inv};
-                *(f32x4 *)(po + 32 * dt + 8 * j + 4 * hi) = v4;
-            }
-        if (hi == 0) p.part_lse[prow] = m_run + __log2f(l_tot);
-    } else {
-        // empty chunk: contributes nothing to the merge
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                *(f32x4 *)(po + 32 * dt + 8 * j + 4 * hi) = z;
-            }
-        if (hi == 0) p.part_lse[prow] = -INFINITY;
-    }
+        for (int j = 0; j < 4; ++j) {
+            f32x4 v4 = {o[dt][4 * j] * inv, o[dt][4 * j + 1] * inv, o[dt][4 * j + 2] * inv,
+                        o[dt][4 * j + 3] * inv};
+            *(f32x4 *)(po + 32 * dt + 8 * j + 4 * hi) = v4;
+        }
+    // empty chunk: o = 0 and lse = -inf, so it weighs nothing in the merge
+    if (hi == 0) p.part_lse[prow] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
 }
 
-template <int DK, int DV, int NW, bool PF>
+template <int DK, int DV, int NW, int STAGES>
 int launch_one(const DecodeArgs &a, hipStream_t stream)
 {
     dim3 grid(a.S, a.n_hblk, a.B * a.Hkv), block(64 * NW);
-    hipLaunchKernelGGL((decode_bf16_kernel<DK, DV, NW, PF>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_bf16_kernel<DK, DV, NW, STAGES>), grid, block, 0, stream, a);
     return 0;
 }
 
@@ -250,9 +232,15 @@ int decode_bf16_heads_per_block(int Dk, int G)
 
 int launch_decode_bf16(const DecodeArgs &a, int Dk, int Dv, hipStream_t stream)
 {
-    if (Dk == 128 && Dv == 128) return launch_one<128, 128, 1, true>(a, stream);
-    if (Dk == 64 && Dv == 64) return launch_one<64, 64, 1, true>(a, stream);
-    if (Dk == 576 && Dv == 512) return launch_one<576, 512, 4, false>(a, stream);
+    if (Dk == 128 && Dv == 128) return launch_one<128, 128, 1, 2>(a, stream);
+    if (Dk == 64 && Dv == 64) return launch_one<64, 64, 1, 3>(a, stream);
+    if (Dk == 576 && Dv == 512) {
+        // the value must be the latent prefix of the key (v == k, same strides)
+        const bool v_is_k_prefix =
+            a.v == a.k && a.v_sb == a.k_sb && a.v_sh == a.k_sh && a.v_st == a.k_st;
+        if (!v_is_k_prefix) return -1;
+        return launch_mla_decode(a, stream);
+    }
     return -1;
 }
 

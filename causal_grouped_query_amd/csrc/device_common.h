@@ -15,6 +15,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+#define GQA_LDS __attribute__((address_space(3)))
 
 // 32x32x16 bf16 MFMA, fp32 accumulate.  Operand lane layout (both A and B):
 // lane l holds row/column (l & 31) and 8 contraction slots owned by lane
@@ -85,6 +88,55 @@ __device__ __forceinline__ void transpose4x8(const u32x4 r[4], u32x2 out[8])
         out[2 * w + 1].x = __builtin_amdgcn_perm(r[1][w], r[0][w], 0x07060302u);
         out[2 * w + 1].y = __builtin_amdgcn_perm(r[3][w], r[2][w], 0x07060302u);
     }
+}
+
+// 16-byte chunk swizzle for a row-major [rows][CPR chunks] bf16 tile in LDS:
+// chunk c of row r is stored at slot c ^ swz(r).  Bits: slot bit 1 <- r0,
+// bit 2 <- r1, bit 0 <- r3, bit 3 <- r2.  This keeps the 8 rows an MFMA
+// A-operand read touches per 8-lane group (rows 16a+4b+{0..3}, +8) and the
+// 4 rows x 2 chunks a 16-lane ds_read_b64_tr_b16 group touches on distinct
+// 16-byte bank groups.
+// Rows whose chunk count is not a multiple of 16 (e.g. the 72 chunks of a
+// 576-wide row) use only the low 3 bits, so a slot never leaves its aligned
+// group of 8 chunks.
+template <int CPR>
+__device__ __forceinline__ int swz(int r)
+{
+    constexpr int MASK = (CPR % 16 == 0) ? 15 : 7;
+    static_assert(CPR % 8 == 0, "rows must hold a multiple of 8 chunks");
+    return (((r & 3) << 1) | ((r >> 3) & 1) | ((r & 4) << 1)) & MASK;
+}
+
+// Asynchronous global -> LDS copy of 16 bytes per lane (gfx950
+// global_load_lds_dwordx4).  Lane l's bytes land at lds_wave_base + 16*l;
+// lds_wave_base must be the same for the whole wave.
+__device__ __forceinline__ void g2lds16(const void *gptr, void *lds_wave_base)
+{
+    __builtin_amdgcn_global_load_lds(gptr, (GQA_LDS void *)lds_wave_base, 16, 0, 0);
+}
+
+// Wait for this wave's outstanding vector-memory operations (including
+// global -> LDS copies).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (loads complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS transpose read (ds_read_b64_tr_b16).  Within each 16-lane group, lane
+// i receives, for r = 0..3, the 16-bit element (i & 3) of the 8-byte chunk
+// addressed by lane 4r + (i >> 2) of the same group.  If lane 4r + q points
+// at row R0 + r, columns C0 + 4q .. C0 + 4q + 3 of a row-major 16-bit
+// matrix, lane i therefore receives column C0 + i of rows R0 .. R0 + 3.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void *lds_addr)
+{
+    i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GQA_LDS i16x4 *)lds_addr);
+    return __builtin_bit_cast(u32x2, r);
 }
 
 __device__ __forceinline__ float wave_swap_half(float x)

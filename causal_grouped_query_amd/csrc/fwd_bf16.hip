@@ -20,15 +20,20 @@
 //    In the accumulator every lane holds one query column, so row max and row
 //    sum are in-lane plus a single exchange with lane l^32.
 //  * O^T = V^T P^T: P^T needs no data movement (see kperm in
-//    device_common.h); V is transposed into LDS while staging so the A
-//    operand is one 16-byte LDS read.
+//    device_common.h); V stays row-major in LDS and its transposed A operand
+//    comes from two ds_read_b64_tr_b16 per MFMA.
+//  * K and V tiles go straight from HBM to LDS with global_load_lds (no
+//    registers, no VALU), into a double-buffered, XOR-swizzled ring: tile
+//    i+1 is in flight while tile i is computed; one barrier per tile.
 //  * Online softmax in base 2: scale*log2(e) is folded into one FMA per
-//    score, exp via v_exp_f32.
+//    score, exp via v_exp_f32, the row sum via v_dot2 over the bf16-rounded
+//    weights.  The running max is only moved (and O rescaled) when a tile's
+//    max exceeds it by more than 2^8; weights then stay <= 256, which fp32
+//    and bf16 hold exactly as well as weights <= 1, and the result is the
+//    same softmax.
 //  * Grid order: tiles of one (batch, KV head, head block) are consecutive
 //    on one XCD (the dispatcher deals workgroups round-robin over 8 XCDs, so
 //    the remap keeps a KV head's K/V in one L2), heaviest causal tiles first.
-//  * K/V tiles are double-buffered through registers: the global loads of
-//    tile i+1 are in flight while tile i is computed.
 #include "device_common.h"
 #include "launch.h"
 
@@ -42,25 +47,21 @@ constexpr int kThreads = 64 * kNW;
 
 template <int D>
 struct FwdSmem {
-    static constexpr int KP = D + 8;    // K row pitch (elements), breaks bank aliasing
-    static constexpr int VP = kBN + 8;  // V^T row pitch (elements)
-    uint16_t k[kBN * KP];
-    uint16_t vt[D * VP];
+    static constexpr int TILE = kBN * D;  // elements of one K or V tile (swizzled, unpadded)
+    uint16_t k[2][TILE];
+    uint16_t v[2][TILE];
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs p)
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p)
 {
-    constexpr int KP = FwdSmem<D>::KP;
-    constexpr int VP = FwdSmem<D>::VP;
-    constexpr int KS = D / 16;                            // MFMA k-steps over the head dim
-    constexpr int DT = D / 32;                            // 32-row tiles of O^T
-    constexpr int KCH = kBN * D / 8;                      // 16-byte chunks per K tile
-    constexpr int KPT = (KCH + kThreads - 1) / kThreads;  // chunks per thread
-    constexpr int VBL = (kBN / 4) * (D / 8);              // 4x8 V blocks per tile
-    constexpr int VPT = (VBL + kThreads - 1) / kThreads;  // blocks per thread
+    constexpr int CPR = D / 8;                     // 16-byte chunks per row
+    constexpr int KS = D / 16;                     // MFMA k-steps over the head dim
+    constexpr int DT = D / 32;                     // 32-row tiles of O^T
+    constexpr int NINS = kBN * CPR / kThreads;     // async copies per thread per tensor
+    static_assert(kBN * CPR % kThreads == 0, "tile must split evenly over the workgroup");
 
-    __shared__ __attribute__((aligned(16))) FwdSmem<D> sm;
+    __shared__ __attribute__((aligned(1024))) FwdSmem<D> sm;
 
     // ---- workgroup -> (unit, query tile), XCD-aware, heaviest first ----
     const int nblk = gridDim.x;
@@ -96,6 +97,22 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs p)
     const uint16_t *kbase = p.k + (size_t)bk * p.Tk * D;
     const uint16_t *vbase = p.v + (size_t)bk * p.Tk * D;
 
+    // Async copy of keys [k0, k0 + 64) of K and V into ring slot `buf`.  LDS
+    // chunk Lc = row * CPR + slot holds global chunk slot ^ swz(row); rows
+    // past Tk re-read row Tk - 1 (in bounds; those keys are masked).
+    auto issue_tile = [&](int k0, int buf) {
+#pragma unroll
+        for (int j = 0; j < NINS; ++j) {
+            const int base = (j * kNW + w) * 64;  // first LDS chunk of this wave's copy
+            const int Lc = base + lane;
+            const int row = Lc / CPR, slot = Lc % CPR;
+            const int c = slot ^ swz<CPR>(row);
+            const size_t grow = (size_t)min(k0 + row, p.Tk - 1) * D + c * 8;
+            g2lds16(kbase + grow, &sm.k[buf][base * 8]);
+            g2lds16(vbase + grow, &sm.v[buf][base * 8]);
+        }
+    };
+
     // ---- Q^T in registers (B operand), zero for rows past Tq ----
     u32x4 qreg[KS];
     {
@@ -113,138 +130,124 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(FwdArgs p)
     for (int i = 0; i < DT; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
-    float m_run = -INFINITY;  // running max of scaled scores (log2 units)
+    float m_run = -INFINITY;  // running reference max of scaled scores (log2 units)
     float l_run = 0.f;        // this lane's half of the running sum
 
-    u32x4 kpre[KPT];
-    u32x4 vpre[VPT][4];
-
-    auto load_tile = [&](int k0) {
+    // per-lane LDS offsets (elements) that do not depend on the tile
+    int koff[2][KS];
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int c = tid + i * kThreads;
-            const int row = c / (D / 8), cc = c % (D / 8);
-            u32x4 z = {0u, 0u, 0u, 0u};
-            kpre[i] = (c < KCH && k0 + row < p.Tk)
-                          ? *(const u32x4 *)(kbase + (size_t)(k0 + row) * D + cc * 8)
-                          : z;
-        }
+    for (int t = 0; t < 2; ++t) {
+        const int rr = 32 * t + kperm(col);
 #pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int vb = tid + i * kThreads;
-            const int db = vb % (D / 8), kb = vb / (D / 8);
+        for (int ks = 0; ks < KS; ++ks) koff[t][ks] = rr * D + (((2 * ks + hi) ^ swz<CPR>(rr)) * 8);
+    }
+    // V^T operand through transpose reads: lane = 16 g + i points at row
+    // 16 st + 8 (g >> 1) + 4 h + (i >> 2), columns 32 dt + 16 (g & 1) + 4 (i & 3)
+    const int vg = lane >> 4, vi = lane & 15;
+    int voff[4][2];  // [st][h], column part added per dt
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int key = k0 + 4 * kb + j;
-                u32x4 z = {0u, 0u, 0u, 0u};
-                vpre[i][j] = (vb < VBL && key < p.Tk)
-                                 ? *(const u32x4 *)(vbase + (size_t)key * D + db * 8)
-                                 : z;
-            }
-        }
-    };
-
-    auto store_tile = [&]() {
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int c = tid + i * kThreads;
-            const int row = c / (D / 8), cc = c % (D / 8);
-            if (c < KCH) *(u32x4 *)(&sm.k[row * KP + cc * 8]) = kpre[i];
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int vb = tid + i * kThreads;
-            const int db = vb % (D / 8), kb = vb / (D / 8);
-            if (vb < VBL) {
-                u32x2 t8[8];
-                transpose4x8(vpre[i], t8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    *(u32x2 *)(&sm.vt[(db * 8 + e) * VP + 4 * kb]) = t8[e];
-            }
-        }
-    };
+        for (int h = 0; h < 2; ++h) voff[st][h] = 16 * st + 8 * (vg >> 1) + 4 * h + (vi >> 2);
 
     const float c = p.c;
-    if (ntiles > 0) load_tile(0);
+    if (ntiles > 0) issue_tile(0, 0);
+    wait_vmem();
+    __syncthreads();
 
     for (int it = 0; it < ntiles; ++it) {
         const int k0 = it * kBN;
-        __syncthreads();  // everyone is done reading the previous tile
-        store_tile();
-        __syncthreads();
-        if (it + 1 < ntiles) load_tile(k0 + kBN);
-        if (!wave_active || k0 > wlast) continue;
+        const int buf = it & 1;
+        if (it + 1 < ntiles) issue_tile(k0 + kBN, buf ^ 1);
 
-        // ---- S^T = K Q^T for 64 keys (two 32-key tiles) ----
-        f32x16 s[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) s[t][e] = 0.f;
-            const uint16_t *krow = &sm.k[(32 * t + kperm(col)) * KP + 8 * hi];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                s[t] = mfma32x32x16(*(const u32x4 *)(krow + 16 * ks), qreg[ks], s[t]);
-        }
+        if (wave_active && k0 <= wlast) {
+            const uint16_t *ks_ = sm.k[buf];
+            const uint16_t *vs_ = sm.v[buf];
 
-        // ---- mask (diagonal and ragged tiles only) ----
-        const bool need_mask = (p.causal && k0 + kBN - 1 > off + q0) || (k0 + kBN > p.Tk);
-        if (need_mask) {
+            // ---- S^T = K Q^T for 64 keys (two 32-key tiles) ----
+            f32x16 s[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) s[t][e] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    s[t] = mfma32x32x16(*(const u32x4 *)(ks_ + koff[t][ks]), qreg[ks], s[t]);
+            }
+
+            // ---- mask (diagonal and ragged tiles only) ----
+            const bool need_mask = (p.causal && k0 + kBN - 1 > off + q0) || (k0 + kBN > p.Tk);
+            if (need_mask) {
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        if (k0 + acc_key(t, e, hi) > lim) s[t][e] = -INFINITY;
+            }
+
+            // ---- online softmax (base 2, lazily rescaled) ----
+            float mx = s[0][0];
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    if (k0 + acc_key(t, e, hi) > lim) s[t][e] = -INFINITY;
-        }
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t][e]);
+            mx = fmaxf(mx, wave_swap_half(mx));
+            const float mt = mx * c;
+            if (__any(mt > m_run + 8.0f)) {
+                // only lanes whose own max crossed the threshold move their
+                // reference, so a row never depends on keys it cannot see
+                const float m_new = (mt > m_run + 8.0f) ? mt : m_run;
+                const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int i = 0; i < DT; ++i)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+            }
+            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
-        // ---- online softmax (base 2) ----
-        float mx = s[0][0];
+            u32x4 pb[4];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t][e]);
-        mx = fmaxf(mx, wave_swap_half(mx));
-        const float m_new = fmaxf(m_run, mx * c);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        m_run = m_new;
-        l_run *= alpha;
+                for (int h = 0; h < 2; ++h) {
+                    float pv[8];
 #pragma unroll
-        for (int i = 0; i < DT; ++i)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+                    for (int e = 0; e < 8; ++e)
+                        pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * h + e], c, -m_use));
+                    u32x4 pk;
+                    pk.x = pack_bf16x2(pv[0], pv[1]);
+                    pk.y = pack_bf16x2(pv[2], pv[3]);
+                    pk.z = pack_bf16x2(pv[4], pv[5]);
+                    pk.w = pack_bf16x2(pv[6], pv[7]);
+                    l_run = sum_bf16x8(pk, l_run);
+                    pb[2 * t + h] = pk;
+                }
+            }
 
-        u32x4 pb[4];
-        float psum = 0.f;
+            // ---- O^T += V^T P^T ----
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+            for (int st = 0; st < 4; ++st) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                float pv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * h + e], c, -m_use));
-                u32x4 pk;
-                pk.x = pack_bf16x2(pv[0], pv[1]);
-                pk.y = pack_bf16x2(pv[2], pv[3]);
-                pk.z = pack_bf16x2(pv[4], pv[5]);
-                pk.w = pack_bf16x2(pv[6], pv[7]);
-                psum = sum_bf16x8(pk, psum);
-                pb[2 * t + h] = pk;
+                for (int dt = 0; dt < DT; ++dt) {
+                    const int cb = 32 * dt + 16 * (vg & 1) + 4 * (vi & 3);  // column of this lane's chunk
+                    u32x2 lo, hi2;
+                    {
+                        const int row = voff[st][0];
+                        lo = lds_read_tr16(vs_ + row * D + (((cb >> 3) ^ swz<CPR>(row)) * 8) + (cb & 7));
+                    }
+                    {
+                        const int row = voff[st][1];
+                        hi2 = lds_read_tr16(vs_ + row * D + (((cb >> 3) ^ swz<CPR>(row)) * 8) + (cb & 7));
+                    }
+                    u32x4 va = {lo.x, lo.y, hi2.x, hi2.y};
+                    o[dt] = mfma32x32x16(va, pb[st], o[dt]);
+                }
             }
         }
-        l_run += psum;
-
-        // ---- O^T += V^T P^T ----
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const u32x4 va = *(const u32x4 *)(&sm.vt[(32 * dt + col) * VP + 16 * st + 8 * hi]);
-                o[dt] = mfma32x32x16(va, pb[st], o[dt]);
-            }
-        }
+        wait_vmem();
+        __syncthreads();  // tile it+1 landed; everyone is done with slot `buf`
     }
 
     if (!wave_active || qi >= p.Tq) return;

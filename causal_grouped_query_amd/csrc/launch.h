@@ -45,6 +45,8 @@ struct DecodeArgs {
 };
 
 int launch_decode_bf16(const DecodeArgs &a, int Dk, int Dv, hipStream_t stream);
+// Absorbed-MLA shape (Dk 576, Dv 512, V = latent prefix of K), 128 heads per block.
+int launch_mla_decode(const DecodeArgs &a, hipStream_t stream);
 int decode_bf16_key_tile();
 int decode_bf16_heads_per_block(int Dk, int G);
 

@@ -101,6 +101,7 @@ size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_splits);
  *            (element strides; d is unit-stride; t < Tmax).  For the
  *            absorbed-MLA shape pass v = k with the same strides and
  *            Dv = 512 < Dk = 576: the value is the latent prefix of each key.
+ *            (For (576, 512) any other v returns GQA_ERR_UNSUPPORTED.)
  *            Strides must be multiples of 8 elements and the base pointers
  *            16-byte aligned.
  *   out      [B, Hq, 1, Dv]  contiguous

@@ -85,6 +85,9 @@ def _dec(**kw):
     (dict(S=-1), INVALID), (dict(S=1025), INVALID), (dict(scale=float("nan")), INVALID),
     (dict(k=FAKE + 8), INVALID), (dict(lens=FAKE + 2), INVALID),
     (dict(Dk=96, Dv=96), UNSUP), (dict(Dk=576, Dv=512, dtype=F32, kst=576, vst=576), UNSUP),
+    # absorbed MLA: the value must be the key's latent prefix (same pointer and strides)
+    (dict(Dk=576, Dv=512, kst=576, vst=576, v=FAKE + 4096), UNSUP),
+    (dict(Dk=576, Dv=512, kst=576, vst=512), UNSUP),
     (dict(ws=0), WS), (dict(wsb=100), WS), (dict(ws=FAKE + 4), WS),
 ])
 def test_decode_rejects_on_host(kw, code):
