@@ -86,6 +86,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extra", action="store_true", help="skip the MQA-suffix / MLA / fp32 workloads")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -102,6 +104,17 @@ def main() -> int:
         return 2
     gqa.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
+
+    if args.copy_calibration:
+        # a plain copy of known size: reads 1 GiB, writes 1 GiB per launch
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+        return 0
 
     # ---------------- inputs (seeded, synthetic, resident in HBM) ----------------
     wp, wd = W.GQA_PREFILL, W.GQA_DECODE
