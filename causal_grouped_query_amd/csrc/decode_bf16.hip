@@ -68,24 +68,24 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kern
     const uint16_t *kb = (const uint16_t *)p.k + (size_t)b * p.k_sb + (size_t)kvh * p.k_sh;
     const uint16_t *vb = (const uint16_t *)p.v + (size_t)b * p.v_sb + (size_t)kvh * p.v_sh;
 
-    // Async copy of keys [k0, k0 + 32) into ring slot `slot`; rows past the
-    // chunk end re-read its last key (in bounds; masked below).
+    // Async copy of keys [k0, k0 + 32) into ring slot `slot` (plane layout,
+    // see PlaneTile); rows past the chunk end re-read its last key (in
+    // bounds; masked below).
+    using Tile = PlaneTile<kTK>;
     auto issue_tile = [&](int k0, int slot) {
 #pragma unroll
         for (int j = 0; j < KINS; ++j) {
             const int base = (j * NW + w) * 64;
-            const int Lc = base + lane;
-            const int row = Lc / CPRK, sl = Lc % CPRK;
-            const int c = sl ^ swz<CPRK>(row);
-            g2lds16(kb + (size_t)min(k0 + row, kend - 1) * p.k_st + c * 8, &sm.k[slot][base * 8]);
+            int row, chunk;
+            Tile::slot_source(base + lane, row, chunk);
+            g2lds16(kb + (size_t)min(k0 + row, kend - 1) * p.k_st + chunk * 8, &sm.k[slot][base * 8]);
         }
 #pragma unroll
         for (int j = 0; j < VINS; ++j) {
             const int base = (j * NW + w) * 64;
-            const int Lc = base + lane;
-            const int row = Lc / CPRV, sl = Lc % CPRV;
-            const int c = sl ^ swz<CPRV>(row);
-            g2lds16(vb + (size_t)min(k0 + row, kend - 1) * p.v_st + c * 8, &sm.v[slot][base * 8]);
+            int row, chunk;
+            Tile::slot_source(base + lane, row, chunk);
+            g2lds16(vb + (size_t)min(k0 + row, kend - 1) * p.v_st + chunk * 8, &sm.v[slot][base * 8]);
         }
     };
 
@@ -107,8 +107,12 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kern
     float m_run = -INFINITY, l_run = 0.f;
 
     const int krow = kperm(col);
-    const int kswz = swz<CPRK>(krow);
+    const int kbase_even = Tile::offset(krow, hi);
+    const int kbase_odd = Tile::offset(krow, 2 + hi);
     const int vg = lane >> 4, vi = lane & 15;
+    const int vrow = 8 * (vg >> 1) + (vi >> 2), vchunk = 2 * (vg & 1) + ((vi >> 1) & 1);
+    const int vb_h0 = Tile::offset(vrow, vchunk) + 8 * (vi & 1);      // rows 16 st + vrow
+    const int vb_h1 = Tile::offset(vrow + 4, vchunk) + 8 * (vi & 1);  // rows 16 st + vrow + 4
 
     // prologue: fill all but one ring slot
 #pragma unroll
@@ -126,13 +130,15 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kern
         __syncthreads();  // tile visible to all waves; slot of tile it-1 is free
         if (it + STAGES - 1 < ntiles) issue_tile(k0 + (STAGES - 1) * kTK, (it + STAGES - 1) % STAGES);
 
-        const uint16_t *ks_ = sm.k[slot];
+        const char *ks_ = (const char *)sm.k[slot];
         f32x16 s;
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            s = mfma32x32x16(*(const u32x4 *)(ks_ + krow * DK + (((2 * ks + hi) ^ kswz) * 8)), qreg[ks], s);
+        for (int ks = 0; ks < KS; ++ks) {
+            const int off_ = ((ks & 1) ? kbase_odd : kbase_even) + (ks >> 1) * Tile::PLANE_BYTES;
+            s = mfma32x32x16(*(const u32x4 *)(ks_ + off_), qreg[ks], s);
+        }
 
         if (k0 + kTK > kend) {
 #pragma unroll
@@ -143,7 +149,7 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kern
         float mx = s[0];
 #pragma unroll
         for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
-        mx = fmaxf(mx, wave_swap_half(mx));
+        mx = halves_max(mx);
         const float mt = mx * c;
         if (__any(mt > m_run + 8.0f)) {
             // only lanes whose own max crossed the threshold move their
@@ -173,20 +179,15 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kern
             l_run = sum_bf16x8(pb[h], l_run);
         }
 
-        // O^T += V^T P^T; V^T via transpose reads of the row-major V tile
-        const uint16_t *vs_ = sm.v[slot];
-        constexpr int VP = DV;
-        constexpr int VCPR = CPRV;
+        // O^T += V^T P^T; V^T via transpose reads of the V tile
+        const char *vs_ = (const char *)sm.v[slot];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-            const int r0 = 16 * st + 8 * (vg >> 1) + (vi >> 2);
-            const int r1 = r0 + 4;
-            const int sw0 = swz<VCPR>(r0), sw1 = swz<VCPR>(r1);
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
-                const int cb = 32 * dt + 16 * (vg & 1) + 4 * (vi & 3);
-                const u32x2 lo = lds_read_tr16(vs_ + r0 * VP + (((cb >> 3) ^ sw0) * 8) + (cb & 7));
-                const u32x2 hv = lds_read_tr16(vs_ + r1 * VP + (((cb >> 3) ^ sw1) * 8) + (cb & 7));
+                const int o_ = dt * Tile::PLANE_BYTES + 16 * st * 64;
+                const u32x2 lo = lds_read_tr16(vs_ + vb_h0 + o_);
+                const u32x2 hv = lds_read_tr16(vs_ + vb_h1 + o_);
                 u32x4 va = {lo.x, lo.y, hv.x, hv.y};
                 o[dt] = mfma32x32x16(va, pb[st], o[dt]);
             }
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kern
     }
 
     if (!head_ok) return;
-    const float l_tot = l_run + wave_swap_half(l_run);
+    const float l_tot = halves_sum(l_run);
     const size_t prow = ((size_t)b * p.Hq + head) * p.S + split;
     float *po = p.part_o + prow * DV;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;

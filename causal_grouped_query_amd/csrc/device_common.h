@@ -90,22 +90,47 @@ __device__ __forceinline__ void transpose4x8(const u32x4 r[4], u32x2 out[8])
     }
 }
 
-// 16-byte chunk swizzle for a row-major [rows][CPR chunks] bf16 tile in LDS:
-// chunk c of row r is stored at slot c ^ swz(r).  Bits: slot bit 1 <- r0,
-// bit 2 <- r1, bit 0 <- r3, bit 3 <- r2.  This keeps the 8 rows an MFMA
-// A-operand read touches per 8-lane group (rows 16a+4b+{0..3}, +8) and the
-// 4 rows x 2 chunks a 16-lane ds_read_b64_tr_b16 group touches on distinct
-// 16-byte bank groups.
-// Rows whose chunk count is not a multiple of 16 (e.g. the 72 chunks of a
-// 576-wide row) use only the low 3 bits, so a slot never leaves its aligned
-// group of 8 chunks.
-template <int CPR>
-__device__ __forceinline__ int swz(int r)
+// LDS tile layout ("planes").  A tile of R rows x CPR 16-byte chunks is
+// stored plane-major: plane p holds chunks 4p..4p+3 of every row (64 bytes
+// per row), and chunk c of row r sits at position (c & 3) ^ pswz(r) of its
+// row inside the plane, with pswz(r) = r3 | (r1 ^ r2) << 1 (row bits).
+// Bank groups are 16-byte positions inside a 128-byte (32-bank) or 256-byte
+// (64-bank) window.  With this swizzle
+//  * an MFMA A-operand read (one chunk of rows kperm(0..31): rows
+//    16a + {0..3, 8..11} per 8 lanes, rows 16a + 0..15 per 16 lanes) and
+//  * a ds_read_b64_tr_b16 read (rows r0 + 0..3, chunks {c0, c0 + 1} per 16
+//    lanes; all four chunks of a plane per 32 lanes)
+// touch distinct bank groups in both window sizes, and every per-lane
+// address of a tile loop is a base register plus an immediate.
+#ifndef GQA_PSWZ
+#define GQA_PSWZ 1
+#endif
+__device__ __forceinline__ int pswz(int r)
 {
-    constexpr int MASK = (CPR % 16 == 0) ? 15 : 7;
-    static_assert(CPR % 8 == 0, "rows must hold a multiple of 8 chunks");
-    return (((r & 3) << 1) | ((r >> 3) & 1) | ((r & 4) << 1)) & MASK;
+#if GQA_PSWZ
+    return ((r >> 3) & 1) | ((((r >> 1) ^ (r >> 2)) & 1) << 1);
+#else
+    return ((r >> 3) & 1) | (((r >> 1) & 1) << 1);
+#endif
 }
+
+template <int R>
+struct PlaneTile {
+    static constexpr int PLANE_BYTES = R * 64;
+    // byte offset of chunk c of row r
+    static __device__ __forceinline__ int offset(int r, int c)
+    {
+        return (c >> 2) * PLANE_BYTES + r * 64 + (((c & 3) ^ pswz(r)) << 4);
+    }
+    // The 16-byte slot a copy lane fills: slot = 64 * copy + lane (copies
+    // write 1 KiB blocks in order).  Returns the (row, chunk) it must fetch.
+    static __device__ __forceinline__ void slot_source(int slot, int &r, int &c)
+    {
+        const int plane = slot / (R * 4), rem = slot % (R * 4);
+        r = rem >> 2;
+        c = plane * 4 + ((rem & 3) ^ pswz(r));
+    }
+};
 
 // Asynchronous global -> LDS copy of 16 bytes per lane (gfx950
 // global_load_lds_dwordx4).  Lane l's bytes land at lds_wave_base + 16*l;
@@ -139,10 +164,19 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void *lds_addr)
     return __builtin_bit_cast(u32x2, r);
 }
 
-__device__ __forceinline__ float wave_swap_half(float x)
+// Combine a value with the one held by lane l ^ 32 (same accumulator
+// column, other half of the key rows) using gfx950 v_permlane32_swap: after
+// the swap the two results hold the low and the high half-wave's values in
+// every lane, so max / sum of the pair is the same in both lanes.
+__device__ __forceinline__ float halves_max(float x)
 {
-    // exchange with lane l ^ 32 (the other half of the wave)
-    return __shfl_xor(x, 32, 64);
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 } // namespace gqa

@@ -23,14 +23,16 @@
 //    device_common.h); V stays row-major in LDS and its transposed A operand
 //    comes from two ds_read_b64_tr_b16 per MFMA.
 //  * K and V tiles go straight from HBM to LDS with global_load_lds (no
-//    registers, no VALU), into a double-buffered, XOR-swizzled ring: tile
-//    i+1 is in flight while tile i is computed; one barrier per tile.
+//    registers, no VALU), into a double buffer in the swizzled plane layout
+//    of device_common.h (every LDS read of the loop is a base register plus
+//    an immediate): tile i+1 is in flight while tile i is computed; one
+//    barrier per tile.
 //  * Online softmax in base 2: scale*log2(e) is folded into one FMA per
 //    score, exp via v_exp_f32, the row sum via v_dot2 over the bf16-rounded
 //    weights.  The running max is only moved (and O rescaled) when a tile's
 //    max exceeds it by more than 2^8; weights then stay <= 256, which fp32
-//    and bf16 hold exactly as well as weights <= 1, and the result is the
-//    same softmax.
+//    and bf16 carry with the same relative precision as weights <= 1, and
+//    the normalised result is the same softmax.
 //  * Grid order: tiles of one (batch, KV head, head block) are consecutive
 //    on one XCD (the dispatcher deals workgroups round-robin over 8 XCDs, so
 //    the remap keeps a KV head's K/V in one L2), heaviest causal tiles first.
@@ -60,6 +62,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p)
     constexpr int DT = D / 32;                     // 32-row tiles of O^T
     constexpr int NINS = kBN * CPR / kThreads;     // async copies per thread per tensor
     static_assert(kBN * CPR % kThreads == 0, "tile must split evenly over the workgroup");
+    using Tile = PlaneTile<kBN>;
 
     __shared__ __attribute__((aligned(1024))) FwdSmem<D> sm;
 
@@ -77,7 +80,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p)
     const int b = bk / p.Hkv;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, w = tid >> 6;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
     const int col = lane & 31, hi = lane >> 5;
     const int head = kvh * p.G + hblk * p.Gt + (w % p.Gt);
     const int q0 = qt * p.Pt + (w / p.Gt) * 32;  // first query index of this wave
@@ -97,19 +101,29 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p)
     const uint16_t *kbase = p.k + (size_t)bk * p.Tk * D;
     const uint16_t *vbase = p.v + (size_t)bk * p.Tk * D;
 
-    // Async copy of keys [k0, k0 + 64) of K and V into ring slot `buf`.  LDS
-    // chunk Lc = row * CPR + slot holds global chunk slot ^ swz(row); rows
-    // past Tk re-read row Tk - 1 (in bounds; those keys are masked).
-    auto issue_tile = [&](int k0, int buf) {
+    // ---- async copies (plane layout, see PlaneTile) ----
+    // Copy j of this wave fills 16-byte slots 64 (j * 4 + w) + lane; the
+    // source (row, chunk) of each slot is fixed, so its element offset is
+    // computed once.  Rows past Tk re-read row Tk - 1 (in bounds, masked).
+    int grow_[NINS], goff_[NINS];
 #pragma unroll
-        for (int j = 0; j < NINS; ++j) {
-            const int base = (j * kNW + w) * 64;  // first LDS chunk of this wave's copy
-            const int Lc = base + lane;
-            const int row = Lc / CPR, slot = Lc % CPR;
-            const int c = slot ^ swz<CPR>(row);
-            const size_t grow = (size_t)min(k0 + row, p.Tk - 1) * D + c * 8;
-            g2lds16(kbase + grow, &sm.k[buf][base * 8]);
-            g2lds16(vbase + grow, &sm.v[buf][base * 8]);
+    for (int j = 0; j < NINS; ++j) {
+        int row, chunk;
+        Tile::slot_source((j * kNW + w) * 64 + lane, row, chunk);
+        grow_[j] = row;
+        goff_[j] = row * D + chunk * 8;
+    }
+    auto issue = [&](const uint16_t *src, uint16_t *dst, int k0) {
+        if (k0 + kBN <= p.Tk) {
+            const uint16_t *s0 = src + (size_t)k0 * D;
+#pragma unroll
+            for (int j = 0; j < NINS; ++j) g2lds16(s0 + goff_[j], dst + (j * kNW + w) * 64 * 8);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NINS; ++j) {
+                const int row = min(k0 + grow_[j], p.Tk - 1);
+                g2lds16(src + (size_t)row * D + (goff_[j] - grow_[j] * D), dst + (j * kNW + w) * 64 * 8);
+            }
         }
     };
 
@@ -133,125 +147,122 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p)
     float m_run = -INFINITY;  // running reference max of scaled scores (log2 units)
     float l_run = 0.f;        // this lane's half of the running sum
 
-    // per-lane LDS offsets (elements) that do not depend on the tile
-    int koff[2][KS];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int rr = 32 * t + kperm(col);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) koff[t][ks] = rr * D + (((2 * ks + hi) ^ swz<CPR>(rr)) * 8);
-    }
-    // V^T operand through transpose reads: lane = 16 g + i points at row
-    // 16 st + 8 (g >> 1) + 4 h + (i >> 2), columns 32 dt + 16 (g & 1) + 4 (i & 3)
+    // Per-lane LDS byte offsets; everything else in the tile loop is an
+    // immediate.  K operand: row 32 t + kperm(col), chunk 2 ks + hi.
+    const int krow = kperm(col);
+    const int kb_even = Tile::offset(krow, hi);     // chunks with (2 ks + hi) & 3 = hi
+    const int kb_odd = Tile::offset(krow, 2 + hi);  // and = 2 + hi
+    // V^T operand through transpose reads: lane 16 g + i points at row
+    // 16 st + 8 (g >> 1) + 4 h + (i >> 2), columns 32 dt + 16 (g & 1) + 4 (i & 3).
     const int vg = lane >> 4, vi = lane & 15;
-    int voff[4][2];  // [st][h], column part added per dt
-#pragma unroll
-    for (int st = 0; st < 4; ++st)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) voff[st][h] = 16 * st + 8 * (vg >> 1) + 4 * h + (vi >> 2);
+    const int vrow = 8 * (vg >> 1) + (vi >> 2), vchunk = 2 * (vg & 1) + ((vi >> 1) & 1);
+    const int vb_h0 = Tile::offset(vrow, vchunk) + 8 * (vi & 1);
+    const int vb_h1 = Tile::offset(vrow + 4, vchunk) + 8 * (vi & 1);
 
     const float c = p.c;
-    if (ntiles > 0) issue_tile(0, 0);
-    wait_vmem();
-    __syncthreads();
 
-    for (int it = 0; it < ntiles; ++it) {
-        const int k0 = it * kBN;
-        const int buf = it & 1;
-        if (it + 1 < ntiles) issue_tile(k0 + kBN, buf ^ 1);
-
-        if (wave_active && k0 <= wlast) {
-            const uint16_t *ks_ = sm.k[buf];
-            const uint16_t *vs_ = sm.v[buf];
-
-            // ---- S^T = K Q^T for 64 keys (two 32-key tiles) ----
-            f32x16 s[2];
+    // S^T = K Q^T for the 64 keys in a K ring slot
+    auto scores = [&](const char *ks_, f32x16 (&s)[2]) {
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < 2; ++t) {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) s[t][e] = 0.f;
+            for (int e = 0; e < 16; ++e) s[t][e] = 0.f;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    s[t] = mfma32x32x16(*(const u32x4 *)(ks_ + koff[t][ks]), qreg[ks], s[t]);
-            }
-
-            // ---- mask (diagonal and ragged tiles only) ----
-            const bool need_mask = (p.causal && k0 + kBN - 1 > off + q0) || (k0 + kBN > p.Tk);
-            if (need_mask) {
-#pragma unroll
-                for (int t = 0; t < 2; ++t)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        if (k0 + acc_key(t, e, hi) > lim) s[t][e] = -INFINITY;
-            }
-
-            // ---- online softmax (base 2, lazily rescaled) ----
-            float mx = s[0][0];
-#pragma unroll
-            for (int t = 0; t < 2; ++t)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t][e]);
-            mx = fmaxf(mx, wave_swap_half(mx));
-            const float mt = mx * c;
-            if (__any(mt > m_run + 8.0f)) {
-                // only lanes whose own max crossed the threshold move their
-                // reference, so a row never depends on keys it cannot see
-                const float m_new = (mt > m_run + 8.0f) ? mt : m_run;
-                const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-                m_run = m_new;
-                l_run *= alpha;
-#pragma unroll
-                for (int i = 0; i < DT; ++i)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
-            }
-            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-
-            u32x4 pb[4];
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    float pv[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[t][8 * h + e], c, -m_use));
-                    u32x4 pk;
-                    pk.x = pack_bf16x2(pv[0], pv[1]);
-                    pk.y = pack_bf16x2(pv[2], pv[3]);
-                    pk.z = pack_bf16x2(pv[4], pv[5]);
-                    pk.w = pack_bf16x2(pv[6], pv[7]);
-                    l_run = sum_bf16x8(pk, l_run);
-                    pb[2 * t + h] = pk;
-                }
-            }
-
-            // ---- O^T += V^T P^T ----
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const int cb = 32 * dt + 16 * (vg & 1) + 4 * (vi & 3);  // column of this lane's chunk
-                    u32x2 lo, hi2;
-                    {
-                        const int row = voff[st][0];
-                        lo = lds_read_tr16(vs_ + row * D + (((cb >> 3) ^ swz<CPR>(row)) * 8) + (cb & 7));
-                    }
-                    {
-                        const int row = voff[st][1];
-                        hi2 = lds_read_tr16(vs_ + row * D + (((cb >> 3) ^ swz<CPR>(row)) * 8) + (cb & 7));
-                    }
-                    u32x4 va = {lo.x, lo.y, hi2.x, hi2.y};
-                    o[dt] = mfma32x32x16(va, pb[st], o[dt]);
-                }
+            for (int ks = 0; ks < KS; ++ks) {
+                const int off_ = ((ks & 1) ? kb_odd : kb_even) + (ks >> 1) * Tile::PLANE_BYTES + t * 32 * 64;
+                s[t] = mfma32x32x16(*(const u32x4 *)(ks_ + off_), qreg[ks], s[t]);
             }
         }
+    };
+    // scaled max of a score tile (both lane halves combined)
+    auto tile_max = [&](const f32x16 (&s)[2]) {
+        float mx = s[0][0];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t][e]);
+        return halves_max(mx) * c;
+    };
+    // diagonal / ragged tiles: masked keys get -inf (rarely taken)
+    auto mask_tile = [&](int k0, f32x16 (&s)[2]) {
+        const bool need_mask = (p.causal && k0 + kBN - 1 > off + q0) || (k0 + kBN > p.Tk);
+        if (!need_mask) return false;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (k0 + acc_key(t, e, hi) > lim) s[t][e] = -INFINITY;
+        return true;
+    };
+
+    // Plain double buffer: tile it+1 is copied while tile it is computed.
+    auto step_plain = [&](int it) {
+        const int k0 = it * kBN;
+        if (!(wave_active && k0 <= wlast)) return;
+        f32x16 sc[2];
+        scores((const char *)sm.k[it & 1], sc);
+        mask_tile(k0, sc);
+        const float mt = tile_max(sc);
+        if (__any(mt > m_run + 8.0f)) {
+            const float m_new = (mt > m_run + 8.0f) ? mt : m_run;
+            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < DT; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        u32x4 pb[4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float pv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * h + e], c, -m_use));
+                u32x4 pk;
+                pk.x = pack_bf16x2(pv[0], pv[1]);
+                pk.y = pack_bf16x2(pv[2], pv[3]);
+                pk.z = pack_bf16x2(pv[4], pv[5]);
+                pk.w = pack_bf16x2(pv[6], pv[7]);
+                l_run = sum_bf16x8(pk, l_run);
+                pb[2 * t + h] = pk;
+            }
+        }
+        const char *vs_ = (const char *)sm.v[it & 1];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int o_ = dt * Tile::PLANE_BYTES + 16 * st * 64;
+                const u32x2 lo = lds_read_tr16(vs_ + vb_h0 + o_);
+                const u32x2 hv = lds_read_tr16(vs_ + vb_h1 + o_);
+                u32x4 va = {lo.x, lo.y, hv.x, hv.y};
+                o[dt] = mfma32x32x16(va, pb[st], o[dt]);
+            }
+        }
+    };
+    if (ntiles > 0) {
+        issue(kbase, sm.k[0], 0);
+        issue(vbase, sm.v[0], 0);
+    }
+    wait_vmem();
+    __syncthreads();
+    for (int it = 0; it < ntiles; ++it) {
+        if (it + 1 < ntiles) {
+            issue(kbase, sm.k[(it + 1) & 1], (it + 1) * kBN);
+            issue(vbase, sm.v[(it + 1) & 1], (it + 1) * kBN);
+        }
+        step_plain(it);
         wait_vmem();
-        __syncthreads();  // tile it+1 landed; everyone is done with slot `buf`
+        __syncthreads();
     }
 
     if (!wave_active || qi >= p.Tq) return;
-    const float l_tot = l_run + wave_swap_half(l_run);
+    const float l_tot = halves_sum(l_run);
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     uint16_t *orow = p.out + (((size_t)b * p.Hq + head) * p.Tq + qi) * D;
 #pragma unroll

@@ -71,12 +71,12 @@ __global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
     // wave copy j covers LDS chunks [64 j, 64 j + 64); waves take j = w, w + 8, ...
     // (36 copies: waves 0-3 do 5, waves 4-7 do 4; the count per wave is fixed)
     const int my_copies = (NCOPY - w + kNW - 1) / kNW;
+    using Tile = PlaneTile<kTK>;
     auto issue_tile = [&](int k0, int slot) {
         for (int j = w; j < NCOPY; j += kNW) {
-            const int Lc = j * 64 + lane;
-            const int row = Lc / kCPR, sl = Lc % kCPR;
-            const int c = sl ^ swz<kCPR>(row);
-            g2lds16(kb + (size_t)min(k0 + row, kend - 1) * p.k_st + c * 8, &sm.k[slot][j * 64 * 8]);
+            int row, chunk;
+            Tile::slot_source(j * 64 + lane, row, chunk);
+            g2lds16(kb + (size_t)min(k0 + row, kend - 1) * p.k_st + chunk * 8, &sm.k[slot][j * 64 * 8]);
         }
     };
 
@@ -99,8 +99,12 @@ __global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
     float m_run = -INFINITY, l_run = 0.f;
 
     const int krow = kperm(col);
-    const int kswz = swz<kCPR>(krow);
+    const int kbase_even = Tile::offset(krow, hi);
+    const int kbase_odd = Tile::offset(krow, 2 + hi);
     const int vg = lane >> 4, vi = lane & 15;
+    const int vrow = 8 * (vg >> 1) + (vi >> 2), vchunk = 2 * (vg & 1) + ((vi >> 1) & 1);
+    const int vb_h0 = Tile::offset(vrow, vchunk) + 8 * (vi & 1);      // rows 16 st + vrow
+    const int vb_h1 = Tile::offset(vrow + 4, vchunk) + 8 * (vi & 1);  // rows 16 st + vrow + 4
     float *xs_mine = &sm.xs[w][0];
     const float *xs_peer = &sm.xs[w ^ 4][0];
 
@@ -124,14 +128,15 @@ __global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
         __syncthreads();  // tile visible; the previous slot and exchange buffers are free
         if (it + kStages - 1 < ntiles) issue_tile(k0 + (kStages - 1) * kTK, (it + kStages - 1) % kStages);
 
-        const uint16_t *ks_ = sm.k[slot];
+        const char *ks_ = (const char *)sm.k[slot];
         f32x16 s;
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[e] = 0.f;
 #pragma unroll
         for (int ks = 0; ks < kKSH; ++ks) {
-            const int chunk = 36 * half + 2 * ks + hi;
-            s = mfma32x32x16(*(const u32x4 *)(ks_ + krow * kDK + ((chunk ^ kswz) * 8)), qreg[ks], s);
+            // chunk 36 half + 2 ks + hi lives in plane 9 half + ks / 2
+            const int off_ = ((ks & 1) ? kbase_odd : kbase_even) + (9 * half + (ks >> 1)) * Tile::PLANE_BYTES;
+            s = mfma32x32x16(*(const u32x4 *)(ks_ + off_), qreg[ks], s);
         }
         // swap partial scores with the partner wave (same heads, other half)
 #pragma unroll
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
         float mx = s[0];
 #pragma unroll
         for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
-        mx = fmaxf(mx, wave_swap_half(mx));
+        mx = halves_max(mx);
         const float mt = mx * c;
         if (__any(mt > m_run + 8.0f)) {
             const float m_new = (mt > m_run + 8.0f) ? mt : m_run;
@@ -187,17 +192,15 @@ __global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
             l_run = sum_bf16x8(pb[h], l_run);
         }
 
-        // O^T (this half's 256 dims) += V^T P^T, V^T = transpose of the latent prefix
+        // O^T (this half's 256 dims) += V^T P^T, V^T = transpose of the latent
+        // prefix: output dims 256 half + 32 dt + ... live in plane 8 half + dt
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-            const int r0 = 16 * st + 8 * (vg >> 1) + (vi >> 2);
-            const int r1 = r0 + 4;
-            const int sw0 = swz<kCPR>(r0), sw1 = swz<kCPR>(r1);
 #pragma unroll
             for (int dt = 0; dt < kDTH; ++dt) {
-                const int cb = 256 * half + 32 * dt + 16 * (vg & 1) + 4 * (vi & 3);
-                const u32x2 lo = lds_read_tr16(ks_ + r0 * kDK + (((cb >> 3) ^ sw0) * 8) + (cb & 7));
-                const u32x2 hv = lds_read_tr16(ks_ + r1 * kDK + (((cb >> 3) ^ sw1) * 8) + (cb & 7));
+                const int o_ = (8 * half + dt) * Tile::PLANE_BYTES + 16 * st * 64;
+                const u32x2 lo = lds_read_tr16(ks_ + vb_h0 + o_);
+                const u32x2 hv = lds_read_tr16(ks_ + vb_h1 + o_);
                 u32x4 va = {lo.x, lo.y, hv.x, hv.y};
                 o[dt] = mfma32x32x16(va, pb[st], o[dt]);
             }
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
     }
 
     if (!head_ok) return;
-    const float l_tot = l_run + wave_swap_half(l_run);
+    const float l_tot = halves_sum(l_run);
     const size_t prow = ((size_t)b * p.Hq + head) * p.S + split;
     float *po = p.part_o + prow * kDV + 256 * half;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
