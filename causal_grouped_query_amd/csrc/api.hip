@@ -123,11 +123,15 @@ GQA_API int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out,
         a.Tq = Tq;
         a.Tk = Tk;
         a.G = G;
-        const int rows = gqa::fwd_bf16_rows_per_block();  // 128 = 4 waves x 32 rows
+        // one wave owns one query head x rows_per_wave positions; a workgroup
+        // takes Gt heads of the group (largest power of two dividing both G
+        // and the wave count) x Pt positions
+        const int waves = gqa::fwd_bf16_waves_per_block();
+        const int rpw = gqa::fwd_bf16_rows_per_wave();
         int gt = 1;
-        while (gt * 2 <= rows / 32 && G % (gt * 2) == 0) gt *= 2;
+        while (gt * 2 <= waves && G % (gt * 2) == 0) gt *= 2;
         a.Gt = gt;
-        a.Pt = rows / gt;
+        a.Pt = rpw * (waves / gt);
         a.n_hblk = G / gt;
         a.n_qt = (Tq + a.Pt - 1) / a.Pt;
         const long long units = (long long)B * Hkv * a.n_hblk;

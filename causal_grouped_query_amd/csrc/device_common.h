@@ -18,6 +18,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 #define GQA_LDS __attribute__((address_space(3)))
+#define GQA_GLOBAL __attribute__((address_space(1)))
 
 // 32x32x16 bf16 MFMA, fp32 accumulate.  Operand lane layout (both A and B):
 // lane l holds row/column (l & 31) and 8 contraction slots owned by lane
@@ -138,6 +139,21 @@ struct PlaneTile {
 __device__ __forceinline__ void g2lds16(const void *gptr, void *lds_wave_base)
 {
     __builtin_amdgcn_global_load_lds(gptr, (GQA_LDS void *)lds_wave_base, 16, 0, 0);
+}
+
+// Same copy from a workgroup-uniform base plus a per-lane unsigned byte
+// offset: selects the scalar-base form (global_load_lds_dwordx4 v_off,
+// s[base]), so no per-lane 64-bit address arithmetic is needed.
+__device__ __forceinline__ void g2lds16(const void *uniform_base, unsigned byte_off, void *lds_wave_base)
+{
+    // readfirstlane keeps the base in SGPRs (and opaque to loop strength
+    // reduction, which would otherwise rebuild per-lane 64-bit pointers)
+    const unsigned long long a = (unsigned long long)uniform_base;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+    const GQA_GLOBAL char *b = (const GQA_GLOBAL char *)(((unsigned long long)hi << 32) | lo);
+    __builtin_amdgcn_global_load_lds((const GQA_GLOBAL void *)(b + byte_off), (GQA_LDS void *)lds_wave_base,
+                                     16, 0, 0);
 }
 
 // Wait for this wave's outstanding vector-memory operations (including

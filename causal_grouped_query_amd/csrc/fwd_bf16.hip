@@ -9,12 +9,13 @@
 // Tq x Tk matrix in HBM.
 //
 // gfx950 design
-//  * One workgroup = 4 waves = 128 query rows that all read ONE KV head:
-//    Gt query heads of the group x Pt positions (Gt * Pt = 128).  Each K/V
-//    tile is staged in LDS once and used by the whole group of heads; there
-//    is no repeat_interleave copy, the head map g(a) = a / (Hq/Hkv) is pure
-//    addressing.
-//  * A wave owns 32 query rows.  Scores are computed transposed,
+//  * One workgroup = NW waves that all read ONE KV head: Gt query heads of
+//    the group x Pt positions.  Each K/V tile is staged in LDS once and used
+//    by the whole group of heads; there is no repeat_interleave copy, the
+//    head map g(a) = a / (Hq/Hkv) is pure addressing.
+//  * A wave owns 32 * NC query rows (NC column blocks of the MFMA); every
+//    K operand and every V^T operand read from LDS feeds NC MFMAs, so LDS
+//    reads and HBM/L2 -> LDS copies per FLOP fall as 1 / NC.  Scores are computed transposed,
 //    S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: Q^T sits in registers as the
 //    B operand for the whole key loop, K rows come from LDS as the A operand.
 //    In the accumulator every lane holds one query column, so row max and row
@@ -43,24 +44,41 @@ namespace gqa {
 
 namespace {
 
-constexpr int kNW = 4;        // waves per workgroup
-constexpr int kBN = 64;       // keys per tile
+#ifndef GQA_FWD_NC
+#define GQA_FWD_NC 1      // 32-row column blocks per wave
+#endif
+#ifndef GQA_FWD_NW
+#define GQA_FWD_NW 4      // waves per workgroup
+#endif
+#ifndef GQA_FWD_STAGES
+#define GQA_FWD_STAGES 2  // K/V ring depth
+#endif
+#ifndef GQA_FWD_PREFETCH
+#define GQA_FWD_PREFETCH 6  // LDS operand reads kept in flight ahead of the MFMAs (0: compiler's choice)
+#endif
+constexpr int kNC = GQA_FWD_NC;
+constexpr int kNW = GQA_FWD_NW;
+constexpr int kBN = 64;           // keys per tile
+constexpr int kNT = kBN / 32;     // 32-key score tiles per key tile
+constexpr int kStages = GQA_FWD_STAGES;
 constexpr int kThreads = 64 * kNW;
+constexpr int kWavesPerSimd = kNC == 1 ? 2 : 1;  // register budget: 256 or 512 per lane
 
 template <int D>
 struct FwdSmem {
-    static constexpr int TILE = kBN * D;  // elements of one K or V tile (swizzled, unpadded)
-    uint16_t k[2][TILE];
-    uint16_t v[2][TILE];
+    static constexpr int TILE = kBN * D;  // elements of one K or V tile (plane layout)
+    uint16_t k[kStages][TILE];
+    uint16_t v[kStages][TILE];
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p)
+__global__ __launch_bounds__(kThreads, kWavesPerSimd) void fwd_bf16_kernel(FwdArgs p)
 {
     constexpr int CPR = D / 8;                     // 16-byte chunks per row
     constexpr int KS = D / 16;                     // MFMA k-steps over the head dim
     constexpr int DT = D / 32;                     // 32-row tiles of O^T
     constexpr int NINS = kBN * CPR / kThreads;     // async copies per thread per tensor
+    constexpr int ROWS = 32 * kNC;                 // query rows per wave
     static_assert(kBN * CPR % kThreads == 0, "tile must split evenly over the workgroup");
     using Tile = PlaneTile<kBN>;
 
@@ -84,9 +102,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p)
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
     const int col = lane & 31, hi = lane >> 5;
     const int head = kvh * p.G + hblk * p.Gt + (w % p.Gt);
-    const int q0 = qt * p.Pt + (w / p.Gt) * 32;  // first query index of this wave
-    const int off = p.Tk - p.Tq;                 // absolute position of query 0
-    const int qi = q0 + col;                     // this lane's query
+    const int q0 = qt * p.Pt + (w / p.Gt) * ROWS;  // first query index of this wave
+    const int off = p.Tk - p.Tq;                   // absolute position of query 0
     const bool wave_active = q0 < p.Tq;
 
     // keys the workgroup needs: [0, kend)
@@ -94,58 +111,71 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p)
     if (p.causal) kend = min(p.Tk, off + min(p.Tq, qt * p.Pt + p.Pt));
     const int ntiles = (kend + kBN - 1) / kBN;
     // last key any row of this wave can see
-    const int wlast = p.causal ? off + min(q0 + 31, p.Tq - 1) : p.Tk - 1;
-    // last key this lane's query can see
-    const int lim = p.causal ? min(off + qi, p.Tk - 1) : p.Tk - 1;
+    const int wlast = p.causal ? off + min(q0 + ROWS - 1, p.Tq - 1) : p.Tk - 1;
+    // last key each of this lane's queries can see
+    int lim[kNC];
+#pragma unroll
+    for (int cb = 0; cb < kNC; ++cb) lim[cb] = p.causal ? min(off + q0 + 32 * cb + col, p.Tk - 1) : p.Tk - 1;
 
     const uint16_t *kbase = p.k + (size_t)bk * p.Tk * D;
     const uint16_t *vbase = p.v + (size_t)bk * p.Tk * D;
 
     // ---- async copies (plane layout, see PlaneTile) ----
-    // Copy j of this wave fills 16-byte slots 64 (j * 4 + w) + lane; the
-    // source (row, chunk) of each slot is fixed, so its element offset is
-    // computed once.  Rows past Tk re-read row Tk - 1 (in bounds, masked).
-    int grow_[NINS], goff_[NINS];
+    // Copy j of this wave fills 16-byte slots 64 (j * NW + w) + lane; the
+    // source (row, chunk) of each slot is fixed, so its byte offset inside a
+    // tile is computed once.  Rows past Tk re-read row Tk - 1 (in bounds,
+    // masked).
+    int grow_[NINS];
+    unsigned goff_[NINS];
 #pragma unroll
     for (int j = 0; j < NINS; ++j) {
         int row, chunk;
         Tile::slot_source((j * kNW + w) * 64 + lane, row, chunk);
         grow_[j] = row;
-        goff_[j] = row * D + chunk * 8;
+        goff_[j] = (unsigned)(row * D + chunk * 8) * 2u;
     }
     auto issue = [&](const uint16_t *src, uint16_t *dst, int k0) {
         if (k0 + kBN <= p.Tk) {
             const uint16_t *s0 = src + (size_t)k0 * D;
 #pragma unroll
-            for (int j = 0; j < NINS; ++j) g2lds16(s0 + goff_[j], dst + (j * kNW + w) * 64 * 8);
+            for (int j = 0; j < NINS; ++j) g2lds16(s0, goff_[j], dst + (j * kNW + w) * 64 * 8);
         } else {
 #pragma unroll
             for (int j = 0; j < NINS; ++j) {
                 const int row = min(k0 + grow_[j], p.Tk - 1);
-                g2lds16(src + (size_t)row * D + (goff_[j] - grow_[j] * D), dst + (j * kNW + w) * 64 * 8);
+                g2lds16((const char *)(src + (size_t)row * D) + (goff_[j] - (unsigned)grow_[j] * D * 2u),
+                        dst + (j * kNW + w) * 64 * 8);
             }
         }
     };
 
-    // ---- Q^T in registers (B operand), zero for rows past Tq ----
-    u32x4 qreg[KS];
-    {
+    // ---- Q^T in registers (B operands), zero for rows past Tq ----
+    u32x4 qreg[kNC][KS];
+#pragma unroll
+    for (int cb = 0; cb < kNC; ++cb) {
+        const int qi = q0 + 32 * cb + col;
         const bool ok = wave_active && qi < p.Tq;
         const uint16_t *qrow = p.q + (((size_t)b * p.Hq + head) * p.Tq + (ok ? qi : 0)) * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 z = {0u, 0u, 0u, 0u};
-            qreg[ks] = ok ? *(const u32x4 *)(qrow + 16 * ks + 8 * hi) : z;
+            qreg[cb][ks] = ok ? *(const u32x4 *)(qrow + 16 * ks + 8 * hi) : z;
         }
     }
 
-    f32x16 o[DT];
+    f32x16 o[kNC][DT];
 #pragma unroll
-    for (int i = 0; i < DT; ++i)
+    for (int cb = 0; cb < kNC; ++cb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
-    float m_run = -INFINITY;  // running reference max of scaled scores (log2 units)
-    float l_run = 0.f;        // this lane's half of the running sum
+        for (int i = 0; i < DT; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[cb][i][e] = 0.f;
+    float m_run[kNC], l_run[kNC];  // running reference max (log2 units), this lane's half of the sum
+#pragma unroll
+    for (int cb = 0; cb < kNC; ++cb) {
+        m_run[cb] = -INFINITY;
+        l_run[cb] = 0.f;
+    }
 
     // Per-lane LDS byte offsets; everything else in the tile loop is an
     // immediate.  K operand: row 32 t + kperm(col), chunk 2 ks + hi.
@@ -161,119 +191,175 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdArgs p)
 
     const float c = p.c;
 
-    // S^T = K Q^T for the 64 keys in a K ring slot
-    auto scores = [&](const char *ks_, f32x16 (&s)[2]) {
+    // One tile: S^T = K Q^T (each K operand feeds NC MFMAs), mask on
+    // diagonal / ragged tiles, online softmax, O^T += V^T P^T (each V^T
+    // operand feeds NC MFMAs).
+    auto step = [&](int it) {
+        const int k0 = it * kBN;
+        if (!(wave_active && k0 <= wlast)) return;
+        const char *ks_ = (const char *)sm.k[it % kStages];
+        f32x16 sc[kNC][kNT];
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int cb = 0; cb < kNC; ++cb)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) s[t][e] = 0.f;
+            for (int t = 0; t < kNT; ++t)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) sc[cb][t][e] = 0.f;
+#pragma unroll
+        for (int t = 0; t < kNT; ++t) {
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 const int off_ = ((ks & 1) ? kb_odd : kb_even) + (ks >> 1) * Tile::PLANE_BYTES + t * 32 * 64;
-                s[t] = mfma32x32x16(*(const u32x4 *)(ks_ + off_), qreg[ks], s[t]);
+                const u32x4 a = *(const u32x4 *)(ks_ + off_);
+#pragma unroll
+                for (int cb = 0; cb < kNC; ++cb) sc[cb][t] = mfma32x32x16(a, qreg[cb][ks], sc[cb][t]);
             }
         }
-    };
-    // scaled max of a score tile (both lane halves combined)
-    auto tile_max = [&](const f32x16 (&s)[2]) {
-        float mx = s[0][0];
+#if GQA_FWD_PREFETCH
+        {
+            // schedule: PREFETCH operand reads first, then one MFMA group per
+            // further read, so the LDS latency overlaps earlier MFMAs
+            constexpr int NR = kNT * KS, PF = GQA_FWD_PREFETCH < NR ? GQA_FWD_PREFETCH : NR;
+            __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[t][e]);
-        return halves_max(mx) * c;
-    };
-    // diagonal / ragged tiles: masked keys get -inf (rarely taken)
-    auto mask_tile = [&](int k0, f32x16 (&s)[2]) {
-        const bool need_mask = (p.causal && k0 + kBN - 1 > off + q0) || (k0 + kBN > p.Tk);
-        if (!need_mask) return false;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                if (k0 + acc_key(t, e, hi) > lim) s[t][e] = -INFINITY;
-        return true;
-    };
+            for (int i = 0; i < NR - PF; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, kNC, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kNC * PF, 0);
+        }
+#endif
 
-    // Plain double buffer: tile it+1 is copied while tile it is computed.
-    auto step_plain = [&](int it) {
-        const int k0 = it * kBN;
-        if (!(wave_active && k0 <= wlast)) return;
-        f32x16 sc[2];
-        scores((const char *)sm.k[it & 1], sc);
-        mask_tile(k0, sc);
-        const float mt = tile_max(sc);
-        if (__any(mt > m_run + 8.0f)) {
-            const float m_new = (mt > m_run + 8.0f) ? mt : m_run;
-            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
+        const bool need_mask = (p.causal && k0 + kBN - 1 > off + q0) || (k0 + kBN > p.Tk);
+        if (need_mask) {
 #pragma unroll
-            for (int i = 0; i < DT; ++i)
+            for (int cb = 0; cb < kNC; ++cb)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+                for (int t = 0; t < kNT; ++t)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        if (k0 + acc_key(t, e, hi) > lim[cb]) sc[cb][t][e] = -INFINITY;
         }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        u32x4 pb[4];
+
+        // online softmax (base 2); the reference max of a lane's query only
+        // moves (and its O column is rescaled) when a tile max exceeds it by
+        // more than 2^8 -- and only for that lane, so a row never depends on
+        // keys it cannot see
+        float mt[kNC];
+        bool any_move = false;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int cb = 0; cb < kNC; ++cb) {
+            float mx = sc[cb][0][0];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                float pv[8];
+            for (int t = 0; t < kNT; ++t)
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * h + e], c, -m_use));
-                u32x4 pk;
-                pk.x = pack_bf16x2(pv[0], pv[1]);
-                pk.y = pack_bf16x2(pv[2], pv[3]);
-                pk.z = pack_bf16x2(pv[4], pv[5]);
-                pk.w = pack_bf16x2(pv[6], pv[7]);
-                l_run = sum_bf16x8(pk, l_run);
-                pb[2 * t + h] = pk;
+                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[cb][t][e]);
+            mt[cb] = halves_max(mx) * c;
+            any_move |= mt[cb] > m_run[cb] + 8.0f;
+        }
+        if (__any(any_move)) {
+#pragma unroll
+            for (int cb = 0; cb < kNC; ++cb) {
+                const float m_new = (mt[cb] > m_run[cb] + 8.0f) ? mt[cb] : m_run[cb];
+                const float alpha =
+                    (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[cb] - m_new);
+                m_run[cb] = m_new;
+                l_run[cb] *= alpha;
+#pragma unroll
+                for (int i = 0; i < DT; ++i)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) o[cb][i][e] *= alpha;
             }
         }
-        const char *vs_ = (const char *)sm.v[it & 1];
+        u32x4 pb[kNC][2 * kNT];
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
+        for (int cb = 0; cb < kNC; ++cb) {
+            const float m_use = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];
+#pragma unroll
+            for (int t = 0; t < kNT; ++t) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    float pv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cb][t][8 * h + e], c, -m_use));
+                    u32x4 pk;
+                    pk.x = pack_bf16x2(pv[0], pv[1]);
+                    pk.y = pack_bf16x2(pv[2], pv[3]);
+                    pk.z = pack_bf16x2(pv[4], pv[5]);
+                    pk.w = pack_bf16x2(pv[6], pv[7]);
+                    l_run[cb] = sum_bf16x8(pk, l_run[cb]);
+                    pb[cb][2 * t + h] = pk;
+                }
+            }
+        }
+
+        const char *vs_ = (const char *)sm.v[it % kStages];
+#pragma unroll
+        for (int st = 0; st < 2 * kNT; ++st) {
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) {
                 const int o_ = dt * Tile::PLANE_BYTES + 16 * st * 64;
                 const u32x2 lo = lds_read_tr16(vs_ + vb_h0 + o_);
                 const u32x2 hv = lds_read_tr16(vs_ + vb_h1 + o_);
-                u32x4 va = {lo.x, lo.y, hv.x, hv.y};
-                o[dt] = mfma32x32x16(va, pb[st], o[dt]);
+                const u32x4 va = {lo.x, lo.y, hv.x, hv.y};
+#pragma unroll
+                for (int cb = 0; cb < kNC; ++cb) o[cb][dt] = mfma32x32x16(va, pb[cb][st], o[cb][dt]);
             }
         }
-    };
-    if (ntiles > 0) {
-        issue(kbase, sm.k[0], 0);
-        issue(vbase, sm.v[0], 0);
-    }
-    wait_vmem();
-    __syncthreads();
-    for (int it = 0; it < ntiles; ++it) {
-        if (it + 1 < ntiles) {
-            issue(kbase, sm.k[(it + 1) & 1], (it + 1) * kBN);
-            issue(vbase, sm.v[(it + 1) & 1], (it + 1) * kBN);
+#if GQA_FWD_PREFETCH
+        {
+            constexpr int NM = 2 * kNT * DT, PF = GQA_FWD_PREFETCH < NM ? GQA_FWD_PREFETCH : NM;
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+            for (int i = 0; i < NM - PF; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, kNC, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kNC * PF, 0);
         }
-        step_plain(it);
-        wait_vmem();
-        __syncthreads();
+#endif
+    };
+
+    // ring of kStages K/V slots: kStages - 1 tiles in flight while one is computed
+#pragma unroll
+    for (int s_ = 0; s_ < kStages - 1; ++s_)
+        if (s_ < ntiles) {
+            issue(kbase, sm.k[s_], s_ * kBN);
+            issue(vbase, sm.v[s_], s_ * kBN);
+        }
+    for (int it = 0; it < ntiles; ++it) {
+        if (it + kStages - 2 < ntiles)
+            wait_vmem_le<(kStages - 2) * 2 * NINS>();  // tile it landed; later ones may fly
+        else
+            wait_vmem();
+        __syncthreads();  // tile it visible; the slot of tile it-1 is free
+        const int nx = it + kStages - 1;
+        if (nx < ntiles) {
+            issue(kbase, sm.k[nx % kStages], nx * kBN);
+            issue(vbase, sm.v[nx % kStages], nx * kBN);
+        }
+        step(it);
     }
 
-    if (!wave_active || qi >= p.Tq) return;
-    const float l_tot = halves_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    uint16_t *orow = p.out + (((size_t)b * p.Hq + head) * p.Tq + qi) * D;
+    if (!wave_active) return;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int cb = 0; cb < kNC; ++cb) {
+        const int qi = q0 + 32 * cb + col;
+        if (qi >= p.Tq) continue;
+        const float l_tot = halves_sum(l_run[cb]);
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        uint16_t *orow = p.out + (((size_t)b * p.Hq + head) * p.Tq + qi) * D;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int d = 32 * dt + 8 * j + 4 * hi;
-            u32x2 pk;
-            pk.x = pack_bf16x2(o[dt][4 * j + 0] * inv, o[dt][4 * j + 1] * inv);
-            pk.y = pack_bf16x2(o[dt][4 * j + 2] * inv, o[dt][4 * j + 3] * inv);
-            *(u32x2 *)(orow + d) = pk;
+        for (int dt = 0; dt < DT; ++dt) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = 32 * dt + 8 * j + 4 * hi;
+                u32x2 pk;
+                pk.x = pack_bf16x2(o[cb][dt][4 * j + 0] * inv, o[cb][dt][4 * j + 1] * inv);
+                pk.y = pack_bf16x2(o[cb][dt][4 * j + 2] * inv, o[cb][dt][4 * j + 3] * inv);
+                *(u32x2 *)(orow + d) = pk;
+            }
         }
     }
 }
@@ -294,6 +380,7 @@ int launch_fwd_bf16(const FwdArgs &a, int D, hipStream_t stream)
     return 0;
 }
 
-int fwd_bf16_rows_per_block() { return 32 * kNW; }
+int fwd_bf16_waves_per_block() { return kNW; }
+int fwd_bf16_rows_per_wave() { return 32 * kNC; }
 
 } // namespace gqa

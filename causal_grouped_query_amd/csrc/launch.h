@@ -15,7 +15,7 @@ struct FwdArgs {
     uint16_t *out;
     int B, Hq, Hkv, Tq, Tk;
     int G;       // Hq / Hkv
-    int Gt;      // query heads per workgroup (divides G)
+    int Gt;      // query heads per workgroup (divides G and the wave count)
     int Pt;      // query positions per workgroup (Gt * Pt = rows per workgroup)
     int n_hblk;  // G / Gt
     int n_qt;    // ceil(Tq / Pt)
@@ -25,7 +25,8 @@ struct FwdArgs {
 };
 
 int launch_fwd_bf16(const FwdArgs &a, int D, hipStream_t stream);
-int fwd_bf16_rows_per_block();
+int fwd_bf16_waves_per_block();
+int fwd_bf16_rows_per_wave();
 
 // Split-KV decode partials over a strided cache.
 struct DecodeArgs {
