@@ -190,6 +190,8 @@ GQA_API int gqa_attn_decode(const void *q, const void *k, const void *v, void *o
     if (k_sb <= 0 || k_sh <= 0 || k_st <= 0 || v_sb <= 0 || v_sh <= 0 || v_st <= 0)
         return GQA_ERR_INVALID_ARG;
     if (k_st < Dk || v_st < Dv) return GQA_ERR_INVALID_ARG;  // rows may not overlap
+    // the kernels address a 32-key tile with 32-bit byte offsets
+    if (k_st > (1LL << 25) || v_st > (1LL << 25)) return GQA_ERR_UNSUPPORTED;
     if (num_splits < 0 || num_splits > kMaxSplits) return GQA_ERR_INVALID_ARG;
     if (!head_dims_decode(Dk, Dv, dtype)) return GQA_ERR_UNSUPPORTED;
     if (Dk == 576 && !(v == k && v_sb == k_sb && v_sh == k_sh && v_st == k_st))
@@ -239,7 +241,7 @@ GQA_API int gqa_attn_decode(const void *q, const void *k, const void *v, void *o
     if (dtype == GQA_BF16) {
         const int hpb = gqa::decode_bf16_heads_per_block(Dk, G);
         a.n_hblk = (G + hpb - 1) / hpb;
-        if ((long long)B * Hkv > 65535 || a.n_hblk > 65535) return GQA_ERR_UNSUPPORTED;
+        if ((long long)B * Hkv * S > 0x7fffffffLL || a.n_hblk > 65535) return GQA_ERR_UNSUPPORTED;
         a.c = folded_scale(scale);
         (void)hipGetLastError();
         rc = gqa::launch_decode_bf16(a, Dk, Dv, st);

@@ -26,6 +26,9 @@ namespace gqa {
 namespace {
 
 constexpr int kTK = 32;  // keys per tile
+#ifndef GQA_DEC_STAGES
+#define GQA_DEC_STAGES 2  // K/V ring depth for the 128-dim kernel
+#endif
 
 template <int DK, int DV, int STAGES>
 struct DecSmem {
@@ -48,12 +51,17 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kern
 
     __shared__ __attribute__((aligned(1024))) DecSmem<DK, DV, STAGES> sm;
 
-    const int split = blockIdx.x;
+    // chunk-major order: every sequence's first chunk is dispatched before
+    // any second chunk, so full chunks start first and the short / empty
+    // ones of ragged lengths fill the tail
+    const int nbk = p.B * p.Hkv;
+    const int split = blockIdx.x / nbk;
+    const int bk = blockIdx.x - split * nbk;  // b * Hkv + kv head
     const int hblk = blockIdx.y;
-    const int bk = blockIdx.z;  // b * Hkv + kv head
     const int kvh = bk % p.Hkv, b = bk / p.Hkv;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 31, hi = lane >> 5;
     const int hh = (hblk * NW + w) * 32 + col;  // head within the group
     const bool head_ok = hh < p.G;
@@ -72,20 +80,46 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kern
     // see PlaneTile); rows past the chunk end re-read its last key (in
     // bounds; masked below).
     using Tile = PlaneTile<kTK>;
+    // per-lane byte offsets of each copy's source inside a tile (row, chunk)
+    int krow_[KINS], vrow_[VINS];
+    unsigned koff_[KINS], voff_[VINS];
+#pragma unroll
+    for (int j = 0; j < KINS; ++j) {
+        int row, chunk;
+        Tile::slot_source((j * NW + w) * 64 + lane, row, chunk);
+        krow_[j] = row;
+        koff_[j] = (unsigned)(row * p.k_st + chunk * 8) * 2u;
+    }
+#pragma unroll
+    for (int j = 0; j < VINS; ++j) {
+        int row, chunk;
+        Tile::slot_source((j * NW + w) * 64 + lane, row, chunk);
+        vrow_[j] = row;
+        voff_[j] = (unsigned)(row * p.v_st + chunk * 8) * 2u;
+    }
     auto issue_tile = [&](int k0, int slot) {
+        if (k0 + kTK <= kend) {
+            const uint16_t *k0p = kb + (size_t)k0 * p.k_st;
+            const uint16_t *v0p = vb + (size_t)k0 * p.v_st;
 #pragma unroll
-        for (int j = 0; j < KINS; ++j) {
-            const int base = (j * NW + w) * 64;
-            int row, chunk;
-            Tile::slot_source(base + lane, row, chunk);
-            g2lds16(kb + (size_t)min(k0 + row, kend - 1) * p.k_st + chunk * 8, &sm.k[slot][base * 8]);
-        }
+            for (int j = 0; j < KINS; ++j) g2lds16(k0p, koff_[j], &sm.k[slot][(j * NW + w) * 64 * 8]);
 #pragma unroll
-        for (int j = 0; j < VINS; ++j) {
-            const int base = (j * NW + w) * 64;
-            int row, chunk;
-            Tile::slot_source(base + lane, row, chunk);
-            g2lds16(vb + (size_t)min(k0 + row, kend - 1) * p.v_st + chunk * 8, &sm.v[slot][base * 8]);
+            for (int j = 0; j < VINS; ++j) g2lds16(v0p, voff_[j], &sm.v[slot][(j * NW + w) * 64 * 8]);
+        } else {
+            // ragged last tile: rows past the chunk end re-read its last key
+            // (in bounds; masked below)
+#pragma unroll
+            for (int j = 0; j < KINS; ++j) {
+                const int row = min(k0 + krow_[j], kend - 1);
+                g2lds16((const char *)(kb + (size_t)row * p.k_st) + (koff_[j] - (unsigned)(krow_[j] * p.k_st) * 2u),
+                        &sm.k[slot][(j * NW + w) * 64 * 8]);
+            }
+#pragma unroll
+            for (int j = 0; j < VINS; ++j) {
+                const int row = min(k0 + vrow_[j], kend - 1);
+                g2lds16((const char *)(vb + (size_t)row * p.v_st) + (voff_[j] - (unsigned)(vrow_[j] * p.v_st) * 2u),
+                        &sm.v[slot][(j * NW + w) * 64 * 8]);
+            }
         }
     };
 
@@ -214,7 +248,7 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kern
 template <int DK, int DV, int NW, int STAGES>
 int launch_one(const DecodeArgs &a, hipStream_t stream)
 {
-    dim3 grid(a.S, a.n_hblk, a.B * a.Hkv), block(64 * NW);
+    dim3 grid(a.S * a.B * a.Hkv, a.n_hblk), block(64 * NW);
     hipLaunchKernelGGL((decode_bf16_kernel<DK, DV, NW, STAGES>), grid, block, 0, stream, a);
     return 0;
 }
@@ -233,7 +267,7 @@ int decode_bf16_heads_per_block(int Dk, int G)
 
 int launch_decode_bf16(const DecodeArgs &a, int Dk, int Dv, hipStream_t stream)
 {
-    if (Dk == 128 && Dv == 128) return launch_one<128, 128, 1, 2>(a, stream);
+    if (Dk == 128 && Dv == 128) return launch_one<128, 128, 1, GQA_DEC_STAGES>(a, stream);
     if (Dk == 64 && Dv == 64) return launch_one<64, 64, 1, 3>(a, stream);
     if (Dk == 576 && Dv == 512) {
         // the value must be the latent prefix of the key (v == k, same strides)

@@ -48,9 +48,11 @@ __global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
     constexpr int NCOPY = kTK * kCPR / 64;  // 36 wave-copies per tile, spread over 8 waves
     __shared__ __attribute__((aligned(1024))) MlaSmem sm;
 
-    const int split = blockIdx.x;
+    // chunk-major order, as in the other decode kernel
+    const int nbk = p.B * p.Hkv;
+    const int split = blockIdx.x / nbk;
+    const int bk = blockIdx.x - split * nbk;  // b * Hkv + kv head
     const int hblk = blockIdx.y;
-    const int bk = blockIdx.z;  // b * Hkv + kv head
     const int kvh = bk % p.Hkv, b = bk / p.Hkv;
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -227,7 +229,7 @@ __global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
 
 int launch_mla_decode(const DecodeArgs &a, hipStream_t stream)
 {
-    dim3 grid(a.S, a.n_hblk, a.B * a.Hkv), block(kNT);
+    dim3 grid(a.S * a.B * a.Hkv, a.n_hblk), block(kNT);
     hipLaunchKernelGGL(mla_decode_kernel, grid, block, 0, stream, a);
     return 0;
 }
