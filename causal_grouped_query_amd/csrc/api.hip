@@ -66,9 +66,15 @@ int default_splits(int B, int Hq, int Hkv, int Tmax, int Dk)
         if (s > 64) s = 64;
         return (int)s;
     }
-    // small head dims: ~512-key chunks keep thousands of single-wave
-    // workgroups in flight and bound the imbalance of ragged lengths
-    long long s = (Tmax + 511) / 512;
+    // small head dims: single-wave workgroups, ~5 resident per CU.  Aim for
+    // ~2.5 workgroups per resident slot if every sequence were full length
+    // (ragged lengths leave many chunks short or empty, and chunk-major
+    // dispatch puts those in the tail), with chunks of at least 256 keys.
+    groups = (long long)B * Hkv * ((G + 31) / 32);
+    min_chunk = 256;
+    long long s = (3200 + groups - 1) / groups;
+    long long cap = (Tmax + min_chunk - 1) / min_chunk;
+    if (s > cap) s = cap;
     if (s < 1) s = 1;
     if (s > 64) s = 64;
     return (int)s;

@@ -33,6 +33,9 @@ constexpr int kDV = 512;     // value width (the latent)
 constexpr int kNW = 8;       // waves per workgroup
 constexpr int kNT = 64 * kNW;
 constexpr int kStages = 3;
+#ifndef GQA_MLA_PREFETCH
+#define GQA_MLA_PREFETCH 0  // LDS operand reads kept in flight ahead of the MFMAs (spills if > 0)
+#endif
 constexpr int kCPR = kDK / 8;              // 72 16-byte chunks per key row
 constexpr int kKSH = kDK / 16 / 2;         // 18 MFMA k-steps per half
 constexpr int kDTH = kDV / 32 / 2;         // 8 output tiles per half
@@ -140,6 +143,16 @@ __global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
             const int off_ = ((ks & 1) ? kbase_odd : kbase_even) + (9 * half + (ks >> 1)) * Tile::PLANE_BYTES;
             s = mfma32x32x16(*(const u32x4 *)(ks_ + off_), qreg[ks], s);
         }
+#if GQA_MLA_PREFETCH
+        // keep GQA_MLA_PREFETCH operand reads in flight ahead of the MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, GQA_MLA_PREFETCH, 0);
+#pragma unroll
+        for (int i = 0; i < kKSH - GQA_MLA_PREFETCH; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, GQA_MLA_PREFETCH, 0);
+#endif
         // swap partial scores with the partner wave (same heads, other half)
 #pragma unroll
         for (int e = 0; e < 16; e += 4) {
@@ -207,6 +220,15 @@ __global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
                 o[dt] = mfma32x32x16(va, pb[st], o[dt]);
             }
         }
+#if GQA_MLA_PREFETCH
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * GQA_MLA_PREFETCH, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * kDTH - GQA_MLA_PREFETCH; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, GQA_MLA_PREFETCH, 0);
+#endif
     }
 
     if (!head_ok) return;
