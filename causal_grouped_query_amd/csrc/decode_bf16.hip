@@ -131,6 +131,8 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kern
             u32x4 z = {0u, 0u, 0u, 0u};
             qreg[ks] = head_ok ? *(const u32x4 *)(qrow + 16 * ks + 8 * hi) : z;
         }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) hold_reg(qreg[ks]);
     }
 
     f32x16 o[DT];
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kern
             wait_vmem_le<(STAGES - 2) * NI>();  // tile `it` landed, later ones may fly
         else
             wait_vmem();
-        __syncthreads();  // tile visible to all waves; slot of tile it-1 is free
+        lds_barrier();  // tile visible to all waves; slot of tile it-1 is free
         if (it + STAGES - 1 < ntiles) issue_tile(k0 + (STAGES - 1) * kTK, (it + STAGES - 1) % STAGES);
 
         const char *ks_ = (const char *)sm.k[slot];

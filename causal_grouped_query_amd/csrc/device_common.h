@@ -136,24 +136,58 @@ struct PlaneTile {
 // Asynchronous global -> LDS copy of 16 bytes per lane (gfx950
 // global_load_lds_dwordx4).  Lane l's bytes land at lds_wave_base + 16*l;
 // lds_wave_base must be the same for the whole wave.
+//
+// The copies are written as inline assembly on purpose.  Seen as builtins,
+// the compiler treats every later LDS transpose read and every workgroup
+// barrier as depending on all copies still in flight and drains them
+// (s_waitcnt vmcnt(0)), which turns a multi-stage K/V ring into a single
+// stage.  Here the compiler knows nothing of the copies: every wait on them
+// is explicit (wait_vmem / wait_vmem_le before lds_barrier).  The
+// instructions have no register results; they only read their address
+// operands at issue.  M0 carries the LDS base (1 wait state before the copy).
+__device__ __forceinline__ unsigned lds_u32(const void *lds_ptr)
+{
+    return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(GQA_LDS const void *)lds_ptr);
+}
+
 __device__ __forceinline__ void g2lds16(const void *gptr, void *lds_wave_base)
 {
-    __builtin_amdgcn_global_load_lds(gptr, (GQA_LDS void *)lds_wave_base, 16, 0, 0);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+                 "s"(lds_u32(lds_wave_base))
+                 : "memory");
 }
 
 // Same copy from a workgroup-uniform base plus a per-lane unsigned byte
-// offset: selects the scalar-base form (global_load_lds_dwordx4 v_off,
-// s[base]), so no per-lane 64-bit address arithmetic is needed.
+// offset (scalar-base form: no per-lane 64-bit address arithmetic).
 __device__ __forceinline__ void g2lds16(const void *uniform_base, unsigned byte_off, void *lds_wave_base)
 {
-    // readfirstlane keeps the base in SGPRs (and opaque to loop strength
-    // reduction, which would otherwise rebuild per-lane 64-bit pointers)
     const unsigned long long a = (unsigned long long)uniform_base;
     const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
     const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
-    const GQA_GLOBAL char *b = (const GQA_GLOBAL char *)(((unsigned long long)hi << 32) | lo);
-    __builtin_amdgcn_global_load_lds((const GQA_GLOBAL void *)(b + byte_off), (GQA_LDS void *)lds_wave_base,
-                                     16, 0, 0);
+    const unsigned long long base = ((unsigned long long)hi << 32) | lo;
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(byte_off), "s"(base),
+                 "s"(lds_u32(lds_wave_base))
+                 : "memory");
+}
+
+// Complete a register's pending global load here: the compiler waits for it
+// before an asm statement that reads the register.  Without this, a value
+// loaded before a loop whose copies are issued as inline assembly can leave a
+// (needlessly full) vmcnt wait inside the loop body.
+template <typename T>
+__device__ __forceinline__ void hold_reg(const T &x)
+{
+    asm volatile("" ::"v"(x));
+}
+
+// Workgroup barrier for LDS hand-off: this wave's LDS reads and writes are
+// complete (lgkmcnt(0)) before it arrives.  Unlike __syncthreads it does not
+// drain outstanding vector-memory operations, so copies for later tiles stay
+// in flight across it; the copies a reader needs must be waited for (by every
+// wave, for its own copies) before the barrier.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // Wait for this wave's outstanding vector-memory operations (including

@@ -162,6 +162,10 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void fwd_bf16_kernel(FwdAr
             qreg[cb][ks] = ok ? *(const u32x4 *)(qrow + 16 * ks + 8 * hi) : z;
         }
     }
+#pragma unroll
+    for (int cb = 0; cb < kNC; ++cb)
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) hold_reg(qreg[cb][ks]);
 
     f32x16 o[kNC][DT];
 #pragma unroll
@@ -333,7 +337,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void fwd_bf16_kernel(FwdAr
             wait_vmem_le<(kStages - 2) * 2 * NINS>();  // tile it landed; later ones may fly
         else
             wait_vmem();
-        __syncthreads();  // tile it visible; the slot of tile it-1 is free
+        lds_barrier();  // tile it visible; the slot of tile it-1 is free
         const int nx = it + kStages - 1;
         if (nx < ntiles) {
             issue(kbase, sm.k[nx % kStages], nx * kBN);
@@ -363,6 +367,7 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void fwd_bf16_kernel(FwdAr
         }
     }
 }
+
 
 } // namespace
 

@@ -94,6 +94,8 @@ __global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
             u32x4 z = {0u, 0u, 0u, 0u};
             qreg[ks] = head_ok ? *(const u32x4 *)(qrow + 16 * ks + 8 * hi) : z;
         }
+#pragma unroll
+        for (int ks = 0; ks < kKSH; ++ks) hold_reg(qreg[ks]);
     }
 
     f32x16 o[kDTH];
@@ -130,7 +132,7 @@ __global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
         } else {
             wait_vmem();
         }
-        __syncthreads();  // tile visible; the previous slot and exchange buffers are free
+        lds_barrier();  // tile visible; the previous slot and exchange buffers are free
         if (it + kStages - 1 < ntiles) issue_tile(k0 + (kStages - 1) * kTK, (it + kStages - 1) % kStages);
 
         const char *ks_ = (const char *)sm.k[slot];
@@ -159,7 +161,7 @@ __global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
             f32x4 v4 = {s[e], s[e + 1], s[e + 2], s[e + 3]};
             *(f32x4 *)(xs_mine + e * 64 + 4 * lane) = v4;
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int e = 0; e < 16; e += 4) {
             // (fp addition commutes, so both waves get bit-identical sums)
