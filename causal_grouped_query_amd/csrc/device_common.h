@@ -31,6 +31,15 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const u32x4 &a, const u32x4 &b, c
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// 16x16x32 bf16 MFMA, fp32 accumulate.  Lane l holds row/column (l & 15)
+// and contraction slots 8*(l>>4) .. +7 of A and B; accumulator element i is
+// row 4*(l>>4) + i, column (l & 15).
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4 &a, const u32x4 &b, const f32x4 &c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 // Round-to-nearest-even fp32 -> bf16 for two values, packed lo | hi << 16.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
@@ -115,13 +124,22 @@ __device__ __forceinline__ int pswz(int r)
 #endif
 }
 
-template <int R>
+// Swizzle used by the 16x16x32 operand reads of the absorbed-MLA kernel
+// (A rows 16 t + (l & 15), chunk l >> 4; V^T transpose rows 4 (l >> 4) + r):
+// measured free of LDS bank conflicts for both read shapes; pswz is not.
+__device__ __forceinline__ int pswz16(int r)
+{
+    return (__builtin_popcount(r & 7) & 1) | ((__builtin_popcount(r & 5) & 1) << 1);
+}
+
+template <int R, bool SW16 = false>
 struct PlaneTile {
     static constexpr int PLANE_BYTES = R * 64;
+    static __device__ __forceinline__ int swz(int r) { return SW16 ? pswz16(r) : pswz(r); }
     // byte offset of chunk c of row r
     static __device__ __forceinline__ int offset(int r, int c)
     {
-        return (c >> 2) * PLANE_BYTES + r * 64 + (((c & 3) ^ pswz(r)) << 4);
+        return (c >> 2) * PLANE_BYTES + r * 64 + (((c & 3) ^ swz(r)) << 4);
     }
     // The 16-byte slot a copy lane fills: slot = 64 * copy + lane (copies
     // write 1 KiB blocks in order).  Returns the (row, chunk) it must fetch.
@@ -129,7 +147,7 @@ struct PlaneTile {
     {
         const int plane = slot / (R * 4), rem = slot % (R * 4);
         r = rem >> 2;
-        c = plane * 4 + ((rem & 3) ^ pswz(r));
+        c = plane * 4 + ((rem & 3) ^ swz(r));
     }
 };
 
@@ -227,6 +245,20 @@ __device__ __forceinline__ float halves_sum(float x)
 {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Max / sum over the four lanes l, l^16, l^32, l^48 (one 16x16 accumulator
+// column) with v_permlane16_swap and v_permlane32_swap; every lane of the
+// column gets the same result.
+__device__ __forceinline__ float quarters_max(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return halves_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float quarters_sum(float x)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return halves_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
 }
 
 } // namespace gqa

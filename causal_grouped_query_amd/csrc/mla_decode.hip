@@ -7,17 +7,18 @@
 //
 // A workgroup owns 128 query heads of one sequence and one key chunk; the
 // key tile (32 keys x 576) is copied HBM -> LDS once with global_load_lds
-// into a 3-deep ring and read by all 8 waves.  The per-wave register budget
-// is the problem this layout solves: one wave holding Q^T for 32 heads over
-// 576 dims (144 VGPRs) and O^T over 512 dims (256 accumulators) does not fit.
-// Instead wave w = (head group hg = w & 3, half = w >> 2):
-//   * computes the partial scores of its 32 heads over dims
-//     [288*half, 288*half + 288) with v_mfma_f32_32x32x16_bf16 (18 steps),
-//   * swaps partial scores with its partner wave (same heads, other half)
-//     through LDS and adds them (both waves then hold the same full scores),
-//   * runs the online softmax (identical in both waves),
-//   * accumulates O^T for output dims [256*half, 256*half + 256) from V^T
-//     transpose reads (ds_read_b64_tr_b16) of the same LDS key tile.
+// into a 3-deep ring and read by all 8 waves.  Wave w owns 16 heads and works
+// with v_mfma_f32_16x16x32_bf16, so its whole state fits one wave's share of
+// the register file (2 waves per SIMD): Q^T over 576 dims (72 VGPRs) and O^T
+// over 512 dims (128 accumulators).  Per tile and wave:
+//   * scores S^T = K Q^T: 2 key blocks x 18 contraction steps,
+//   * online softmax per head: each head is one accumulator column held by
+//     the four lanes l, l^16, l^32, l^48 (reduced with permlane swaps),
+//   * O^T += V^T P^T over 32 blocks of 16 output dims; the P^T operand is the
+//     lane's own 8 weights (the contraction slots of lane group g are the
+//     keys its score accumulators hold), and V^T comes from two
+//     ds_read_b64_tr_b16 of the same LDS key tile.
+// No scores are exchanged between waves, so the tile loop has one barrier.
 // Partial outputs and log-sum-exp values go to the workspace exactly as for
 // the other decode kernels; combine.hip merges them.
 #include "device_common.h"
@@ -32,21 +33,21 @@ constexpr int kDK = 576;     // key width (latent 512 + rope 64)
 constexpr int kDV = 512;     // value width (the latent)
 constexpr int kNW = 8;       // waves per workgroup
 constexpr int kNT = 64 * kNW;
+constexpr int kHW = 16;      // heads per wave
 constexpr int kStages = 3;
-#ifndef GQA_MLA_PREFETCH
-#define GQA_MLA_PREFETCH 0  // LDS operand reads kept in flight ahead of the MFMAs (spills if > 0)
+#ifndef GQA_MLA_PF
+#define GQA_MLA_PF 6  // operand reads issued ahead of the MFMAs (0: compiler's choice)
 #endif
-constexpr int kCPR = kDK / 8;              // 72 16-byte chunks per key row
-constexpr int kKSH = kDK / 16 / 2;         // 18 MFMA k-steps per half
-constexpr int kDTH = kDV / 32 / 2;         // 8 output tiles per half
+constexpr int kCPR = kDK / 8;   // 72 16-byte chunks per key row
+constexpr int kKS = kDK / 32;   // 18 contraction steps of 32 dims
+constexpr int kDB = kDV / 16;   // 32 output blocks of 16 dims
 static_assert(kTK * kCPR % 64 == 0, "tile is whole wave copies");
 
 struct MlaSmem {
     uint16_t k[kStages][kTK * kDK];
-    float xs[kNW][16 * 64];  // partial-score exchange, one f32x16 per lane per wave
 };
 
-__global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
+__global__ __launch_bounds__(kNT, 1) void mla_decode_kernel(DecodeArgs p)
 {
     constexpr int NCOPY = kTK * kCPR / 64;  // 36 wave-copies per tile, spread over 8 waves
     __shared__ __attribute__((aligned(1024))) MlaSmem sm;
@@ -58,10 +59,10 @@ __global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
     const int hblk = blockIdx.y;
     const int kvh = bk % p.Hkv, b = bk / p.Hkv;
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int col = lane & 31, hi = lane >> 5;
-    const int hg = w & 3, half = w >> 2;
-    const int hh = hblk * 128 + hg * 32 + col;  // head within the group
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r16 = lane & 15, g = lane >> 4;
+    const int hh = hblk * (kHW * kNW) + kHW * w + r16;  // head within the group
     const bool head_ok = hh < p.G;
     const int head = kvh * p.G + (head_ok ? hh : 0);
 
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
     // wave copy j covers LDS chunks [64 j, 64 j + 64); waves take j = w, w + 8, ...
     // (36 copies: waves 0-3 do 5, waves 4-7 do 4; the count per wave is fixed)
     const int my_copies = (NCOPY - w + kNW - 1) / kNW;
-    using Tile = PlaneTile<kTK>;
+    using Tile = PlaneTile<kTK, true>;
     auto issue_tile = [&](int k0, int slot) {
         for (int j = w; j < NCOPY; j += kNW) {
             int row, chunk;
@@ -85,35 +86,38 @@ __global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
         }
     };
 
-    // Q^T for this wave's heads over its half of the key dims
-    u32x4 qreg[kKSH];
+    // Q^T (B operand): head r16 of this wave, dims 32 ks + 8 g .. + 7
+    u32x4 qreg[kKS];
     {
-        const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * p.Hq + head) * kDK + 288 * half;
+        const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * p.Hq + head) * kDK + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < kKSH; ++ks) {
+        for (int ks = 0; ks < kKS; ++ks) {
             u32x4 z = {0u, 0u, 0u, 0u};
-            qreg[ks] = head_ok ? *(const u32x4 *)(qrow + 16 * ks + 8 * hi) : z;
+            qreg[ks] = head_ok ? *(const u32x4 *)(qrow + 32 * ks) : z;
         }
 #pragma unroll
-        for (int ks = 0; ks < kKSH; ++ks) hold_reg(qreg[ks]);
+        for (int ks = 0; ks < kKS; ++ks) hold_reg(qreg[ks]);
     }
 
-    f32x16 o[kDTH];
+    f32x4 o[kDB];
 #pragma unroll
-    for (int i = 0; i < kDTH; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
+    for (int i = 0; i < kDB; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    const int krow = kperm(col);
-    const int kbase_even = Tile::offset(krow, hi);
-    const int kbase_odd = Tile::offset(krow, 2 + hi);
-    const int vg = lane >> 4, vi = lane & 15;
-    const int vrow = 8 * (vg >> 1) + (vi >> 2), vchunk = 2 * (vg & 1) + ((vi >> 1) & 1);
-    const int vb_h0 = Tile::offset(vrow, vchunk) + 8 * (vi & 1);      // rows 16 st + vrow
-    const int vb_h1 = Tile::offset(vrow + 4, vchunk) + 8 * (vi & 1);  // rows 16 st + vrow + 4
-    float *xs_mine = &sm.xs[w][0];
-    const float *xs_peer = &sm.xs[w ^ 4][0];
+    // K operand (A): key row 16 t + r16, dims 32 ks + 8 g .. + 7 = chunk
+    // 4 ks + g, i.e. plane ks, chunk g of the plane.  Rows r and r + 16 share
+    // the swizzle, so block 1 is block 0 + 16 rows.
+    const int kb0 = Tile::offset(r16, g);
+    // V^T operand (A) by transpose reads: in 16-lane group g, lane 4 r + q
+    // points at key 4 g + r (first read) or 16 + 4 g + r (second read), the
+    // keys of contraction slots r and 4 + r (the lane's score elements),
+    // dims 16 db + 4 q .. + 3: chunk 2 db + (q >> 1) (plane db >> 1, chunk
+    // 2 (db & 1) + (q >> 1) of the plane), byte 8 (q & 1) inside it.
+    const int vr = r16 >> 2, vq = r16 & 3;
+    // (the second read is the first one 16 rows further down)
+    int vb[2];  // [db & 1]
+#pragma unroll
+    for (int odd = 0; odd < 2; ++odd) vb[odd] = Tile::offset(4 * g + vr, 2 * odd + (vq >> 1)) + 8 * (vq & 1);
 
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
@@ -132,121 +136,92 @@ __global__ __launch_bounds__(kNT, 2) void mla_decode_kernel(DecodeArgs p)
         } else {
             wait_vmem();
         }
-        lds_barrier();  // tile visible; the previous slot and exchange buffers are free
+        lds_barrier();  // tile visible; the slot of tile it-1 is free
         if (it + kStages - 1 < ntiles) issue_tile(k0 + (kStages - 1) * kTK, (it + kStages - 1) % kStages);
 
         const char *ks_ = (const char *)sm.k[slot];
-        f32x16 s;
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < kKSH; ++ks) {
-            // chunk 36 half + 2 ks + hi lives in plane 9 half + ks / 2
-            const int off_ = ((ks & 1) ? kbase_odd : kbase_even) + (9 * half + (ks >> 1)) * Tile::PLANE_BYTES;
-            s = mfma32x32x16(*(const u32x4 *)(ks_ + off_), qreg[ks], s);
+        for (int ks = 0; ks < kKS; ++ks) {
+            s0 = mfma16x16x32(*(const u32x4 *)(ks_ + kb0 + ks * Tile::PLANE_BYTES), qreg[ks], s0);
+            s1 = mfma16x16x32(*(const u32x4 *)(ks_ + kb0 + 16 * 64 + ks * Tile::PLANE_BYTES), qreg[ks], s1);
         }
-#if GQA_MLA_PREFETCH
-        // keep GQA_MLA_PREFETCH operand reads in flight ahead of the MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x100, GQA_MLA_PREFETCH, 0);
+#if GQA_MLA_PF
+        __builtin_amdgcn_sched_group_barrier(0x100, GQA_MLA_PF, 0);
 #pragma unroll
-        for (int i = 0; i < kKSH - GQA_MLA_PREFETCH; ++i) {
+        for (int i = 0; i < 2 * kKS - GQA_MLA_PF; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, GQA_MLA_PREFETCH, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, GQA_MLA_PF, 0);
 #endif
-        // swap partial scores with the partner wave (same heads, other half)
-#pragma unroll
-        for (int e = 0; e < 16; e += 4) {
-            f32x4 v4 = {s[e], s[e + 1], s[e + 2], s[e + 3]};
-            *(f32x4 *)(xs_mine + e * 64 + 4 * lane) = v4;
-        }
-        lds_barrier();
-#pragma unroll
-        for (int e = 0; e < 16; e += 4) {
-            // (fp addition commutes, so both waves get bit-identical sums)
-            const f32x4 v4 = *(const f32x4 *)(xs_peer + e * 64 + 4 * lane);
-            s[e] += v4[0];
-            s[e + 1] += v4[1];
-            s[e + 2] += v4[2];
-            s[e + 3] += v4[3];
-        }
-
+        // element i of s0 / s1: key 4 g + i / 16 + 4 g + i, head r16
         if (k0 + kTK > kend) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                if (k0 + acc_key(0, e, hi) >= kend) s[e] = -INFINITY;
+            for (int i = 0; i < 4; ++i) {
+                if (k0 + 4 * g + i >= kend) s0[i] = -INFINITY;
+                if (k0 + 16 + 4 * g + i >= kend) s1[i] = -INFINITY;
+            }
         }
 
-        float mx = s[0];
-#pragma unroll
-        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
-        mx = halves_max(mx);
-        const float mt = mx * c;
+        float mx = fmaxf(fmaxf(s0[0], s0[1]), fmaxf(s0[2], s0[3]));
+        mx = fmaxf(mx, fmaxf(fmaxf(s1[0], s1[1]), fmaxf(s1[2], s1[3])));
+        const float mt = quarters_max(mx) * c;
         if (__any(mt > m_run + 8.0f)) {
+            // only heads whose max crossed the threshold move their reference
             const float m_new = (mt > m_run + 8.0f) ? mt : m_run;
             const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
             l_run *= alpha;
 #pragma unroll
-            for (int i = 0; i < kDTH; ++i)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+            for (int i = 0; i < kDB; ++i) o[i] *= alpha;
         }
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
-        u32x4 pb[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        u32x4 pb;
+        {
             float pv[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h + e], c, -m_use));
-            pb[h].x = pack_bf16x2(pv[0], pv[1]);
-            pb[h].y = pack_bf16x2(pv[2], pv[3]);
-            pb[h].z = pack_bf16x2(pv[4], pv[5]);
-            pb[h].w = pack_bf16x2(pv[6], pv[7]);
-            l_run = sum_bf16x8(pb[h], l_run);
+            for (int i = 0; i < 4; ++i) {
+                pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s0[i], c, -m_use));
+                pv[4 + i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s1[i], c, -m_use));
+            }
+            pb.x = pack_bf16x2(pv[0], pv[1]);
+            pb.y = pack_bf16x2(pv[2], pv[3]);
+            pb.z = pack_bf16x2(pv[4], pv[5]);
+            pb.w = pack_bf16x2(pv[6], pv[7]);
+            l_run = sum_bf16x8(pb, l_run);
         }
 
-        // O^T (this half's 256 dims) += V^T P^T, V^T = transpose of the latent
-        // prefix: output dims 256 half + 32 dt + ... live in plane 8 half + dt
+        // O^T += V^T P^T over the latent prefix of the tile
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-#pragma unroll
-            for (int dt = 0; dt < kDTH; ++dt) {
-                const int o_ = (8 * half + dt) * Tile::PLANE_BYTES + 16 * st * 64;
-                const u32x2 lo = lds_read_tr16(ks_ + vb_h0 + o_);
-                const u32x2 hv = lds_read_tr16(ks_ + vb_h1 + o_);
-                u32x4 va = {lo.x, lo.y, hv.x, hv.y};
-                o[dt] = mfma32x32x16(va, pb[st], o[dt]);
-            }
+        for (int db = 0; db < kDB; ++db) {
+            const int o_ = (db >> 1) * Tile::PLANE_BYTES;
+            const u32x2 lo = lds_read_tr16(ks_ + vb[db & 1] + o_);
+            const u32x2 hv = lds_read_tr16(ks_ + vb[db & 1] + 16 * 64 + o_);
+            const u32x4 va = {lo.x, lo.y, hv.x, hv.y};
+            o[db] = mfma16x16x32(va, pb, o[db]);
         }
-#if GQA_MLA_PREFETCH
-        __builtin_amdgcn_sched_group_barrier(0x100, 2 * GQA_MLA_PREFETCH, 0);
+#if GQA_MLA_PF
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * GQA_MLA_PF, 0);
 #pragma unroll
-        for (int i = 0; i < 2 * kDTH - GQA_MLA_PREFETCH; ++i) {
+        for (int i = 0; i < kDB - GQA_MLA_PF; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, GQA_MLA_PREFETCH, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, GQA_MLA_PF, 0);
 #endif
     }
 
     if (!head_ok) return;
-    const float l_tot = halves_sum(l_run);
+    const float l_tot = quarters_sum(l_run);
     const size_t prow = ((size_t)b * p.Hq + head) * p.S + split;
-    float *po = p.part_o + prow * kDV + 256 * half;
+    float *po = p.part_o + prow * kDV + 4 * g;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // element i of o[db]: output dim 16 db + 4 g + i, head r16
 #pragma unroll
-    for (int dt = 0; dt < kDTH; ++dt)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            f32x4 v4 = {o[dt][4 * j] * inv, o[dt][4 * j + 1] * inv, o[dt][4 * j + 2] * inv,
-                        o[dt][4 * j + 3] * inv};
-            *(f32x4 *)(po + 32 * dt + 8 * j + 4 * hi) = v4;
-        }
-    if (half == 0 && hi == 0) p.part_lse[prow] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
+    for (int db = 0; db < kDB; ++db) *(f32x4 *)(po + 16 * db) = o[db] * inv;
+    if (g == 0) p.part_lse[prow] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
 }
 
 } // namespace
