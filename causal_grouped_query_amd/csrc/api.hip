@@ -47,43 +47,56 @@ int launch_status(int rc)
     return hipGetLastError() == hipSuccess ? GQA_OK : GQA_ERR_HIP;
 }
 
-// Keys per split when the caller leaves the choice to the library.  The
-// choice depends only on the shape (it assumes the 256 compute units of an
-// MI355X) so that the workspace size is known before any device call.
-int default_splits(int B, int Hq, int Hkv, int Tmax, int Dk)
+// Splits when the caller leaves the choice to the library.  The choice
+// depends only on the shape (it assumes the 256 compute units of an MI355X)
+// so that the workspace size is known before any device call.
+int default_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int dtype)
 {
     const int G = Hq / Hkv;
-    long long groups;
-    int min_chunk;
     if (Dk == 576) {
-        // absorbed MLA: a workgroup covers 128 query heads of a sequence
-        groups = (long long)B * Hkv * ((G + 127) / 128);
-        min_chunk = 256;
-        long long s = (256 + groups - 1) / groups;  // one workgroup per CU, equal chunks
-        long long cap = (Tmax + min_chunk - 1) / min_chunk;
+        // absorbed MLA: a workgroup covers 128 query heads of a sequence and
+        // one of S equal key chunks; one workgroup per CU
+        const long long groups = (long long)B * Hkv * ((G + 127) / 128);
+        long long s = (256 + groups - 1) / groups;
+        const long long cap = (Tmax + 255) / 256;
         if (s > cap) s = cap;
         if (s < 1) s = 1;
         if (s > 64) s = 64;
         return (int)s;
     }
-    // small head dims: single-wave workgroups, ~5 resident per CU.  Aim for
-    // ~2.5 workgroups per resident slot if every sequence were full length
-    // (ragged lengths leave many chunks short or empty, and chunk-major
-    // dispatch puts those in the tail), with chunks of at least 256 keys.
-    groups = (long long)B * Hkv * ((G + 31) / 32);
-    min_chunk = 256;
-    long long s = (3200 + groups - 1) / groups;
-    long long cap = (Tmax + min_chunk - 1) / min_chunk;
+    const long long streams = (long long)B * Hkv * ((G + 31) / 32);
+    if (dtype == GQA_BF16) {
+        // flat decode: S bounds the pieces any stream may be cut into.  The
+        // kernel runs min(resident workgroups, ~T (S-2) / (n_max + S - 4))
+        // workgroups for T key tiles in all and n_max in the longest stream;
+        // with every sequence full, T = streams * n_max, so S - 2 of twice
+        // the resident workgroups per stream keeps all of them busy even when
+        // the lengths are ragged.
+        const long long wgs = gqa::decode_bf16_flat_workgroups(Dk);
+        long long s = 2 + (2 * wgs + streams - 1) / streams;
+        const long long cap = 2 + (Tmax + 31) / 32;
+        if (s < 8) s = 8;
+        if (s > cap) s = cap;
+        if (s > 64) s = 64;
+        return (int)(s < 3 ? 3 : s);
+    }
+    // fp32 path: one workgroup per (split, batch, KV head); ~2.5 workgroups
+    // per resident slot if every sequence were full length, chunks of at
+    // least 256 keys
+    long long s = (3200 + streams - 1) / streams;
+    const long long cap = (Tmax + 255) / 256;
     if (s > cap) s = cap;
     if (s < 1) s = 1;
     if (s > 64) s = 64;
     return (int)s;
 }
 
+// workspace: fp32 partial outputs [B, Hq, S, Dv], fp32 partial log2-sum-exp
+// [B, Hq, S], int32 partial counts per stream [<= B * Hq]
 size_t ws_bytes(int B, int Hq, int Dv, int S)
 {
     const size_t rows = (size_t)B * Hq * S;
-    size_t bytes = rows * Dv * sizeof(float) + rows * sizeof(float);
+    size_t bytes = rows * Dv * sizeof(float) + rows * sizeof(float) + (size_t)B * Hq * sizeof(int);
     return (bytes + 255) & ~(size_t)255;
 }
 
@@ -174,7 +187,7 @@ GQA_API int gqa_attn_decode_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int
     if (rc != GQA_OK) return rc;
     if (Tmax <= 0) return GQA_ERR_INVALID_ARG;
     if (!head_dims_decode(Dk, Dv, dtype)) return GQA_ERR_UNSUPPORTED;
-    return default_splits(B, Hq, Hkv, Tmax, Dk);
+    return default_splits(B, Hq, Hkv, Tmax, Dk, dtype);
 }
 
 GQA_API size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_splits)
@@ -213,7 +226,7 @@ GQA_API int gqa_attn_decode(const void *q, const void *k, const void *v, void *o
     }
     if (!aligned(seq_lens, 4)) return GQA_ERR_INVALID_ARG;
 
-    const int S = num_splits ? num_splits : default_splits(B, Hq, Hkv, Tmax, Dk);
+    const int S = num_splits ? num_splits : default_splits(B, Hq, Hkv, Tmax, Dk, dtype);
     const size_t need = ws_bytes(B, Hq, Dv, S);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return GQA_ERR_WORKSPACE;
 
@@ -242,12 +255,19 @@ GQA_API int gqa_attn_decode(const void *q, const void *k, const void *v, void *o
     a.v_st = v_st;
     a.S = S;
     a.chunk = chunk;
+    a.counts = nullptr;
+    a.n_wg = 0;
     hipStream_t st = (hipStream_t)stream;
 
     if (dtype == GQA_BF16) {
         const int hpb = gqa::decode_bf16_heads_per_block(Dk, G);
         a.n_hblk = (G + hpb - 1) / hpb;
         if ((long long)B * Hkv * S > 0x7fffffffLL || a.n_hblk > 65535) return GQA_ERR_UNSUPPORTED;
+        if (Dk <= 128 && S >= 3) {
+            // flat decode (balanced over all sequences); S bounds the pieces per stream
+            a.counts = (int *)(a.part_lse + (size_t)B * Hq * S);
+            a.n_wg = gqa::decode_bf16_flat_workgroups(Dk);
+        }
         a.c = folded_scale(scale);
         (void)hipGetLastError();
         rc = gqa::launch_decode_bf16(a, Dk, Dv, st);
@@ -268,5 +288,10 @@ GQA_API int gqa_attn_decode(const void *q, const void *k, const void *v, void *o
     c.S = S;
     c.Dv = Dv;
     c.out_bf16 = dtype == GQA_BF16;
+    c.counts = a.counts;
+    c.lens = seq_lens;
+    c.Hkv = Hkv;
+    c.G = G;
+    c.n_hblk = a.n_hblk;
     return launch_status(gqa::launch_combine(c, st));
 }

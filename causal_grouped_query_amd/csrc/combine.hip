@@ -8,6 +8,8 @@
 // the same merge online softmax applies tile by tile ("A Visual Guide to
 // Attention", section on sources and execution).  Empty chunks carry
 // lse = -inf and weigh nothing; a row with no keys at all yields zeros.
+// After the balanced (flat) decode a row has a variable number of pieces,
+// recorded per stream by the partial kernel.
 #include "launch.h"
 
 namespace gqa {
@@ -22,15 +24,21 @@ __global__ __launch_bounds__(kCT) void combine_kernel(CombineArgs p)
     const size_t row = blockIdx.x;  // b * Hq + head
     const float *lse = p.part_lse + row * p.S;
     const float *po = p.part_o + row * (size_t)p.S * p.Dv;
+    int ns = p.S;
+    if (p.counts) {
+        const int b = (int)(row / p.Hq), head = (int)(row % p.Hq);
+        const int w = (b * p.Hkv + head / p.G) * p.n_hblk + (head % p.G) / 32;
+        ns = p.lens[b] > 0 ? p.counts[w] : 0;
+    }
 
     float L = -INFINITY;
-    for (int s = 0; s < p.S; ++s) L = fmaxf(L, lse[s]);
+    for (int s = 0; s < ns; ++s) L = fmaxf(L, lse[s]);
     const int d0 = threadIdx.x * 4;
     if (d0 >= p.Dv) return;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     if (L != -INFINITY) {
-        for (int s = 0; s < p.S; ++s) {
+        for (int s = 0; s < ns; ++s) {
             const float w = __builtin_amdgcn_exp2f(lse[s] - L);
             if (w == 0.f) continue;
             wsum += w;

@@ -18,6 +18,11 @@
 // STAGES-deep ring (STAGES-1 tiles in flight while one is computed); V^T
 // comes from ds_read_b64_tr_b16.  (The absorbed-MLA shape has its own kernel,
 // mla_decode.hip, whose register budget needs a different wave layout.)
+//
+// Two schedules share this tile computation: decode_bf16_kernel cuts every
+// sequence into S equal chunks (one workgroup each), decode_bf16_flat_kernel
+// shares all key tiles of all sequences out evenly over a fixed number of
+// workgroups (used for S >= 3; ragged lengths then cost no balance).
 #include "device_common.h"
 #include "launch.h"
 
@@ -247,6 +252,331 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kern
     if (hi == 0) p.part_lse[prow] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
 }
 
+// ---------------------------------------------------------------------------
+// Flat decode: the same tile computation, but the work is balanced instead of
+// cut into fixed chunks per sequence.  All (batch, KV head, head block)
+// streams are laid end to end as one sequence of T key tiles (stream w of
+// batch b holds ceil(len_b / 32) tiles); workgroup i of the N that run takes
+// the contiguous tiles [i T / N, (i+1) T / N).  Ragged lengths therefore cost
+// nothing in balance, and each workgroup starts up once.  A workgroup writes
+// one normalised partial (o, lse) for every stream piece it covers, into
+// partial slot i - (first workgroup of that stream); the workgroup holding a
+// stream's first tile also records how many pieces the stream has.  N is
+// capped so that no stream is cut into more than S pieces: consecutive cuts
+// are at least floor(T / N) tiles apart, so a stream of n tiles has at most
+// (n - 2) / floor(T / N) + 2 pieces.
+template <int DK, int DV, int STAGES>
+__global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
+{
+    constexpr int NT = 64;
+    constexpr int CPRK = DK / 8, CPRV = DV / 8;
+    constexpr int KS = DK / 16;
+    constexpr int DT = DV / 32;
+    constexpr int KINS = kTK * CPRK / NT;
+    constexpr int VINS = kTK * CPRV / NT;
+    constexpr int NI = KINS + VINS;
+    static_assert(STAGES >= 2 && (STAGES - 2) * NI < 64, "ring depth");
+
+    __shared__ __attribute__((aligned(1024))) DecSmem<DK, DV, STAGES> sm;
+
+    const int lane = threadIdx.x;
+    const int col = lane & 31, hi = lane >> 5;
+    const int H = p.Hkv * p.n_hblk;  // streams per batch
+    auto ntile = [&](int len) {
+        len = len < 0 ? 0 : (len > p.Tmax ? p.Tmax : len);
+        return (len + kTK - 1) / kTK;
+    };
+
+    // ---- total tiles T and the longest stream (every workgroup computes them) ----
+    long long tsum = 0;
+    int nmax = 0;
+    for (int b0 = 0; b0 < p.B; b0 += 64) {
+        const int n = b0 + lane < p.B ? ntile(p.lens[b0 + lane]) : 0;
+        tsum += n;
+        nmax = max(nmax, n);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        tsum += __shfl_xor(tsum, o);
+        nmax = max(nmax, __shfl_xor(nmax, o));
+    }
+    const long long T = tsum * H;
+    if (T == 0) return;  // every sequence is empty: the combine writes zeros
+    const long long S2 = p.S - 2;  // the host uses this kernel only for S >= 3
+    long long ne = T * S2 / ((nmax > 2 ? nmax - 2 : 0) + S2);
+    ne = ne < 1 ? 1 : (ne > p.n_wg ? p.n_wg : ne);
+    const long long N = ne;
+    const long long wi = blockIdx.x;
+    if (wi >= N) return;
+    const long long lo = wi * T / N, hi_t = (wi + 1) * T / N;
+    if (lo >= hi_t) return;
+    auto wg_of = [&](long long t) {  // workgroup whose range holds tile t
+        long long x = t * N / T;
+        while (x + 1 < N && (x + 1) * T / N <= t) ++x;
+        return x;
+    };
+
+    // ---- cursors over (batch b, stream s of the batch, tile u of the stream) ----
+    // (all fields are wave-uniform and kept in scalar registers, so the
+    // length of the next batch is a scalar load: a vector load here would
+    // make the compiler drain the copy ring with vmcnt(0) on every tile)
+    struct Cur {
+        int b, s, u, n;    // n = tiles per stream of batch b
+        int len;           // clamped length of batch b
+        long long base;    // global index of batch b's first tile
+        int lens64, chunk; // lengths of batches 64 chunk + lane (one per lane)
+    };
+    auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+    auto uni64 = [](long long x) {
+        const unsigned lo32 = __builtin_amdgcn_readfirstlane((unsigned)x);
+        const unsigned hi32 = __builtin_amdgcn_readfirstlane((unsigned)((unsigned long long)x >> 32));
+        return (long long)(((unsigned long long)hi32 << 32) | lo32);
+    };
+    auto clamp_len = [&](int len) { return len < 0 ? 0 : (len > p.Tmax ? p.Tmax : len); };
+    auto locate = [&](long long t) {
+        Cur c;
+        long long base = 0;
+        for (int b0 = 0;; b0 += 64) {
+            const int b = b0 + lane;
+            const long long v = b < p.B ? (long long)ntile(p.lens[b]) * H : 0;
+            long long incl = v;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const long long y = __shfl_up(incl, o);
+                if (lane >= o) incl += y;
+            }
+            const unsigned long long hit = __ballot(b < p.B && base + incl > t);
+            if (hit) {
+                const int L = __ffsll((long long)hit) - 1;
+                const long long incl_l = __shfl(incl, L), v_l = __shfl(v, L);
+                c.b = uni(b0 + L);
+                c.base = uni64(base + incl_l - v_l);
+                c.n = uni((int)(v_l / H));
+                const long long rel = t - c.base;
+                c.s = uni((int)(rel / c.n));
+                c.u = uni((int)(rel % c.n));
+                c.chunk = uni(b0 >> 6);
+                c.lens64 = b < p.B ? clamp_len(p.lens[b]) : 0;
+                c.len = __builtin_amdgcn_readlane(c.lens64, L);
+                return c;
+            }
+            base += __shfl(incl, 63);
+        }
+    };
+    auto advance = [&](Cur &c) {
+        if (++c.u < c.n) return;
+        c.u = 0;
+        if (++c.s < H) return;
+        c.s = 0;
+        c.base += (long long)H * c.n;
+        do {
+            c.b = uni(c.b + 1);
+            if (c.b >= p.B) {  // past the last batch (only the copy cursor gets here)
+                c.len = kTK;
+            } else {
+                if ((c.b >> 6) != c.chunk) {  // next 64 batches: one vector load
+                    c.chunk = c.b >> 6;
+                    const int bb = 64 * c.chunk + lane;
+                    c.lens64 = bb < p.B ? clamp_len(p.lens[bb]) : 0;
+                }
+                c.len = __builtin_amdgcn_readlane(c.lens64, c.b & 63);
+            }
+            c.n = (c.len + kTK - 1) / kTK;
+        } while (c.n == 0);
+    };
+
+    using Tile = PlaneTile<kTK>;
+    int krow_[KINS], vrow_[VINS];
+    unsigned koff_[KINS], voff_[VINS];
+#pragma unroll
+    for (int j = 0; j < KINS; ++j) {
+        int row, chunk;
+        Tile::slot_source(j * 64 + lane, row, chunk);
+        krow_[j] = row;
+        koff_[j] = (unsigned)(row * p.k_st + chunk * 8) * 2u;
+    }
+#pragma unroll
+    for (int j = 0; j < VINS; ++j) {
+        int row, chunk;
+        Tile::slot_source(j * 64 + lane, row, chunk);
+        vrow_[j] = row;
+        voff_[j] = (unsigned)(row * p.v_st + chunk * 8) * 2u;
+    }
+    // copy the tile under cursor c into ring slot `slot`
+    auto issue_tile = [&](const Cur &c, int slot) {
+        const int kvh = c.s / p.n_hblk;
+        const int len = c.len;
+        const int k0 = c.u * kTK;
+        const uint16_t *kb = (const uint16_t *)p.k + (size_t)c.b * p.k_sb + (size_t)kvh * p.k_sh;
+        const uint16_t *vb = (const uint16_t *)p.v + (size_t)c.b * p.v_sb + (size_t)kvh * p.v_sh;
+        if (k0 + kTK <= len) {
+            const uint16_t *k0p = kb + (size_t)k0 * p.k_st;
+            const uint16_t *v0p = vb + (size_t)k0 * p.v_st;
+#pragma unroll
+            for (int j = 0; j < KINS; ++j) g2lds16(k0p, koff_[j], &sm.k[slot][j * 64 * 8]);
+#pragma unroll
+            for (int j = 0; j < VINS; ++j) g2lds16(v0p, voff_[j], &sm.v[slot][j * 64 * 8]);
+        } else {
+            // ragged last tile: rows past the sequence end re-read its last
+            // key (in bounds; masked below)
+#pragma unroll
+            for (int j = 0; j < KINS; ++j) {
+                const int row = min(k0 + krow_[j], len - 1);
+                g2lds16((const char *)(kb + (size_t)row * p.k_st) + (koff_[j] - (unsigned)(krow_[j] * p.k_st) * 2u),
+                        &sm.k[slot][j * 64 * 8]);
+            }
+#pragma unroll
+            for (int j = 0; j < VINS; ++j) {
+                const int row = min(k0 + vrow_[j], len - 1);
+                g2lds16((const char *)(vb + (size_t)row * p.v_st) + (voff_[j] - (unsigned)(vrow_[j] * p.v_st) * 2u),
+                        &sm.v[slot][j * 64 * 8]);
+            }
+        }
+    };
+
+    const int krow = kperm(col);
+    const int kbase_even = Tile::offset(krow, hi);
+    const int kbase_odd = Tile::offset(krow, 2 + hi);
+    const int vg = lane >> 4, vi = lane & 15;
+    const int vrow = 8 * (vg >> 1) + (vi >> 2), vchunk = 2 * (vg & 1) + ((vi >> 1) & 1);
+    const int vb_h0 = Tile::offset(vrow, vchunk) + 8 * (vi & 1);
+    const int vb_h1 = Tile::offset(vrow + 4, vchunk) + 8 * (vi & 1);
+    const float c = p.c;
+
+    const int ntl = (int)(hi_t - lo);  // tiles of this workgroup
+    Cur dc = locate(lo);               // copy cursor (runs STAGES-1 tiles ahead)
+    Cur cc = dc;                       // compute cursor
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < ntl) {
+            issue_tile(dc, s);
+            advance(dc);
+        }
+
+    u32x4 qreg[KS];
+    f32x16 o[DT];
+    float m_run = -INFINITY, l_run = 0.f;
+    bool head_ok = false;
+    int head = 0;
+    for (int it = 0; it < ntl; ++it) {
+        const int slot = it % STAGES;
+        if (it + STAGES - 2 < ntl)
+            wait_vmem_le<(STAGES - 2) * NI>();  // tile `it` landed, later ones may fly
+        else
+            wait_vmem();
+        lds_barrier();  // this wave's reads of the slot being refilled are complete
+        if (it + STAGES - 1 < ntl) {
+            issue_tile(dc, (it + STAGES - 1) % STAGES);
+            advance(dc);
+        }
+
+        const int kvh = cc.s / p.n_hblk, hblk = cc.s % p.n_hblk;
+        if (it == 0 || cc.u == 0) {
+            // a new stream piece: its queries, fresh accumulators
+            const int hh = hblk * 32 + col;
+            head_ok = hh < p.G;
+            head = kvh * p.G + (head_ok ? hh : 0);
+            const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)cc.b * p.Hq + head) * DK;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                u32x4 z = {0u, 0u, 0u, 0u};
+                qreg[ks] = head_ok ? *(const u32x4 *)(qrow + 16 * ks + 8 * hi) : z;
+            }
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) hold_reg(qreg[ks]);
+#pragma unroll
+            for (int i = 0; i < DT; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
+            m_run = -INFINITY;
+            l_run = 0.f;
+        }
+        const int kend = cc.len;
+        const int k0 = cc.u * kTK;
+
+        const char *ks_ = (const char *)sm.k[slot];
+        f32x16 s;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[e] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int off_ = ((ks & 1) ? kbase_odd : kbase_even) + (ks >> 1) * Tile::PLANE_BYTES;
+            s = mfma32x32x16(*(const u32x4 *)(ks_ + off_), qreg[ks], s);
+        }
+        if (k0 + kTK > kend) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (k0 + acc_key(0, e, hi) >= kend) s[e] = -INFINITY;
+        }
+        float mx = s[0];
+#pragma unroll
+        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+        mx = halves_max(mx);
+        const float mt = mx * c;
+        if (__any(mt > m_run + 8.0f)) {
+            const float m_new = (mt > m_run + 8.0f) ? mt : m_run;
+            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < DT; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+        }
+        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        u32x4 pb[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            float pv[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h + e], c, -m_use));
+            pb[h].x = pack_bf16x2(pv[0], pv[1]);
+            pb[h].y = pack_bf16x2(pv[2], pv[3]);
+            pb[h].z = pack_bf16x2(pv[4], pv[5]);
+            pb[h].w = pack_bf16x2(pv[6], pv[7]);
+            l_run = sum_bf16x8(pb[h], l_run);
+        }
+        const char *vs_ = (const char *)sm.v[slot];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int o_ = dt * Tile::PLANE_BYTES + 16 * st * 64;
+                const u32x2 lo2 = lds_read_tr16(vs_ + vb_h0 + o_);
+                const u32x2 hv = lds_read_tr16(vs_ + vb_h1 + o_);
+                u32x4 va = {lo2.x, lo2.y, hv.x, hv.y};
+                o[dt] = mfma32x32x16(va, pb[st], o[dt]);
+            }
+        }
+
+        if (cc.u == cc.n - 1 || it == ntl - 1) {
+            // end of this workgroup's piece of the stream: write its partial
+            const long long pw = cc.base + (long long)cc.s * cc.n;  // the stream's first tile
+            const long long first = wg_of(pw);
+            const int j = (int)(wi - first);
+            if (head_ok) {
+                const float l_tot = halves_sum(l_run);
+                const size_t prow = ((size_t)cc.b * p.Hq + head) * p.S + j;
+                float *po = p.part_o + prow * DV;
+                const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) {
+                        f32x4 v4 = {o[dt][4 * jj] * inv, o[dt][4 * jj + 1] * inv, o[dt][4 * jj + 2] * inv,
+                                    o[dt][4 * jj + 3] * inv};
+                        *(f32x4 *)(po + 32 * dt + 8 * jj + 4 * hi) = v4;
+                    }
+                if (hi == 0) p.part_lse[prow] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
+            }
+            if (j == 0 && lane == 0)
+                p.counts[(size_t)cc.b * H + cc.s] = (int)(wg_of(pw + cc.n - 1) - wi + 1);
+        }
+        advance(cc);
+    }
+}
+
 template <int DK, int DV, int NW, int STAGES>
 int launch_one(const DecodeArgs &a, hipStream_t stream)
 {
@@ -267,8 +597,32 @@ int decode_bf16_heads_per_block(int Dk, int G)
     return 32;
 }
 
+int decode_bf16_flat_workgroups(int Dk)
+{
+    // 8 per compute unit on the 256 CUs of an MI355X.  The occupancy query
+    // allows 5 resident 32 KiB-LDS workgroups per CU, but measured over 1280
+    // .. 3200 workgroups the ragged GQA decode is fastest at 2048 (226 us)
+    // and clearly slower at 1280 (258 us) and above 2048 (244 .. 251 us).
+    (void)Dk;
+    return 8 * 256;
+}
+
+template <int DK, int DV, int STAGES>
+int launch_flat(const DecodeArgs &a, hipStream_t stream)
+{
+    dim3 grid(a.n_wg), block(64);
+    hipLaunchKernelGGL((decode_bf16_flat_kernel<DK, DV, STAGES>), grid, block, 0, stream, a);
+    return 0;
+}
+
 int launch_decode_bf16(const DecodeArgs &a, int Dk, int Dv, hipStream_t stream)
 {
+    if (a.counts) {
+        if (a.S < 3 || a.n_wg < 1) return -1;
+        if (Dk == 128 && Dv == 128) return launch_flat<128, 128, GQA_DEC_STAGES>(a, stream);
+        if (Dk == 64 && Dv == 64) return launch_flat<64, 64, 3>(a, stream);
+        return -1;
+    }
     if (Dk == 128 && Dv == 128) return launch_one<128, 128, 1, GQA_DEC_STAGES>(a, stream);
     if (Dk == 64 && Dv == 64) return launch_one<64, 64, 1, 3>(a, stream);
     if (Dk == 576 && Dv == 512) {

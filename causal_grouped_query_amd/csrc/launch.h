@@ -39,16 +39,20 @@ struct DecodeArgs {
     int B, Hq, Hkv, Tmax, G;
     long long k_sb, k_sh, k_st;
     long long v_sb, v_sh, v_st;
-    int S;               // splits
+    int S;               // splits (flat kernel: most partials any stream may need)
     int chunk;           // keys per split (multiple of the key tile)
     int n_hblk;          // head blocks per KV head
     float c;             // scale * log2(e)
+    int *counts;         // flat kernel: partials written per stream [B * Hkv * n_hblk]
+    int n_wg;            // flat kernel: workgroups launched
 };
 
 int launch_decode_bf16(const DecodeArgs &a, int Dk, int Dv, hipStream_t stream);
 // Absorbed-MLA shape (Dk 576, Dv 512, V = latent prefix of K), 128 heads per block.
 int launch_mla_decode(const DecodeArgs &a, hipStream_t stream);
 int decode_bf16_key_tile();
+// Flat (persistent, balanced) decode for Dk = Dv <= 128: workgroups to launch.
+int decode_bf16_flat_workgroups(int Dk);
 int decode_bf16_heads_per_block(int Dk, int G);
 
 // fp32 VALU paths (small head dims; exactness-first).
@@ -68,6 +72,12 @@ struct CombineArgs {
     void *out;           // [B, Hq, 1, Dv], bf16 or fp32
     int B, Hq, S, Dv;
     int out_bf16;
+    // flat decode: the number of partials of row (b, head) is
+    // counts[(b * Hkv + head / G) * n_hblk + (head % G) / 32] (0 when lens[b] <= 0);
+    // counts == nullptr: every row has S partials
+    const int *counts;
+    const int *lens;
+    int Hkv, G, n_hblk;
 };
 int launch_combine(const CombineArgs &a, hipStream_t stream);
 

@@ -85,8 +85,9 @@ int gqa_attn_decode_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int Dv, int
 
 /*
  * Bytes of device workspace gqa_attn_decode needs for num_splits splits
- * (num_splits >= 1): fp32 partial outputs [B, Hq, S, Dv] and fp32 partial
- * log-sum-exp values [B, Hq, S].  Returns 0 for invalid arguments.
+ * (num_splits >= 1): fp32 partial outputs [B, Hq, S, Dv], fp32 partial
+ * log-sum-exp values [B, Hq, S] and B*Hq int32 piece counts.  Returns 0 for
+ * invalid arguments.
  */
 size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_splits);
 
@@ -111,7 +112,13 @@ size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_splits);
  *            Tmax are clamped to Tmax.  Cache slots at t >= seq_lens[b] are
  *            never read into the result (they may hold anything, NaN included).
  *   num_splits  number of key-axis splits, 1 .. 1024, or 0 for the value of
- *            gqa_attn_decode_splits().
+ *            gqa_attn_decode_splits().  For bf16 with Dk = Dv <= 128 and
+ *            num_splits >= 3 the work is balanced over all sequences instead
+ *            (the key tiles of all sequences are shared out evenly over the
+ *            workgroups) and num_splits bounds how many pieces one
+ *            sequence's keys may be cut into; otherwise each sequence's keys
+ *            are cut into num_splits equal chunks.  The result is the same
+ *            attention either way (exact log-sum-exp merge).
  *   workspace   device buffer of at least
  *            gqa_attn_decode_workspace_size(B, Hq, Dv, splits) bytes, 256-byte
  *            aligned; contents on entry are ignored.  Two calls that share a

@@ -179,6 +179,46 @@ def test_decode_matches_oracle(case, dtype, splits):
     _check(out, ref, dtype, f"decode {case} {dtype} S={splits}")
 
 
+# The balanced decode (bf16, splits >= 3) lays the key tiles of all sequences
+# end to end and shares them out evenly: these cases cross the 64-batch
+# length chunks its cursors load, mix empty and full sequences, and take
+# the smallest and largest piece bounds.
+FLAT_CASES = [
+    # B, Hq, Hkv, Tmax, D, lens (None: seeded random in [0, Tmax], zeros included)
+    (130, 8, 2, 96, 128, None),
+    (70, 4, 1, 200, 64, None),
+    (4, 8, 2, 2000, 128, [0, 2000, 0, 1]),
+    (1, 64, 1, 1000, 128, [999]),
+]
+
+
+@pytest.mark.parametrize("case", FLAT_CASES, ids=lambda c: "B{}_Hq{}_Hkv{}_Tmax{}_D{}".format(*c[:5]))
+@pytest.mark.parametrize("splits", [3, 0, 64])
+def test_flat_decode_matches_oracle(case, splits):
+    B, Hq, Hkv, Tmax, D, lens = case
+    seed = zlib.crc32(repr(case).encode()) % 10000
+    if lens is None:
+        g = torch.Generator().manual_seed(seed)
+        lens = torch.randint(0, Tmax + 1, (B,), generator=g).tolist()
+        lens[::7] = [0] * len(lens[::7])
+        lens[1::11] = [Tmax] * len(lens[1::11])
+    q = _rand((B, Hq, 1, D), seed, "bf16")
+    k = _rand((B, Hkv, Tmax, D), seed + 1, "bf16")
+    v = _rand((B, Hkv, Tmax, D), seed + 2, "bf16")
+    for b, n in enumerate(lens):
+        k[b, :, n:] = float("nan")
+        v[b, :, n:] = float("nan")
+    scale = 1.0 / math.sqrt(D)
+    out = gqa.decode(q.cuda(), k.cuda(), v.cuda(), torch.tensor(lens, dtype=torch.int32).cuda(), scale=scale,
+                     num_splits=splits)
+    torch.cuda.synchronize()
+    ref = O.attention(q, k, v, scale, True, kv_lens=lens)
+    empty = [b for b, n in enumerate(lens) if n == 0]
+    assert torch.all(out[empty] == 0)
+    keep = [b for b, n in enumerate(lens) if n > 0]
+    _check(out[keep], ref[keep], "bf16", f"flat decode {case[:5]} S={splits}")
+
+
 def test_decode_strided_cache_view():
     """Caches with a larger capacity are read through strides, not copies."""
     B, Hq, Hkv, Tcap, Tmax, D = 2, 8, 2, 512, 300, 128
