@@ -17,11 +17,13 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
 import os
 import sys
+import statistics
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -117,9 +119,14 @@ def main() -> int:
         return 0
 
     # ---------------- inputs (seeded, synthetic, resident in HBM) ----------------
+    # The prefill alternates between two input sets (seeds s and s + 100) so
+    # that the 256 MB Infinity Cache cannot serve a step's inputs from the
+    # previous step; the decode cache (1.2 GB read per step) exceeds it anyway.
     wp, wd = W.GQA_PREFILL, W.GQA_DECODE
-    q, k, v = (t.to(dev) for t in W.fwd_inputs(wp))
-    out = torch.empty((wp.B, wp.Hq, wp.Tq, wp.Dv), dtype=torch.bfloat16, device=dev)
+    pre_sets = []
+    for wv in (wp, dataclasses.replace(wp, seed=wp.seed + 100)):
+        q, k, v = (t.to(dev) for t in W.fwd_inputs(wv))
+        pre_sets.append((q, k, v, torch.empty((wp.B, wp.Hq, wp.Tq, wp.Dv), dtype=torch.bfloat16, device=dev)))
     dq, dk, dv, lens_cpu = W.decode_inputs(wd, nan_tail=False)
     dq, dk, dv = dq.to(dev), dk.to(dev), dv.to(dev)
     lens = lens_cpu.to(dev)
@@ -128,7 +135,10 @@ def main() -> int:
     ws = torch.empty(gqa.decode_workspace_size(wd.B, wd.Hq, wd.Dv, S), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
+    step_no = [0]
+
     def prefill():
+        q, k, v, out = pre_sets[step_no[0] % 2]
         gqa.attention(q, k, v, scale=wp.scale, causal=True, out=out)
 
     def decode():
@@ -137,6 +147,7 @@ def main() -> int:
     for _ in range(args.warmup):
         prefill()
         decode()
+        step_no[0] += 1
     torch.cuda.synchronize()
 
     K = args.steps
@@ -148,10 +159,13 @@ def main() -> int:
         ev[i][1].record()
         decode()
         ev[i][2].record()
+        step_no[0] += 1
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     t_pre = sum(e[0].elapsed_time(e[1]) for e in ev) / K * 1e-3
     t_dec = sum(e[1].elapsed_time(e[2]) for e in ev) / K * 1e-3
+    t_pre_med = statistics.median(e[0].elapsed_time(e[1]) for e in ev) * 1e-3
+    t_dec_med = statistics.median(e[1].elapsed_time(e[2]) for e in ev) * 1e-3
     ms_step = ev[0][0].elapsed_time(ev[-1][2]) / K
 
     F = fwd_flops(wp)
@@ -165,14 +179,16 @@ def main() -> int:
         "kernel": "fwd_bf16_kernel<128> (gqa_attn_fwd, one launch per step)",
         "bound": "mfma", "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "traffic": tr,
-        "avg_launch_us": round(t_pre * 1e6, 2), "flop_per_launch": F,
+        "avg_launch_us": round(t_pre * 1e6, 2), "median_launch_us": round(t_pre_med * 1e6, 2),
+        "flop_per_launch": F,
     }
     trd = traffic_for("decode_bf16_kernel")
     roofline_decode = {
         "kernel": f"decode_bf16_kernel<128,128> + combine_kernel (gqa_attn_decode, {S} splits)",
         "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
         "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": trd,
-        "avg_launch_us": round(t_dec * 1e6, 2), "kv_bytes_per_launch": DB, "sum_len": int(sum(lens_list)),
+        "avg_launch_us": round(t_dec * 1e6, 2), "median_launch_us": round(t_dec_med * 1e6, 2),
+        "kv_bytes_per_launch": DB, "sum_len": int(sum(lens_list)),
     }
 
     result = {
@@ -204,8 +220,10 @@ def main() -> int:
     }
 
     # free the headline inputs before the extra workloads
-    del q, k, v, out, dq, dk, dv, dout, ws
+    del pre_sets, dq, dk, dv, dout, ws
     torch.cuda.empty_cache()
+    result["context"] = {"hbm_copy_GBps": copy_bandwidth(torch, dev),
+                         "note": "plain 1 GiB device-to-device copy (reads + writes), the practical HBM rate"}
 
     if not args.no_extra:
         result["extra"] = extra_workloads(torch, gqa, W, dev)
@@ -230,17 +248,36 @@ def _time(torch, fn, reps=10, warm=3):
     return s.elapsed_time(e) / reps * 1e-3
 
 
+def copy_bandwidth(torch, dev) -> float:
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    sec = _time(torch, lambda: dst.copy_(src), reps=5, warm=2)
+    del src, dst
+    return round(2 * n / sec / 1e9, 1)
+
+
 def extra_workloads(torch, gqa, W, dev):
     """The other headline shapes, timed the same way (not part of the step)."""
     res = {}
     w = W.MQA_SUFFIX
-    q, k, v = (t.to(dev) for t in W.fwd_inputs(w))
-    out = torch.empty((w.B, w.Hq, w.Tq, w.Dv), dtype=torch.bfloat16, device=dev)
-    sec = _time(torch, lambda: gqa.attention(q, k, v, scale=w.scale, out=out))
+    # two input sets in turn: one set (201 MB) would fit the Infinity Cache
+    sets = []
+    for wv in (w, dataclasses.replace(w, seed=w.seed + 100)):
+        q, k, v = (t.to(dev) for t in W.fwd_inputs(wv))
+        sets.append((q, k, v, torch.empty((w.B, w.Hq, w.Tq, w.Dv), dtype=torch.bfloat16, device=dev)))
+    turn = [0]
+
+    def mqa():
+        q, k, v, out = sets[turn[0] % 2]
+        turn[0] += 1
+        gqa.attention(q, k, v, scale=w.scale, out=out)
+
+    sec = _time(torch, mqa)
     f = fwd_flops(w)
     res[w.name] = {"us": round(sec * 1e6, 1), "TFLOP/s": round(f / sec / 1e12, 1),
                    "frac_mfma_peak": round(f / sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
-    del q, k, v, out
+    del sets
 
     w = W.MLA_DECODE
     q, kc, _, lens = W.decode_inputs(w, nan_tail=False)
@@ -263,6 +300,17 @@ def extra_workloads(torch, gqa, W, dev):
     res[w.name] = {"us": round(sec * 1e6, 1), "note": "parity-only fp32 workload"}
     torch.cuda.empty_cache()
     return res
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(target_s: float):
@@ -295,6 +343,7 @@ def cpu_baseline(target_s: float):
         "value": done_flops / elapsed / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": _cpu_model(),
         "kind": "oracle",
         "sample": f"{done_rows} uniformly drawn query rows (of {n_rows_total}) of {w.name}, fp64, "
                   f"{elapsed:.1f} s",
