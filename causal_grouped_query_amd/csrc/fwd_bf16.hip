@@ -24,10 +24,12 @@
 //    device_common.h); V stays row-major in LDS and its transposed A operand
 //    comes from two ds_read_b64_tr_b16 per MFMA.
 //  * K and V tiles go straight from HBM to LDS with global_load_lds (no
-//    registers, no VALU), into a double buffer in the swizzled plane layout
-//    of device_common.h (every LDS read of the loop is a base register plus
-//    an immediate): tile i+1 is in flight while tile i is computed; one
-//    barrier per tile.
+//    registers, no VALU), into a STAGES-deep ring in the swizzled plane
+//    layout of device_common.h (every LDS read of the loop is a base
+//    register plus an immediate): tiles i+1 .. i+STAGES-1 are in flight while
+//    tile i is computed; one barrier per tile.  Eight waves (256 query rows)
+//    share each tile, one workgroup per CU with a 4-deep ring (128 KiB):
+//    half the L2 -> LDS traffic per FLOP of two 4-wave workgroups per CU.
 //  * Online softmax in base 2: scale*log2(e) is folded into one FMA per
 //    score, exp via v_exp_f32, the row sum via v_dot2 over the bf16-rounded
 //    weights.  The running max is only moved (and O rescaled) when a tile's
@@ -48,10 +50,10 @@ namespace {
 #define GQA_FWD_NC 1      // 32-row column blocks per wave
 #endif
 #ifndef GQA_FWD_NW
-#define GQA_FWD_NW 4      // waves per workgroup
+#define GQA_FWD_NW 8      // waves per workgroup
 #endif
 #ifndef GQA_FWD_STAGES
-#define GQA_FWD_STAGES 2  // K/V ring depth
+#define GQA_FWD_STAGES 4  // K/V ring depth
 #endif
 #ifndef GQA_FWD_PREFETCH
 #define GQA_FWD_PREFETCH 6  // LDS operand reads kept in flight ahead of the MFMAs (0: compiler's choice)
@@ -63,6 +65,8 @@ constexpr int kNT = kBN / 32;     // 32-key score tiles per key tile
 constexpr int kStages = GQA_FWD_STAGES;
 constexpr int kThreads = 64 * kNW;
 constexpr int kWavesPerSimd = kNC == 1 ? 2 : 1;  // register budget: 256 or 512 per lane
+// workgroups per CU that keep kWavesPerSimd waves on each of the 4 SIMDs
+constexpr int kBlocksPerCu = (4 * kWavesPerSimd + kNW - 1) / kNW;
 
 template <int D>
 struct FwdSmem {
@@ -72,7 +76,7 @@ struct FwdSmem {
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads, kWavesPerSimd) void fwd_bf16_kernel(FwdArgs p)
+__global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArgs p)
 {
     constexpr int CPR = D / 8;                     // 16-byte chunks per row
     constexpr int KS = D / 16;                     // MFMA k-steps over the head dim
@@ -198,11 +202,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void fwd_bf16_kernel(FwdAr
     // One tile: S^T = K Q^T (each K operand feeds NC MFMAs), mask on
     // diagonal / ragged tiles, online softmax, O^T += V^T P^T (each V^T
     // operand feeds NC MFMAs).
-    auto step = [&](int it) {
-        const int k0 = it * kBN;
-        if (!(wave_active && k0 <= wlast)) return;
+    auto scores = [&](int it, f32x16 (&sc)[kNC][kNT]) {
         const char *ks_ = (const char *)sm.k[it % kStages];
-        f32x16 sc[kNC][kNT];
 #pragma unroll
         for (int cb = 0; cb < kNC; ++cb)
 #pragma unroll
@@ -234,6 +235,9 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void fwd_bf16_kernel(FwdAr
         }
 #endif
 
+    };
+    auto finish = [&](int it, f32x16 (&sc)[kNC][kNT]) {
+        const int k0 = it * kBN;
         const bool need_mask = (p.causal && k0 + kBN - 1 > off + q0) || (k0 + kBN > p.Tk);
         if (need_mask) {
 #pragma unroll
@@ -332,6 +336,8 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void fwd_bf16_kernel(FwdAr
             issue(kbase, sm.k[s_], s_ * kBN);
             issue(vbase, sm.v[s_], s_ * kBN);
         }
+    auto live = [&](int it) { return wave_active && it * kBN <= wlast; };  // tile it has keys this wave sees
+    f32x16 sc[kNC][kNT];
     for (int it = 0; it < ntiles; ++it) {
         if (it + kStages - 2 < ntiles)
             wait_vmem_le<(kStages - 2) * 2 * NINS>();  // tile it landed; later ones may fly
@@ -343,7 +349,10 @@ __global__ __launch_bounds__(kThreads, kWavesPerSimd) void fwd_bf16_kernel(FwdAr
             issue(kbase, sm.k[nx % kStages], nx * kBN);
             issue(vbase, sm.v[nx % kStages], nx * kBN);
         }
-        step(it);
+        if (live(it)) {
+            scores(it, sc);
+            finish(it, sc);
+        }
     }
 
     if (!wave_active) return;
