@@ -60,7 +60,10 @@ namespace {
 #endif
 constexpr int kNC = GQA_FWD_NC;
 constexpr int kNW = GQA_FWD_NW;
-constexpr int kBN = 64;           // keys per tile
+#ifndef GQA_FWD_BN
+#define GQA_FWD_BN 64     // keys per K/V tile
+#endif
+constexpr int kBN = GQA_FWD_BN;   // keys per tile
 constexpr int kNT = kBN / 32;     // 32-key score tiles per key tile
 constexpr int kStages = GQA_FWD_STAGES;
 constexpr int kThreads = 64 * kNW;
@@ -253,24 +256,17 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
         // moves (and its O column is rescaled) when a tile max exceeds it by
         // more than 2^8 -- and only for that lane, so a row never depends on
         // keys it cannot see
-        float mt[kNC];
-        bool any_move = false;
-#pragma unroll
-        for (int cb = 0; cb < kNC; ++cb) {
-            float mx = sc[cb][0][0];
-#pragma unroll
-            for (int t = 0; t < kNT; ++t)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[cb][t][e]);
-            mt[cb] = halves_max(mx) * c;
-            any_move |= mt[cb] > m_run[cb] + 8.0f;
-        }
-        if (__any(any_move)) {
+        auto move_ref = [&]() {
 #pragma unroll
             for (int cb = 0; cb < kNC; ++cb) {
-                const float m_new = (mt[cb] > m_run[cb] + 8.0f) ? mt[cb] : m_run[cb];
-                const float alpha =
-                    (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[cb] - m_new);
+                float mx = sc[cb][0][0];
+#pragma unroll
+                for (int t = 0; t < kNT; ++t)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[cb][t][e]);
+                const float mt = halves_max(mx) * c;
+                const float m_new = (mt > m_run[cb] + 8.0f) ? mt : m_run[cb];
+                const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[cb] - m_new);
                 m_run[cb] = m_new;
                 l_run[cb] *= alpha;
 #pragma unroll
@@ -278,29 +274,49 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
 #pragma unroll
                     for (int e = 0; e < 16; ++e) o[cb][i][e] *= alpha;
             }
-        }
+        };
         u32x4 pb[kNC][2 * kNT];
+        float ts[kNC];  // this lane's sum of the tile's weights
+        auto weights = [&]() {
 #pragma unroll
-        for (int cb = 0; cb < kNC; ++cb) {
-            const float m_use = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];
+            for (int cb = 0; cb < kNC; ++cb) {
+                const float m_use = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];
+                ts[cb] = 0.f;
 #pragma unroll
-            for (int t = 0; t < kNT; ++t) {
+                for (int t = 0; t < kNT; ++t) {
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    float pv[8];
+                    for (int h = 0; h < 2; ++h) {
+                        float pv[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cb][t][8 * h + e], c, -m_use));
-                    u32x4 pk;
-                    pk.x = pack_bf16x2(pv[0], pv[1]);
-                    pk.y = pack_bf16x2(pv[2], pv[3]);
-                    pk.z = pack_bf16x2(pv[4], pv[5]);
-                    pk.w = pack_bf16x2(pv[6], pv[7]);
-                    l_run[cb] = sum_bf16x8(pk, l_run[cb]);
-                    pb[cb][2 * t + h] = pk;
+                        for (int e = 0; e < 8; ++e)
+                            pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[cb][t][8 * h + e], c, -m_use));
+                        u32x4 pk;
+                        pk.x = pack_bf16x2(pv[0], pv[1]);
+                        pk.y = pack_bf16x2(pv[2], pv[3]);
+                        pk.z = pack_bf16x2(pv[4], pv[5]);
+                        pk.w = pack_bf16x2(pv[6], pv[7]);
+                        ts[cb] = sum_bf16x8(pk, ts[cb]);
+                        pb[cb][2 * t + h] = pk;
+                    }
                 }
             }
+        };
+        {
+            bool any_move = false;
+#pragma unroll
+            for (int cb = 0; cb < kNC; ++cb) {
+                float mx = sc[cb][0][0];
+#pragma unroll
+                for (int t = 0; t < kNT; ++t)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[cb][t][e]);
+                any_move |= halves_max(mx) * c > m_run[cb] + 8.0f;
+            }
+            if (__any(any_move)) move_ref();
+            weights();
         }
+#pragma unroll
+        for (int cb = 0; cb < kNC; ++cb) l_run[cb] += ts[cb];
 
         const char *vs_ = (const char *)sm.v[it % kStages];
 #pragma unroll
