@@ -91,12 +91,11 @@ int default_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int dtype)
     return (int)s;
 }
 
-// workspace: fp32 partial outputs [B, Hq, S, Dv], fp32 partial log2-sum-exp
-// [B, Hq, S], int32 partial counts per stream [<= B * Hq]
+// workspace: fp32 partial outputs [B, Hq, S, Dv], fp32 partial log2-sum-exp [B, Hq, S]
 size_t ws_bytes(int B, int Hq, int Dv, int S)
 {
     const size_t rows = (size_t)B * Hq * S;
-    size_t bytes = rows * Dv * sizeof(float) + rows * sizeof(float) + (size_t)B * Hq * sizeof(int);
+    size_t bytes = rows * Dv * sizeof(float) + rows * sizeof(float);
     return (bytes + 255) & ~(size_t)255;
 }
 
@@ -255,7 +254,6 @@ GQA_API int gqa_attn_decode(const void *q, const void *k, const void *v, void *o
     a.v_st = v_st;
     a.S = S;
     a.chunk = chunk;
-    a.counts = nullptr;
     a.n_wg = 0;
     hipStream_t st = (hipStream_t)stream;
 
@@ -265,7 +263,6 @@ GQA_API int gqa_attn_decode(const void *q, const void *k, const void *v, void *o
         if ((long long)B * Hkv * S > 0x7fffffffLL || a.n_hblk > 65535) return GQA_ERR_UNSUPPORTED;
         if (Dk <= 128 && S >= 3) {
             // flat decode (balanced over all sequences); S bounds the pieces per stream
-            a.counts = (int *)(a.part_lse + (size_t)B * Hq * S);
             a.n_wg = gqa::decode_bf16_flat_workgroups(Dk);
         }
         a.c = folded_scale(scale);
@@ -288,10 +285,5 @@ GQA_API int gqa_attn_decode(const void *q, const void *k, const void *v, void *o
     c.S = S;
     c.Dv = Dv;
     c.out_bf16 = dtype == GQA_BF16;
-    c.counts = a.counts;
-    c.lens = seq_lens;
-    c.Hkv = Hkv;
-    c.G = G;
-    c.n_hblk = a.n_hblk;
     return launch_status(gqa::launch_combine(c, st));
 }

@@ -7,9 +7,8 @@
 //     L = log2 sum_s 2^{lse_s},   o = sum_s 2^{lse_s - L} o_s,
 // the same merge online softmax applies tile by tile ("A Visual Guide to
 // Attention", section on sources and execution).  Empty chunks carry
-// lse = -inf and weigh nothing; a row with no keys at all yields zeros.
-// After the balanced (flat) decode a row has a variable number of pieces,
-// recorded per stream by the partial kernel.
+// lse = -inf and weigh nothing (their partial outputs are not even read);
+// a row with no keys at all yields zeros.
 #include "launch.h"
 
 namespace gqa {
@@ -24,31 +23,36 @@ __global__ __launch_bounds__(kCT) void combine_kernel(CombineArgs p)
     const size_t row = blockIdx.x;  // b * Hq + head
     const float *lse = p.part_lse + row * p.S;
     const float *po = p.part_o + row * (size_t)p.S * p.Dv;
-    int ns = p.S;
-    if (p.counts) {
-        const int b = (int)(row / p.Hq), head = (int)(row % p.Hq);
-        const int w = (b * p.Hkv + head / p.G) * p.n_hblk + (head % p.G) / 32;
-        ns = p.lens[b] > 0 ? p.counts[w] : 0;
-    }
+    const int ns = p.S;
 
+    // lane s of each wave holds split s (chunks of 64): max, then weights
+    const int lane = threadIdx.x & 63;
     float L = -INFINITY;
-    for (int s = 0; s < ns; ++s) L = fmaxf(L, lse[s]);
+    for (int s0 = 0; s0 < ns; s0 += 64) L = fmaxf(L, s0 + lane < ns ? lse[s0 + lane] : -INFINITY);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) L = fmaxf(L, __shfl_xor(L, o));
     const int d0 = threadIdx.x * 4;
-    if (d0 >= p.Dv) return;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     if (L != -INFINITY) {
-        for (int s = 0; s < ns; ++s) {
-            const float w = __builtin_amdgcn_exp2f(lse[s] - L);
-            if (w == 0.f) continue;
-            wsum += w;
-            const float4 v = *(const float4 *)(po + (size_t)s * p.Dv + d0);
-            acc[0] = fmaf(w, v.x, acc[0]);
-            acc[1] = fmaf(w, v.y, acc[1]);
-            acc[2] = fmaf(w, v.z, acc[2]);
-            acc[3] = fmaf(w, v.w, acc[3]);
+        for (int s0 = 0; s0 < ns; s0 += 64) {
+            const float wl = s0 + lane < ns ? __builtin_amdgcn_exp2f(lse[s0 + lane] - L) : 0.f;
+            const int n = min(64, ns - s0);
+#pragma unroll 4
+            for (int s = 0; s < n; ++s) {
+                const float w = __shfl(wl, s);
+                wsum += w;
+                if (w != 0.f && d0 < p.Dv) {  // empty slots (lse = -inf) are never read
+                    const float4 v = *(const float4 *)(po + (size_t)(s0 + s) * p.Dv + d0);
+                    acc[0] = fmaf(w, v.x, acc[0]);
+                    acc[1] = fmaf(w, v.y, acc[1]);
+                    acc[2] = fmaf(w, v.z, acc[2]);
+                    acc[3] = fmaf(w, v.w, acc[3]);
+                }
+            }
         }
     }
+    if (d0 >= p.Dv) return;
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     if (OUT_BF16) {
         uint16_t *out = (uint16_t *)p.out + row * p.Dv + d0;

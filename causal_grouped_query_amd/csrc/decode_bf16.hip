@@ -261,7 +261,9 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kern
 // nothing in balance, and each workgroup starts up once.  A workgroup writes
 // one normalised partial (o, lse) for every stream piece it covers, into
 // partial slot i - (first workgroup of that stream); the workgroup holding a
-// stream's first tile also records how many pieces the stream has.  N is
+// stream's first tile marks the slots past the stream's last piece empty
+// (lse = -inf), so the combine merges all S slots as for the chunked
+// schedule.  N is
 // capped so that no stream is cut into more than S pieces: consecutive cuts
 // are at least floor(T / N) tiles apart, so a stream of n tiles has at most
 // (n - 2) / floor(T / N) + 2 pieces.
@@ -301,7 +303,19 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
         nmax = max(nmax, __shfl_xor(nmax, o));
     }
     const long long T = tsum * H;
-    if (T == 0) return;  // every sequence is empty: the combine writes zeros
+    if (blockIdx.x == 0) {
+        // rows of empty sequences get no piece: mark all their partial slots
+        // empty (lse = -inf), so the combine writes zeros for them
+        for (int b0 = 0; b0 < p.B; b0 += 64) {
+            unsigned long long empty = __ballot(b0 + lane < p.B && ntile(p.lens[b0 + lane]) == 0);
+            while (empty) {
+                const int b = b0 + __ffsll((long long)empty) - 1;
+                empty &= empty - 1;
+                for (int i = lane; i < p.Hq * p.S; i += 64) p.part_lse[(size_t)b * p.Hq * p.S + i] = -INFINITY;
+            }
+        }
+    }
+    if (T == 0) return;
     const long long S2 = p.S - 2;  // the host uses this kernel only for S >= 3
     long long ne = T * S2 / ((nmax > 2 ? nmax - 2 : 0) + S2);
     ne = ne < 1 ? 1 : (ne > p.n_wg ? p.n_wg : ne);
@@ -570,8 +584,12 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
                     }
                 if (hi == 0) p.part_lse[prow] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
             }
-            if (j == 0 && lane == 0)
-                p.counts[(size_t)cc.b * H + cc.s] = (int)(wg_of(pw + cc.n - 1) - wi + 1);
+            if (j == 0 && head_ok && hi == 0) {
+                // slots past the stream's last piece are empty for the combine
+                const int count = (int)(wg_of(pw + cc.n - 1) - wi + 1);
+                const size_t prow0 = ((size_t)cc.b * p.Hq + head) * p.S;
+                for (int q = count; q < p.S; ++q) p.part_lse[prow0 + q] = -INFINITY;
+            }
         }
         advance(cc);
     }
@@ -617,8 +635,8 @@ int launch_flat(const DecodeArgs &a, hipStream_t stream)
 
 int launch_decode_bf16(const DecodeArgs &a, int Dk, int Dv, hipStream_t stream)
 {
-    if (a.counts) {
-        if (a.S < 3 || a.n_wg < 1) return -1;
+    if (a.n_wg > 0) {
+        if (a.S < 3) return -1;
         if (Dk == 128 && Dv == 128) return launch_flat<128, 128, GQA_DEC_STAGES>(a, stream);
         if (Dk == 64 && Dv == 64) return launch_flat<64, 64, 3>(a, stream);
         return -1;

@@ -43,8 +43,7 @@ struct DecodeArgs {
     int chunk;           // keys per split (multiple of the key tile)
     int n_hblk;          // head blocks per KV head
     float c;             // scale * log2(e)
-    int *counts;         // flat kernel: partials written per stream [B * Hkv * n_hblk]
-    int n_wg;            // flat kernel: workgroups launched
+    int n_wg;            // > 0: balanced (flat) schedule with this many workgroups
 };
 
 int launch_decode_bf16(const DecodeArgs &a, int Dk, int Dv, hipStream_t stream);
@@ -72,12 +71,6 @@ struct CombineArgs {
     void *out;           // [B, Hq, 1, Dv], bf16 or fp32
     int B, Hq, S, Dv;
     int out_bf16;
-    // flat decode: the number of partials of row (b, head) is
-    // counts[(b * Hkv + head / G) * n_hblk + (head % G) / 32] (0 when lens[b] <= 0);
-    // counts == nullptr: every row has S partials
-    const int *counts;
-    const int *lens;
-    int Hkv, G, n_hblk;
 };
 int launch_combine(const CombineArgs &a, hipStream_t stream);
 

@@ -85,9 +85,8 @@ int gqa_attn_decode_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int Dv, int
 
 /*
  * Bytes of device workspace gqa_attn_decode needs for num_splits splits
- * (num_splits >= 1): fp32 partial outputs [B, Hq, S, Dv], fp32 partial
- * log-sum-exp values [B, Hq, S] and B*Hq int32 piece counts.  Returns 0 for
- * invalid arguments.
+ * (num_splits >= 1): fp32 partial outputs [B, Hq, S, Dv] and fp32 partial
+ * log-sum-exp values [B, Hq, S].  Returns 0 for invalid arguments.
  */
 size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_splits);
 
