@@ -223,7 +223,10 @@ def main() -> int:
     del pre_sets, dq, dk, dv, dout, ws
     torch.cuda.empty_cache()
     result["context"] = {"hbm_copy_GBps": copy_bandwidth(torch, dev),
-                         "note": "plain 1 GiB device-to-device copy (reads + writes), the practical HBM rate"}
+                         "bf16_gemm_TFLOPs": gemm_rate(torch, dev),
+                         "note": "plain 1 GiB device-to-device copy (reads + writes), the practical HBM rate; "
+                                 "8192^3 bf16 GEMM through torch (hipBLASLt), a practical dense-MFMA rate "
+                                 "under the board power limit"}
 
     if not args.no_extra:
         result["extra"] = extra_workloads(torch, gqa, W, dev)
@@ -255,6 +258,17 @@ def copy_bandwidth(torch, dev) -> float:
     sec = _time(torch, lambda: dst.copy_(src), reps=5, warm=2)
     del src, dst
     return round(2 * n / sec / 1e9, 1)
+
+
+def gemm_rate(torch, dev) -> float:
+    n = 8192
+    g = torch.Generator(device=dev).manual_seed(7)
+    a = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+    b = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    sec = _time(torch, lambda: torch.matmul(a, b, out=c), reps=20, warm=5)
+    del a, b, c
+    return round(2.0 * n ** 3 / sec / 1e12, 1)
 
 
 def extra_workloads(torch, gqa, W, dev):

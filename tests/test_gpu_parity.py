@@ -242,7 +242,7 @@ def test_decode_zero_length_row_is_zero():
     assert torch.isfinite(out[1].float()).all()
 
 
-@pytest.mark.parametrize("Hq", [128, 16])
+@pytest.mark.parametrize("Hq", [128, 16, 160])
 @pytest.mark.parametrize("splits", [1, 3, 0])
 def test_mla_absorbed_decode_matches_oracle(Hq, splits):
     """Absorbed MLA: one 576-wide latent key per token, value = its first 512
@@ -259,6 +259,24 @@ def test_mla_absorbed_decode_matches_oracle(Hq, splits):
                      num_splits=splits)
     ref = O.attention(q, k, k[..., :512], scale, True, kv_lens=lens)
     _check(out, ref, "bf16", f"mla Hq={Hq} S={splits}")
+
+
+def test_mla_decode_empty_and_short_sequences():
+    """Absorbed MLA with an empty sequence (zero output) and sequences shorter
+    than one 32-key tile, several splits (most of them empty)."""
+    B, Hq, Tmax = 3, 128, 96
+    lens = [0, 5, 40]
+    q = _rand((B, Hq, 1, 576), 71, "bf16")
+    k = _rand((B, 1, Tmax, 576), 72, "bf16")
+    for b, n in enumerate(lens):
+        k[b, :, n:] = float("nan")
+    kd = k.cuda()
+    scale = 1.0 / math.sqrt(192)
+    out = gqa.decode(q.cuda(), kd, kd[..., :512], torch.tensor(lens, dtype=torch.int32).cuda(), scale=scale,
+                     num_splits=3)
+    assert torch.all(out[0] == 0)
+    ref = O.attention(q[1:], k[1:], k[1:, ..., :512], scale, True, kv_lens=lens[1:])
+    _check(out[1:], ref, "bf16", "mla short / empty")
 
 
 # ------------------------------------------------------------------ headline workloads, full size
