@@ -23,7 +23,11 @@
  *      variants", minimal semantic implementation and the section on masks
  *      and incremental positions)
  *   3. visible keys J = {0..p} when causal, else {0..Tk_b-1}; masked keys are
- *      left out of the sum, which is what a -inf additive mask does
+ *      left out of the sum, which is what a -inf additive mask does.  With a
+ *      sliding window of w positions (causal only) J = {max(0, p-w+1)..p}:
+ *      the w most recent positions, the current one included ("A Visual
+ *      Guide to Attention", section on which positions are visible: SWA
+ *      keeps direct access to the most recent w positions)
  *   4. s_j = scale * sum_d q[d] k_j[d]
  *   5. two-pass softmax: m = max_J s_j, e_j = exp(s_j - m), l = sum_J e_j,
  *      P_j = e_j / l ("Linear Attention and Sparse Attention" survey, 2.1:
@@ -78,20 +82,25 @@ typedef struct {
     int B, Hq, Hkv, Tq, Tk, Dk, Dv;
     double scale;
     int causal;
+    int window; /* 0: none; w > 0 (causal only): keys p-w+1 .. p */
 } problem;
 
-/* Number of keys of batch b, and the visible prefix length for query i. */
-static int visible_count(const problem *P, int b, int i, int *tk_b_out)
+/* Visible keys of query i of batch b: j in [*lo, return value). */
+static int visible_range(const problem *P, int b, int i, int *lo)
 {
     int tk_b = P->kv_lens ? P->kv_lens[b] : P->Tk;
     if (tk_b > P->Tk) tk_b = P->Tk;
     if (tk_b < 0) tk_b = 0;
-    *tk_b_out = tk_b;
+    *lo = 0;
     if (!P->causal) return tk_b;
     long long pos = (long long)tk_b - P->Tq + i; /* absolute query position */
     long long n = pos + 1;                       /* keys 0..pos are visible */
     if (n > tk_b) n = tk_b;
     if (n < 0) n = 0;
+    if (P->window > 0) {
+        long long first = pos - P->window + 1; /* the w most recent positions */
+        if (first > 0) *lo = (int)(first < n ? first : n);
+    }
     return (int)n;
 }
 
@@ -104,12 +113,12 @@ static void attend_row(const problem *P, int b, int a, int i, double *s, double 
 {
     int group = P->Hq / P->Hkv;
     int g = a / group; /* step 1: the KV head this query head reads */
-    int tk_b;
-    int n = visible_count(P, b, i, &tk_b); /* steps 2-3 */
+    int lo;
+    int n = visible_range(P, b, i, &lo); /* steps 2-3: keys lo .. n-1 */
 
     if (probs)
         for (int j = 0; j < P->Tk; ++j) probs[j] = 0.0;
-    if (n == 0) { /* no visible key: defined as a zero row, lse = -inf */
+    if (n <= lo) { /* no visible key: defined as a zero row, lse = -inf */
         for (int d = 0; d < P->Dv; ++d) out_row[d] = 0.0;
         if (lse_out) *lse_out = -INFINITY;
         return;
@@ -118,29 +127,29 @@ static void attend_row(const problem *P, int b, int a, int i, double *s, double 
     /* step 4: scores (the query row is widened once into the scratch tail) */
     double *qrow = s + P->Tk;
     for (int d = 0; d < P->Dk; ++d) qrow[d] = widen(&P->q, b, a, i, d);
-    for (int j = 0; j < n; ++j) {
+    for (int j = lo; j < n; ++j) {
         double acc = 0.0;
         for (int d = 0; d < P->Dk; ++d) acc += qrow[d] * widen(&P->k, b, g, j, d);
         s[j] = P->scale * acc;
     }
 
     /* step 5: first pass for the max, second for the exponentials */
-    double m = s[0];
-    for (int j = 1; j < n; ++j)
+    double m = s[lo];
+    for (int j = lo + 1; j < n; ++j)
         if (s[j] > m) m = s[j];
     double l = 0.0;
-    for (int j = 0; j < n; ++j) {
+    for (int j = lo; j < n; ++j) {
         s[j] = exp(s[j] - m);
         l += s[j];
     }
-    for (int j = 0; j < n; ++j) s[j] /= l; /* s now holds P_j */
+    for (int j = lo; j < n; ++j) s[j] /= l; /* s now holds P_j */
     if (probs)
-        for (int j = 0; j < n; ++j) probs[j] = s[j];
+        for (int j = lo; j < n; ++j) probs[j] = s[j];
 
     /* step 6: weighted sum of values */
     for (int d = 0; d < P->Dv; ++d) {
         double acc = 0.0;
-        for (int j = 0; j < n; ++j) acc += s[j] * widen(&P->v, b, g, j, d);
+        for (int j = lo; j < n; ++j) acc += s[j] * widen(&P->v, b, g, j, d);
         out_row[d] = acc;
     }
     if (lse_out) *lse_out = m + log(l);
@@ -153,6 +162,7 @@ static int check_problem(const problem *P)
         return -1;
     if (P->Hq % P->Hkv != 0) return -1;
     if (P->causal && !P->kv_lens && P->Tq > P->Tk) return -1;
+    if (P->window < 0 || (P->window > 0 && !P->causal)) return -1;
     return 0;
 }
 
@@ -175,6 +185,7 @@ static view4 make_view(const void *base, const long long *st, int dtype)
  * and storage types q_dt/k_dt/v_dt (0 bf16 bits, 1 fp32, 2 fp64).
  * kv_lens: NULL, or B per-sequence key counts (decode caches; keys at
  * positions >= len_b are never read).
+ * window: 0, or (with causal) the sliding-window width w >= 1.
  * out: fp64, contiguous [nrows, Dv] when rows != NULL, else [B, Hq, Tq, Dv].
  * lse: NULL or fp64 [nrows] / [B, Hq, Tq] (natural log).
  * rows: NULL, or nrows flattened row ids r = ((b*Hq) + a)*Tq + i.
@@ -183,7 +194,7 @@ static view4 make_view(const void *base, const long long *st, int dtype)
 int oracle_attention(const void *q, const long long *qs, int q_dt, const void *k,
                      const long long *ks, int k_dt, const void *v, const long long *vs,
                      int v_dt, const int *kv_lens, int B, int Hq, int Hkv, int Tq, int Tk,
-                     int Dk, int Dv, double scale, int causal, const long long *rows,
+                     int Dk, int Dv, double scale, int causal, int window, const long long *rows,
                      long long nrows, double *out, double *lse, int nthreads)
 {
     problem P;
@@ -200,6 +211,7 @@ int oracle_attention(const void *q, const long long *qs, int q_dt, const void *k
     P.Dv = Dv;
     P.scale = scale;
     P.causal = causal;
+    P.window = window;
     if (check_problem(&P)) return -1;
 
     long long total = rows ? nrows : (long long)B * Hq * Tq;
@@ -239,7 +251,8 @@ int oracle_attention(const void *q, const long long *qs, int q_dt, const void *k
 int oracle_probs(const void *q, const long long *qs, int q_dt, const void *k,
                  const long long *ks, int k_dt, const void *v, const long long *vs, int v_dt,
                  const int *kv_lens, int B, int Hq, int Hkv, int Tq, int Tk, int Dk, int Dv,
-                 double scale, int causal, int b, int a, int i, double *probs, double *out_row)
+                 double scale, int causal, int window, int b, int a, int i, double *probs,
+                 double *out_row)
 {
     problem P;
     P.q = make_view(q, qs, q_dt);
@@ -255,6 +268,7 @@ int oracle_probs(const void *q, const long long *qs, int q_dt, const void *k,
     P.Dv = Dv;
     P.scale = scale;
     P.causal = causal;
+    P.window = window;
     if (check_problem(&P) || b < 0 || b >= B || a < 0 || a >= Hq || i < 0 || i >= Tq) return -1;
     double *s = (double *)malloc(sizeof(double) * ((size_t)Tk + (size_t)Dk));
     if (!s) return -1;

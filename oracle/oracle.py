@@ -51,12 +51,12 @@ def _load():
         lib.oracle_attention.restype = I
         lib.oracle_attention.argtypes = [
             P, LLP, I, P, LLP, I, P, LLP, I, P,
-            I, I, I, I, I, I, I, ctypes.c_double, I, P, ctypes.c_longlong, P, P, I,
+            I, I, I, I, I, I, I, ctypes.c_double, I, I, P, ctypes.c_longlong, P, P, I,
         ]
         lib.oracle_probs.restype = I
         lib.oracle_probs.argtypes = [
             P, LLP, I, P, LLP, I, P, LLP, I, P,
-            I, I, I, I, I, I, I, ctypes.c_double, I, I, I, I, P, P,
+            I, I, I, I, I, I, I, ctypes.c_double, I, I, I, I, I, P, P,
         ]
         lib.oracle_lse_merge.restype = None
         lib.oracle_lse_merge.argtypes = [P, P, I, ctypes.c_longlong, I, P, P]
@@ -115,11 +115,13 @@ def _lens_arg(kv_lens, B):
 
 
 def attention(q, k, v, scale: float, causal: bool, kv_lens=None, rows=None, threads: int = 0,
-              with_lse: bool = False):
+              with_lse: bool = False, window: int = 0):
     """fp64 attention.  q [B,Hq,Tq,Dk], k [B,Hkv,Tk,Dk], v [B,Hkv,Tk,Dv].
 
     kv_lens: optional per-sequence key counts (a decode cache of capacity Tk);
-    rows: optional flat row ids ((b*Hq)+a)*Tq+i to compute only those rows.
+    rows: optional flat row ids ((b*Hq)+a)*Tq+i to compute only those rows;
+    window: 0, or (causal only) a sliding window of w positions: the query at
+    position p sees keys max(0, p-w+1) .. p.
     Returns out [B,Hq,Tq,Dv] (or [len(rows), Dv]) in fp64, plus lse if asked.
     """
     Q, K, V = _Operand(q), _Operand(k), _Operand(v)
@@ -141,7 +143,7 @@ def attention(q, k, v, scale: float, causal: bool, kv_lens=None, rows=None, thre
         rows_ptr = rows_arr.ctypes.data
     rc = _load().oracle_attention(
         Q.ptr, Q.strides, Q.code, K.ptr, K.strides, K.code, V.ptr, V.strides, V.code, lens_ptr,
-        B, Hq, Hkv, Tq, Tk, Dk, Dv, float(scale), int(bool(causal)), rows_ptr, nrows,
+        B, Hq, Hkv, Tq, Tk, Dk, Dv, float(scale), int(bool(causal)), int(window), rows_ptr, nrows,
         out.ctypes.data, lse.ctypes.data, int(threads),
     )
     if rc != 0:
@@ -149,7 +151,7 @@ def attention(q, k, v, scale: float, causal: bool, kv_lens=None, rows=None, thre
     return (out, lse) if with_lse else out
 
 
-def probs(q, k, v, scale: float, causal: bool, b: int, a: int, i: int, kv_lens=None):
+def probs(q, k, v, scale: float, causal: bool, b: int, a: int, i: int, kv_lens=None, window: int = 0):
     """The probability row P_j over all Tk keys (zeros where masked) and the output row."""
     Q, K, V = _Operand(q), _Operand(k), _Operand(v)
     B, Hq, Tq, Dk = Q.shape
@@ -160,12 +162,63 @@ def probs(q, k, v, scale: float, causal: bool, b: int, a: int, i: int, kv_lens=N
     o = np.empty((Dv,), dtype=np.float64)
     rc = _load().oracle_probs(
         Q.ptr, Q.strides, Q.code, K.ptr, K.strides, K.code, V.ptr, V.strides, V.code, lens_ptr,
-        B, Hq, Hkv, Tq, Tk, Dk, Dv, float(scale), int(bool(causal)), b, a, i,
+        B, Hq, Hkv, Tq, Tk, Dk, Dv, float(scale), int(bool(causal)), int(window), b, a, i,
         p.ctypes.data, o.ctypes.data,
     )
     if rc != 0:
         raise ValueError("oracle rejected the problem")
     return p, o
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: bool, window: int = 0,
+                     threads: int = 0):
+    """fp64 attention over packed variable-length sequences.
+
+    q [total_q, Hq, Dk], k [total_k, Hkv, Dk], v [total_k, Hkv, Dv] hold the
+    tokens of all sequences back to back; sequence i owns query tokens
+    cu_seqlens_q[i] .. cu_seqlens_q[i+1]-1 and key tokens cu_seqlens_k[i] ..
+    cu_seqlens_k[i+1]-1 (the packed-boundary reading of cu_seqlens on the
+    "Attention Architecture Evolution" page).  Tokens never attend across
+    sequences.  Within a sequence the rules of attention() apply (query j sits
+    at position Tk_i - Tq_i + j; causal; optional window); a query with no
+    visible key (Tq_i > Tk_i) gets a zero row.  Each sequence is computed by
+    attention() on strided views of its own tokens.  Returns out
+    [total_q, Hq, Dv] in fp64.
+    """
+    cq = [int(x) for x in cu_seqlens_q]
+    ck = [int(x) for x in cu_seqlens_k]
+    if len(cq) != len(ck) or len(cq) < 2:
+        raise ValueError("cu_seqlens_q / cu_seqlens_k must have the same length >= 2")
+    total_q, Hq, _ = q.shape
+    Dv = v.shape[2]
+    out = np.zeros((total_q, Hq, Dv), dtype=np.float64)
+
+    def view(x, s, e):  # tokens s..e-1 as a [1, H, T, D] strided view
+        try:
+            import torch
+            if isinstance(x, torch.Tensor):
+                return x[s:e].permute(1, 0, 2).unsqueeze(0)
+        except ImportError:  # pragma: no cover
+            pass
+        return np.asarray(x)[s:e].transpose(1, 0, 2)[None]
+
+    for i in range(len(cq) - 1):
+        tq, tk = cq[i + 1] - cq[i], ck[i + 1] - ck[i]
+        if tq <= 0:
+            continue
+        if tk <= 0 or (causal and tq > tk):
+            # rows with no visible key stay zero; the others follow attention()
+            if tk <= 0:
+                continue
+            qs = view(q, cq[i] + (tq - tk), cq[i + 1])
+            o = attention(qs, view(k, ck[i], ck[i + 1]), view(v, ck[i], ck[i + 1]), scale, causal,
+                          threads=threads, window=window)
+            out[cq[i] + (tq - tk):cq[i + 1]] = o[0].transpose(1, 0, 2)
+            continue
+        o = attention(view(q, cq[i], cq[i + 1]), view(k, ck[i], ck[i + 1]), view(v, ck[i], ck[i + 1]),
+                      scale, causal, threads=threads, window=window)
+        out[cq[i]:cq[i + 1]] = o[0].transpose(1, 0, 2)
+    return out
 
 
 def lse_merge(o_parts, lse_parts):

@@ -353,3 +353,154 @@ def test_rejects_bad_problems():
     k = np.zeros((1, 1, 3, 4))
     with pytest.raises(ValueError):
         O.attention(q, k, k, 1.0, True)  # causal with Tq > Tk
+
+
+# ---------------------------------------------------------------- sliding window
+# "A Visual Guide to Attention", section on which positions are visible: SWA
+# keeps direct access to the most recent w positions.  Reading: keys
+# max(0, p-w+1) .. p for the query at position p (the current position counts).
+
+@pytest.mark.parametrize("Tq,Tk", [(13, 13), (4, 19)])
+def test_window_at_least_all_keys_is_full_causal(Tq, Tk):
+    q = _rand((2, 4, Tq, 8), 80)
+    k = _rand((2, 2, Tk, 8), 81)
+    v = _rand((2, 2, Tk, 8), 82)
+    full = O.attention(q, k, v, 0.5, True)
+    for w in (Tk, Tk + 5):
+        np.testing.assert_array_equal(O.attention(q, k, v, 0.5, True, window=w), full)
+
+
+def test_window_of_one_returns_own_value():
+    """Each query sees only the key at its own position: P = 1 there."""
+    Tq, Tk = 6, 11
+    q = _rand((1, 4, Tq, 8), 83)
+    k = _rand((1, 2, Tk, 8), 84)
+    v = _rand((1, 2, Tk, 5), 85)
+    out = O.attention(q, k, v, 0.7, True, window=1)
+    for a in range(4):
+        np.testing.assert_array_equal(out[0, a], v[0, a // 2, Tk - Tq:].numpy())
+
+
+@pytest.mark.parametrize("w", [2, 3, 8])
+def test_zero_query_gives_window_mean(w):
+    """q = 0: uniform weights over the visible keys, i.e. the mean of
+    v[max(0, p-w+1) .. p]."""
+    Tq, Tk = 7, 12
+    q = torch.zeros((1, 2, Tq, 4), dtype=torch.float64)
+    k = _rand((1, 1, Tk, 4), 86)
+    v = _rand((1, 1, Tk, 3), 87)
+    out = O.attention(q, k, v, 1.0, True, window=w)
+    for i in range(Tq):
+        p = Tk - Tq + i
+        lo = max(0, p - w + 1)
+        exp = v[0, 0, lo:p + 1].numpy().mean(axis=0)
+        np.testing.assert_allclose(out[0, 0, i], exp, rtol=0, atol=1e-13)
+        np.testing.assert_allclose(out[0, 1, i], exp, rtol=0, atol=1e-13)
+
+
+def test_window_probabilities_vanish_outside_and_sum_to_one():
+    Tq, Tk, w = 5, 16, 6
+    q = _rand((1, 2, Tq, 8), 88)
+    k = _rand((1, 1, Tk, 8), 89)
+    v = _rand((1, 1, Tk, 8), 90)
+    for i in range(Tq):
+        p_row, _ = O.probs(q, k, v, 0.6, True, 0, 1, i, window=w)
+        pos = Tk - Tq + i
+        inside = (np.arange(Tk) >= pos - w + 1) & (np.arange(Tk) <= pos)
+        assert np.all(p_row[~inside] == 0.0)
+        assert np.all(p_row[inside] > 0.0)
+        assert abs(p_row.sum() - 1.0) < 1e-12
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Tq,Tk,w", [
+    (2, 4, 2, 9, 9, 3), (1, 8, 1, 5, 21, 4), (2, 6, 6, 17, 17, 16), (1, 2, 1, 1, 30, 7),
+])
+def test_window_matches_explicit_mask(B, Hq, Hkv, Tq, Tk, w):
+    """Independent masked softmax (torch SDPA, CPU float64) with the band mask
+    p-w < j <= p written out."""
+    q = _rand((B, Hq, Tq, 8), 91)
+    k = _rand((B, Hkv, Tk, 8), 92)
+    v = _rand((B, Hkv, Tk, 6), 93)
+    qpos = torch.arange(Tk - Tq, Tk)[:, None]
+    kpos = torch.arange(Tk)[None, :]
+    mask = (kpos <= qpos) & (kpos > qpos - w)
+    ref = F.scaled_dot_product_attention(q, k, v, attn_mask=mask, scale=0.45,
+                                         enable_gqa=(Hq != Hkv)).numpy()
+    np.testing.assert_allclose(O.attention(q, k, v, 0.45, True, window=w), ref, rtol=0, atol=1e-12)
+
+
+def test_window_needs_causal_and_positive_width():
+    q = np.zeros((1, 2, 3, 4))
+    k = np.zeros((1, 1, 3, 4))
+    with pytest.raises(ValueError):
+        O.attention(q, k, k, 1.0, False, window=2)
+    with pytest.raises(ValueError):
+        O.attention(q, k, k, 1.0, True, window=-1)
+
+
+# ---------------------------------------------------------------- packed variable length
+# "Attention Architecture Evolution", GDN section: cu_seqlens only marks the
+# boundaries of packed sequences; "Attention variants", masks section: a real
+# implementation needs padding / packed-segment masks.  Reading: tokens attend
+# only within their own sequence.
+
+def _packed_mask_reference(q, k, v, cq, ck, scale, causal, w):
+    """Whole packed problem as one masked softmax over all tokens (independent
+    of the per-sequence slicing): allowed(i, j) iff same sequence and the
+    causal / window rules hold inside it.  Rows with no allowed key are zero."""
+    tq, tk = cq[-1], ck[-1]
+    seq_q = np.searchsorted(cq, np.arange(tq), side="right") - 1
+    seq_k = np.searchsorted(ck, np.arange(tk), side="right") - 1
+    same = seq_q[:, None] == seq_k[None, :]
+    lq = np.arange(tq) - np.asarray(cq)[seq_q]           # index within its sequence
+    lk = np.arange(tk) - np.asarray(ck)[seq_k]
+    Tq_i = np.diff(cq)[seq_q]
+    Tk_i = np.diff(ck)[seq_q]
+    pos = (Tk_i - Tq_i + lq)[:, None]
+    allowed = same.copy()
+    if causal:
+        allowed &= lk[None, :] <= pos
+        if w > 0:
+            allowed &= lk[None, :] > pos - w
+    Hq, Hkv = q.shape[1], k.shape[1]
+    out = np.zeros((tq, Hq, v.shape[2]))
+    qq, kk, vv = q.numpy(), k.numpy(), v.numpy()
+    for a in range(Hq):
+        g = a // (Hq // Hkv)
+        s = scale * qq[:, a, :] @ kk[:, g, :].T
+        s = np.where(allowed, s, -np.inf)
+        m = s.max(axis=1, keepdims=True)
+        has = np.isfinite(m[:, 0])
+        e = np.where(allowed, np.exp(s - np.where(np.isfinite(m), m, 0.0)), 0.0)
+        l = e.sum(axis=1, keepdims=True)
+        pm = np.divide(e, l, out=np.zeros_like(e), where=l > 0)
+        out[:, a, :] = pm @ vv[:, g, :]
+        out[~has, a, :] = 0.0
+    return out
+
+
+@pytest.mark.parametrize("causal,w", [(True, 0), (True, 3), (False, 0)])
+def test_varlen_equals_block_diagonal_mask(causal, w):
+    lens_q = [5, 1, 9, 4]
+    lens_k = [5, 6, 9, 11]          # sequence 1 and 3: suffix queries
+    cq = np.concatenate([[0], np.cumsum(lens_q)]).tolist()
+    ck = np.concatenate([[0], np.cumsum(lens_k)]).tolist()
+    q = _rand((cq[-1], 4, 8), 94)
+    k = _rand((ck[-1], 2, 8), 95)
+    v = _rand((ck[-1], 2, 6), 96)
+    ours = O.attention_varlen(q, k, v, cq, ck, 0.55, causal, window=w)
+    ref = _packed_mask_reference(q, k, v, cq, ck, 0.55, causal, w)
+    np.testing.assert_allclose(ours, ref, rtol=0, atol=1e-12)
+
+
+def test_varlen_more_queries_than_keys_gives_zero_rows():
+    """Causal, Tq_i > Tk_i: the first Tq_i - Tk_i queries sit before key 0 and
+    see nothing (zero rows); the rest follow the suffix rule."""
+    cq, ck = [0, 6], [0, 4]
+    q = _rand((6, 2, 8), 97)
+    k = _rand((4, 1, 8), 98)
+    v = _rand((4, 1, 8), 99)
+    ours = O.attention_varlen(q, k, v, cq, ck, 0.5, True)
+    assert np.all(ours[:2] == 0.0)
+    ref = _packed_mask_reference(q, k, v, cq, ck, 0.5, True, 0)
+    np.testing.assert_allclose(ours, ref, rtol=0, atol=1e-12)
