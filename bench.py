@@ -36,8 +36,9 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "fwd_bf16_kernel": ["causal_grouped_query_amd/csrc/fwd_bf16.hip",
                         "causal_grouped_query_amd/csrc/device_common.h"],
-    "decode_bf16_kernel": ["causal_grouped_query_amd/csrc/decode_bf16.hip",
-                           "causal_grouped_query_amd/csrc/device_common.h"],
+    "decode_bf16_flat_kernel": ["causal_grouped_query_amd/csrc/decode_bf16.hip",
+                                "causal_grouped_query_amd/csrc/combine.hip",
+                                "causal_grouped_query_amd/csrc/device_common.h"],
 }
 
 
@@ -48,6 +49,17 @@ def causal_pairs(Tq: int, Tk: int) -> int:
 
 def fwd_flops(w) -> float:
     return 2.0 * (w.Dk + w.Dv) * causal_pairs(w.Tq, w.Tk) * w.Hq * w.B
+
+
+def varlen_flops(w) -> float:
+    """Visible (query, key) pairs of a packed sliding-window workload: a query
+    at position p of its sequence sees min(p + 1, window) keys."""
+    win = w.extra["window"]
+    pairs = 0
+    for n in w.extra["lens"]:
+        full = min(n, win)
+        pairs += full * (full + 1) // 2 + (n - full) * win
+    return 2.0 * (w.Dk + w.Dv) * pairs * w.Hq
 
 
 def decode_bytes(w, lens) -> float:
@@ -86,7 +98,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--no-extra", action="store_true", help="skip the MQA-suffix / MLA / fp32 workloads")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the MQA-suffix / sliding-window varlen / MLA / fp32 workloads")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -182,9 +195,9 @@ def main() -> int:
         "avg_launch_us": round(t_pre * 1e6, 2), "median_launch_us": round(t_pre_med * 1e6, 2),
         "flop_per_launch": F,
     }
-    trd = traffic_for("decode_bf16_kernel")
+    trd = traffic_for("decode_bf16_flat_kernel")
     roofline_decode = {
-        "kernel": f"decode_bf16_kernel<128,128> + combine_kernel (gqa_attn_decode, {S} splits)",
+        "kernel": f"decode_bf16_flat_kernel<128,128> + combine_kernel (gqa_attn_decode, balanced, {S} slots)",
         "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
         "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": trd,
         "avg_launch_us": round(t_dec * 1e6, 2), "median_launch_us": round(t_dec_med * 1e6, 2),
@@ -292,6 +305,18 @@ def extra_workloads(torch, gqa, W, dev):
     res[w.name] = {"us": round(sec * 1e6, 1), "TFLOP/s": round(f / sec / 1e12, 1),
                    "frac_mfma_peak": round(f / sec / 1e12 / PEAK_BF16_TFLOPS, 4)}
     del sets
+
+    w = W.SWA_VARLEN
+    q, k, v, cu = W.varlen_inputs(w)
+    q, k, v, cu = q.to(dev), k.to(dev), v.to(dev), cu.to(dev)
+    out = torch.empty((q.shape[0], w.Hq, w.Dv), dtype=torch.bfloat16, device=dev)
+    sec = _time(torch, lambda: gqa.attention_varlen(q, k, v, cu, cu, scale=w.scale, causal=True,
+                                                    window=w.extra["window"], out=out))
+    f = varlen_flops(w)
+    res[w.name] = {"us": round(sec * 1e6, 1), "TFLOP/s": round(f / sec / 1e12, 1),
+                   "frac_mfma_peak": round(f / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
+                   "flop_per_launch": f, "sequences": list(w.extra["lens"]), "window": w.extra["window"]}
+    del q, k, v, cu, out
 
     w = W.MLA_DECODE
     q, kc, _, lens = W.decode_inputs(w, nan_tail=False)

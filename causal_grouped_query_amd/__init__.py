@@ -5,6 +5,8 @@ kernels of the library.  PyTorch supplies device memory and the current
 stream.  There is no fallback: if the library is missing, every call raises.
 
     attention(q, k, v, scale=None, causal=True)       prefill / suffix forward
+    attention_varlen(q, k, v, cu_q, cu_k, scale=None, causal=True, window=0)
+                                                      packed variable-length forward, sliding window
     decode(q, k_cache, v_cache, seq_lens, scale=None) split-KV single-token decode
 
 Shapes follow the C header include/gqa_attn.h: q [B,Hq,Tq,Dk], k [B,Hkv,Tk,Dk],
@@ -18,16 +20,16 @@ import math
 import os
 
 __all__ = [
-    "LIB_PATH", "GQA_BF16", "GQA_F32", "GQAError", "lib", "attention", "decode", "decode_splits",
-    "decode_workspace_size", "strerror",
+    "LIB_PATH", "GQA_BF16", "GQA_F32", "GQAError", "lib", "attention", "attention_varlen", "decode",
+    "decode_splits", "decode_workspace_size", "strerror",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_attn.so")
 GQA_BF16, GQA_F32 = 0, 1
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP = 0, -1, -2, -3, -4
 
-EXPORTS = ("gqa_attn_fwd", "gqa_attn_decode", "gqa_attn_decode_splits", "gqa_attn_decode_workspace_size",
-           "gqa_attn_strerror")
+EXPORTS = ("gqa_attn_fwd", "gqa_attn_fwd_varlen", "gqa_attn_decode", "gqa_attn_decode_splits",
+           "gqa_attn_decode_workspace_size", "gqa_attn_strerror")
 
 _lib = None
 
@@ -50,6 +52,9 @@ def lib() -> ctypes.CDLL:
         P, I, LL, F, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_float, ctypes.c_size_t
         L.gqa_attn_fwd.restype = I
         L.gqa_attn_fwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, F, I, I, P]
+        L.gqa_attn_fwd_varlen.restype = I
+        L.gqa_attn_fwd_varlen.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, LL, LL, LL, LL, LL, LL, LL, LL, F,
+                                          I, I, I, P]
         L.gqa_attn_decode_splits.restype = I
         L.gqa_attn_decode_splits.argtypes = [I, I, I, I, I, I, I]
         L.gqa_attn_decode_workspace_size.restype = SZ
@@ -116,6 +121,59 @@ def attention(q, k, v, scale: float | None = None, causal: bool = True, out=None
                             Dk, Dv, float(scale), int(bool(causal)), _dtype_code(q), _stream())
     if rc != GQA_OK:
         raise GQAError(rc, "gqa_attn_fwd")
+    return out
+
+
+def _token_strides(t, name):
+    """(head stride, token stride) in elements of a [total, H, D] tensor view."""
+    if t.dim() != 3 or t.stride(2) != 1:
+        raise ValueError(f"{name} must be a 3-D [total, H, D] tensor with unit-stride D")
+    return t.stride(1), t.stride(0)
+
+
+def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float | None = None, causal: bool = True,
+                     window: int = 0, out=None):
+    """Packed variable-length forward.  q [total_q, Hq, Dk], k [total_k, Hkv, Dk],
+    v [total_k, Hkv, Dv] (any strides with unit-stride D), bfloat16; sequence i
+    owns tokens cu_seqlens[i] .. cu_seqlens[i+1]-1 (int32 device tensors of
+    num_seqs + 1 offsets).  window = w > 0 (causal only): each query sees its
+    w most recent positions.  cu_seqlens_q[-1] must equal q.shape[0].
+    Returns out [total_q, Hq, Dv].
+    """
+    import torch
+    _check_cuda(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_q.shape != cu_seqlens_k.shape or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q / cu_seqlens_k must be 1-D with the same num_seqs + 1 entries")
+    if not (cu_seqlens_q.is_contiguous() and cu_seqlens_k.is_contiguous()):
+        raise ValueError("cu_seqlens must be contiguous")
+    q_sh, q_st = _token_strides(q, "q")
+    k_sh, k_st = _token_strides(k, "k")
+    v_sh, v_st = _token_strides(v, "v")
+    total_q, Hq, Dk = q.shape
+    _, Hkv, Dk2 = k.shape
+    Dv = v.shape[2]
+    if Dk != Dk2 or v.shape[1] != Hkv or v.shape[0] != k.shape[0]:
+        raise ValueError("inconsistent q/k/v shapes")
+    n = cu_seqlens_q.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dk)
+    if out is None:
+        out = torch.empty((total_q, Hq, Dv), dtype=q.dtype, device=q.device)
+    elif out.shape != (total_q, Hq, Dv) or out.dtype != q.dtype:
+        raise ValueError("out must be a [total_q, Hq, Dv] tensor of q's dtype")
+    if total_q == 0:
+        return out  # no query token (an empty tensor has no storage to pass)
+    o_sh, o_st = _token_strides(out, "out")
+    rc = lib().gqa_attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), n, Hq, Hkv,
+                                   total_q, Dk, Dv, q_sh, q_st, k_sh, k_st, v_sh, v_st, o_sh, o_st,
+                                   float(scale), int(bool(causal)), int(window), _dtype_code(q), _stream())
+    if rc != GQA_OK:
+        raise GQAError(rc, "gqa_attn_fwd_varlen")
     return out
 
 

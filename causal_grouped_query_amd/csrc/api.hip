@@ -99,6 +99,32 @@ size_t ws_bytes(int B, int Hq, int Dv, int S)
     return (bytes + 255) & ~(size_t)255;
 }
 
+// Workgroup geometry of the bf16 forward kernel: one wave owns one query
+// head x rows_per_wave positions; a workgroup takes Gt heads of the group
+// (largest power of two dividing both G and the wave count) x Pt positions.
+// Tq is the (largest) query count per sequence.  False if the grid is too big.
+bool fwd_geometry(gqa::FwdArgs &a, int B, int Hq, int Hkv, int Tq)
+{
+    const int G = Hq / Hkv;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Tq = Tq;
+    a.G = G;
+    const int waves = gqa::fwd_bf16_waves_per_block();
+    const int rpw = gqa::fwd_bf16_rows_per_wave();
+    int gt = 1;
+    while (gt * 2 <= waves && G % (gt * 2) == 0) gt *= 2;
+    a.Gt = gt;
+    a.Pt = rpw * (waves / gt);
+    a.n_hblk = G / gt;
+    a.n_qt = (Tq + a.Pt - 1) / a.Pt;
+    const long long units = (long long)B * Hkv * a.n_hblk;
+    if (units * a.n_qt > 0x7fffffffLL) return false;
+    a.n_units = (int)units;
+    return true;
+}
+
 } // namespace
 
 GQA_API const char *gqa_attn_strerror(int code)
@@ -130,33 +156,16 @@ GQA_API int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out,
     if (dtype == GQA_BF16) {
         if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 8))
             return GQA_ERR_INVALID_ARG;
-        gqa::FwdArgs a;
+        gqa::FwdArgs a = {};
         a.q = (const uint16_t *)q;
         a.k = (const uint16_t *)k;
         a.v = (const uint16_t *)v;
         a.out = (uint16_t *)out;
-        a.B = B;
-        a.Hq = Hq;
-        a.Hkv = Hkv;
-        a.Tq = Tq;
         a.Tk = Tk;
-        a.G = G;
-        // one wave owns one query head x rows_per_wave positions; a workgroup
-        // takes Gt heads of the group (largest power of two dividing both G
-        // and the wave count) x Pt positions
-        const int waves = gqa::fwd_bf16_waves_per_block();
-        const int rpw = gqa::fwd_bf16_rows_per_wave();
-        int gt = 1;
-        while (gt * 2 <= waves && G % (gt * 2) == 0) gt *= 2;
-        a.Gt = gt;
-        a.Pt = rpw * (waves / gt);
-        a.n_hblk = G / gt;
-        a.n_qt = (Tq + a.Pt - 1) / a.Pt;
-        const long long units = (long long)B * Hkv * a.n_hblk;
-        if (units * a.n_qt > 0x7fffffffLL) return GQA_ERR_UNSUPPORTED;
-        a.n_units = (int)units;
+        if (!fwd_geometry(a, B, Hq, Hkv, Tq)) return GQA_ERR_UNSUPPORTED;
         a.causal = causal;
         a.c = folded_scale(scale);
+        a.varlen = 0;
         (void)hipGetLastError();
         return launch_status(gqa::launch_fwd_bf16(a, Dk, st));
     }
@@ -178,6 +187,62 @@ GQA_API int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out,
     a.scale = scale;
     (void)hipGetLastError();
     return launch_status(gqa::launch_fwd_f32(a, Dk, st));
+}
+
+GQA_API int gqa_attn_fwd_varlen(const void *q, const void *k, const void *v, void *out,
+                                const int *cu_seqlens_q, const int *cu_seqlens_k, int num_seqs, int Hq,
+                                int Hkv, int total_q, int Dk, int Dv, long long q_sh, long long q_st,
+                                long long k_sh, long long k_st, long long v_sh, long long v_st,
+                                long long o_sh, long long o_st, float scale, int causal, int window,
+                                int dtype, void *stream)
+{
+    if (!q || !k || !v || !out || !cu_seqlens_q || !cu_seqlens_k) return GQA_ERR_INVALID_ARG;
+    int rc = check_common(num_seqs, Hq, Hkv, Dk, Dv, scale, dtype);
+    if (rc != GQA_OK) return rc;
+    if (total_q < 0) return GQA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return GQA_ERR_INVALID_ARG;
+    if (window < 0 || (window > 0 && !causal)) return GQA_ERR_INVALID_ARG;
+    const long long in_strides[6] = {q_sh, q_st, k_sh, k_st, v_sh, v_st};
+    for (long long st : in_strides)
+        if (st <= 0 || st % 8 != 0) return GQA_ERR_INVALID_ARG;  // 16-byte rows
+    if (o_sh <= 0 || o_st <= 0 || o_sh % 4 != 0 || o_st % 4 != 0) return GQA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 8) ||
+        !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+        return GQA_ERR_INVALID_ARG;
+    if (dtype != GQA_BF16 || !head_dims_fwd(Dk, Dv)) return GQA_ERR_UNSUPPORTED;
+    // per-lane tile offsets are 32-bit: 63 rows of the larger key stride
+    if (63LL * (k_st > v_st ? k_st : v_st) * 2 + 2LL * Dk >= (1LL << 31)) return GQA_ERR_UNSUPPORTED;
+
+    gqa::FwdArgs a = {};
+    a.q = (const uint16_t *)q;
+    a.k = (const uint16_t *)k;
+    a.v = (const uint16_t *)v;
+    a.out = (uint16_t *)out;
+    a.Tk = 0;  // per sequence, from cu_seqlens_k
+    if (total_q == 0) return GQA_OK;  // no query token: nothing to write
+    if (!fwd_geometry(a, num_seqs, Hq, Hkv, 1)) return GQA_ERR_UNSUPPORTED;
+    // grid: (query tiles of all sequences) x (head units of one sequence);
+    // sum_i ceil(Tq_i / Pt) <= total_q / Pt + num_seqs
+    a.n_units = Hkv * a.n_hblk;
+    const long long ntile_bound = (long long)total_q / a.Pt + num_seqs;
+    if (ntile_bound * a.n_units > 0x7fffffffLL) return GQA_ERR_UNSUPPORTED;
+    a.n_qt = (int)ntile_bound;
+    a.causal = causal;
+    a.c = folded_scale(scale);
+    a.varlen = 1;
+    a.cu_q = cu_seqlens_q;
+    a.cu_k = cu_seqlens_k;
+    a.q_sh = q_sh;
+    a.q_st = q_st;
+    a.k_sh = k_sh;
+    a.k_st = k_st;
+    a.v_sh = v_sh;
+    a.v_st = v_st;
+    a.o_sh = o_sh;
+    a.o_st = o_st;
+    a.window = window;
+    (void)hipGetLastError();
+    return launch_status(gqa::launch_fwd_bf16(a, Dk, (hipStream_t)stream));
 }
 
 GQA_API int gqa_attn_decode_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int Dv, int dtype)

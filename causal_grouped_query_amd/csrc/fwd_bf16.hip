@@ -39,6 +39,10 @@
 //  * Grid order: tiles of one (batch, KV head, head block) are consecutive
 //    on one XCD (the dispatcher deals workgroups round-robin over 8 XCDs, so
 //    the remap keeps a KV head's K/V in one L2), heaviest causal tiles first.
+//  * Packed variable-length sequences (cu_seqlens) with an optional sliding
+//    window are the same kernel (template flag VAR): per-sequence bounds,
+//    strided token rows, a key loop that starts at the window's first tile
+//    and a lower mask bound per lane.
 #include "device_common.h"
 #include "launch.h"
 
@@ -78,7 +82,10 @@ struct FwdSmem {
     uint16_t v[kStages][TILE];
 };
 
-template <int D>
+// VAR: packed variable-length sequences (cu_seqlens), strided tensors and an
+// optional sliding window; false: the dense [B,H,T,D] problem (every VAR term
+// below folds away).
+template <int D, bool VAR>
 __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArgs p)
 {
     constexpr int CPR = D / 8;                     // 16-byte chunks per row
@@ -91,18 +98,70 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
 
     __shared__ __attribute__((aligned(1024))) FwdSmem<D> sm;
 
-    // ---- workgroup -> (unit, query tile), XCD-aware, heaviest first ----
+    // ---- workgroup -> (unit, query tile), heaviest first ----
+    // Dense: all units carry the same work, so consecutive query tiles of a
+    // unit go to one XCD (the dispatcher deals ids round-robin over 8 XCDs;
+    // the remap keeps a KV head's K/V in one L2).  Varlen: units differ in
+    // size, so ids run query-tile-major over all units and the round-robin
+    // spreads every sequence over the XCDs (with a multiple of 8 units each
+    // unit still stays on one XCD).
     const int nblk = gridDim.x;
     const int L = blockIdx.x;
-    const int xcd = L & 7, r = L >> 3;
-    const int per = nblk >> 3, rem = nblk & 7;
-    const int Lp = (xcd < rem) ? xcd * (per + 1) + r : rem * (per + 1) + (xcd - rem) * per + r;
-    const int unit = Lp / p.n_qt;
-    const int qt = p.n_qt - 1 - (Lp - unit * p.n_qt);
+    int unit, qt;
+    if (VAR) {
+        // ids enumerate (flat query tile f, head unit u of the sequence); u
+        // runs fastest so one tile's KV heads go to different XCDs.  f counts
+        // the query tiles of all sequences in order (the grid is an upper
+        // bound, there are no empty sequences' tiles in it); within a
+        // sequence the last tiles (most keys) come first.
+        const int u = L % p.n_units;
+        const int f = L / p.n_units;
+        const int lane0 = threadIdx.x & 63;
+        int base = 0, bsel = -1, fb1 = 0;
+        for (int b0 = 0; b0 < p.B; b0 += 64) {
+            const int bb = b0 + lane0;
+            const int nt = bb < p.B ? (max(p.cu_q[bb + 1] - p.cu_q[bb], 0) + p.Pt - 1) / p.Pt : 0;
+            int incl = nt;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(incl, o);
+                if (lane0 >= o) incl += y;
+            }
+            const unsigned long long hit = __ballot(bb < p.B && base + incl > f);
+            if (hit) {
+                const int Lh = __ffsll((long long)hit) - 1;
+                bsel = b0 + Lh;
+                fb1 = base + __shfl(incl, Lh);
+                break;
+            }
+            base += __shfl(incl, 63);
+        }
+        if (bsel < 0) return;  // past the last tile (whole workgroup, before any barrier)
+        qt = fb1 - 1 - f;
+        unit = __builtin_amdgcn_readfirstlane(bsel) * p.n_units + u;
+        qt = __builtin_amdgcn_readfirstlane(qt);
+    } else {
+        const int xcd = L & 7, r = L >> 3;
+        const int per = nblk >> 3, rem = nblk & 7;
+        const int Lp = (xcd < rem) ? xcd * (per + 1) + r : rem * (per + 1) + (xcd - rem) * per + r;
+        unit = Lp / p.n_qt;
+        qt = p.n_qt - 1 - (Lp - unit * p.n_qt);
+    }
     const int hblk = unit % p.n_hblk;
     const int bk = unit / p.n_hblk;  // b * Hkv + kv head
     const int kvh = bk % p.Hkv;
     const int b = bk / p.Hkv;
+
+    // sequence bounds: the whole problem, or sequence b of the packed batch
+    int Tq = p.Tq, Tk = p.Tk, sq0 = 0, sk0 = 0;
+    if (VAR) {
+        sq0 = p.cu_q[b];
+        sk0 = p.cu_k[b];
+        Tq = max(p.cu_q[b + 1] - sq0, 0);
+        Tk = max(p.cu_k[b + 1] - sk0, 0);
+        if (qt * p.Pt >= Tq) return;  // the whole workgroup (no barrier passed yet)
+    }
+    const int win = VAR ? p.window : 0;  // > 0: keys p-w+1 .. p only
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -110,22 +169,32 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
     const int col = lane & 31, hi = lane >> 5;
     const int head = kvh * p.G + hblk * p.Gt + (w % p.Gt);
     const int q0 = qt * p.Pt + (w / p.Gt) * ROWS;  // first query index of this wave
-    const int off = p.Tk - p.Tq;                   // absolute position of query 0
-    const bool wave_active = q0 < p.Tq;
+    const int off = Tk - Tq;                       // absolute position of query 0
+    const bool wave_active = q0 < Tq;
 
-    // keys the workgroup needs: [0, kend)
-    int kend = p.Tk;
-    if (p.causal) kend = min(p.Tk, off + min(p.Tq, qt * p.Pt + p.Pt));
-    const int ntiles = (kend + kBN - 1) / kBN;
+    // keys the workgroup needs: tiles [t0, t0 + ntiles)
+    int kend = Tk;
+    if (p.causal) kend = min(Tk, off + min(Tq, qt * p.Pt + p.Pt));
+    const int t0 = win > 0 ? max(0, off + qt * p.Pt - win + 1) / kBN : 0;
+    const int ntiles = max(0, (kend + kBN - 1) / kBN - t0);
     // last key any row of this wave can see
-    const int wlast = p.causal ? off + min(q0 + ROWS - 1, p.Tq - 1) : p.Tk - 1;
-    // last key each of this lane's queries can see
-    int lim[kNC];
+    const int wlast = p.causal ? off + min(q0 + ROWS - 1, Tq - 1) : Tk - 1;
+    // window: first key the wave's lowest row can see, and the largest first
+    // key of its rows (tiles starting below it need the lower mask)
+    const int wfirst = off + q0 - win + 1;
+    const int wlo_hi = off + min(q0 + ROWS - 1, Tq - 1) - win + 1;
+    // last (and with a window first) key each of this lane's queries can see
+    int lim[kNC], llo[kNC];
 #pragma unroll
-    for (int cb = 0; cb < kNC; ++cb) lim[cb] = p.causal ? min(off + q0 + 32 * cb + col, p.Tk - 1) : p.Tk - 1;
+    for (int cb = 0; cb < kNC; ++cb) {
+        lim[cb] = p.causal ? min(off + q0 + 32 * cb + col, Tk - 1) : Tk - 1;
+        llo[cb] = off + q0 + 32 * cb + col - win + 1;
+    }
 
-    const uint16_t *kbase = p.k + (size_t)bk * p.Tk * D;
-    const uint16_t *vbase = p.v + (size_t)bk * p.Tk * D;
+    // K / V rows: [B,Hkv,T,D] contiguous, or strided tokens of sequence b
+    const long long krs = VAR ? p.k_st : D, vrs = VAR ? p.v_st : D;  // elements between key rows
+    const uint16_t *kbase = VAR ? p.k + (size_t)kvh * p.k_sh + (size_t)sk0 * p.k_st : p.k + (size_t)bk * p.Tk * D;
+    const uint16_t *vbase = VAR ? p.v + (size_t)kvh * p.v_sh + (size_t)sk0 * p.v_st : p.v + (size_t)bk * p.Tk * D;
 
     // ---- async copies (plane layout, see PlaneTile) ----
     // Copy j of this wave fills 16-byte slots 64 (j * NW + w) + lane; the
@@ -133,27 +202,32 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
     // tile is computed once.  Rows past Tk re-read row Tk - 1 (in bounds,
     // masked).
     int grow_[NINS];
-    unsigned goff_[NINS];
+    unsigned goff_[NINS], gvoff_[NINS];  // byte offsets inside a K / V tile
 #pragma unroll
     for (int j = 0; j < NINS; ++j) {
         int row, chunk;
         Tile::slot_source((j * kNW + w) * 64 + lane, row, chunk);
         grow_[j] = row;
-        goff_[j] = (unsigned)(row * D + chunk * 8) * 2u;
+        goff_[j] = (unsigned)(row * krs + chunk * 8) * 2u;
+        gvoff_[j] = VAR ? (unsigned)(row * vrs + chunk * 8) * 2u : goff_[j];
     }
-    auto issue = [&](const uint16_t *src, uint16_t *dst, int k0) {
-        if (k0 + kBN <= p.Tk) {
-            const uint16_t *s0 = src + (size_t)k0 * D;
+    auto issue = [&](const uint16_t *src, uint16_t *dst, int k0, const unsigned (&offs)[NINS], long long rs) {
+        if (k0 + kBN <= Tk) {
+            const uint16_t *s0 = src + (size_t)k0 * rs;
 #pragma unroll
-            for (int j = 0; j < NINS; ++j) g2lds16(s0, goff_[j], dst + (j * kNW + w) * 64 * 8);
+            for (int j = 0; j < NINS; ++j) g2lds16(s0, offs[j], dst + (j * kNW + w) * 64 * 8);
         } else {
 #pragma unroll
             for (int j = 0; j < NINS; ++j) {
-                const int row = min(k0 + grow_[j], p.Tk - 1);
-                g2lds16((const char *)(src + (size_t)row * D) + (goff_[j] - (unsigned)grow_[j] * D * 2u),
+                const int row = min(k0 + grow_[j], Tk - 1);
+                g2lds16((const char *)(src + (size_t)row * rs) + (offs[j] - (unsigned)(grow_[j] * rs) * 2u),
                         dst + (j * kNW + w) * 64 * 8);
             }
         }
+    };
+    auto issue_kv = [&](int j, int slot) {  // tile t0 + j of the workgroup into ring slot `slot`
+        issue(kbase, sm.k[slot], (t0 + j) * kBN, goff_, krs);
+        issue(vbase, sm.v[slot], (t0 + j) * kBN, gvoff_, vrs);
     };
 
     // ---- Q^T in registers (B operands), zero for rows past Tq ----
@@ -161,8 +235,9 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
 #pragma unroll
     for (int cb = 0; cb < kNC; ++cb) {
         const int qi = q0 + 32 * cb + col;
-        const bool ok = wave_active && qi < p.Tq;
-        const uint16_t *qrow = p.q + (((size_t)b * p.Hq + head) * p.Tq + (ok ? qi : 0)) * D;
+        const bool ok = wave_active && qi < Tq;
+        const uint16_t *qrow = VAR ? p.q + (size_t)head * p.q_sh + (size_t)(sq0 + (ok ? qi : 0)) * p.q_st
+                                   : p.q + (((size_t)b * p.Hq + head) * p.Tq + (ok ? qi : 0)) * D;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             u32x4 z = {0u, 0u, 0u, 0u};
@@ -240,16 +315,18 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
 
     };
     auto finish = [&](int it, f32x16 (&sc)[kNC][kNT]) {
-        const int k0 = it * kBN;
-        const bool need_mask = (p.causal && k0 + kBN - 1 > off + q0) || (k0 + kBN > p.Tk);
+        const int k0 = (t0 + it) * kBN;
+        const bool need_mask = (p.causal && k0 + kBN - 1 > off + q0) || (k0 + kBN > Tk) || (win > 0 && k0 < wlo_hi);
         if (need_mask) {
 #pragma unroll
             for (int cb = 0; cb < kNC; ++cb)
 #pragma unroll
                 for (int t = 0; t < kNT; ++t)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        if (k0 + acc_key(t, e, hi) > lim[cb]) sc[cb][t][e] = -INFINITY;
+                    for (int e = 0; e < 16; ++e) {
+                        const int key = k0 + acc_key(t, e, hi);
+                        if (key > lim[cb] || (win > 0 && key < llo[cb])) sc[cb][t][e] = -INFINITY;
+                    }
         }
 
         // online softmax (base 2); the reference max of a lane's query only
@@ -348,11 +425,11 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
     // ring of kStages K/V slots: kStages - 1 tiles in flight while one is computed
 #pragma unroll
     for (int s_ = 0; s_ < kStages - 1; ++s_)
-        if (s_ < ntiles) {
-            issue(kbase, sm.k[s_], s_ * kBN);
-            issue(vbase, sm.v[s_], s_ * kBN);
-        }
-    auto live = [&](int it) { return wave_active && it * kBN <= wlast; };  // tile it has keys this wave sees
+        if (s_ < ntiles) issue_kv(s_, s_);
+    auto live = [&](int it) {  // tile t0 + it has keys this wave sees
+        const int k0 = (t0 + it) * kBN;
+        return wave_active && k0 <= wlast && (win <= 0 || k0 + kBN - 1 >= wfirst);
+    };
     f32x16 sc[kNC][kNT];
     for (int it = 0; it < ntiles; ++it) {
         if (it + kStages - 2 < ntiles)
@@ -361,10 +438,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
             wait_vmem();
         lds_barrier();  // tile it visible; the slot of tile it-1 is free
         const int nx = it + kStages - 1;
-        if (nx < ntiles) {
-            issue(kbase, sm.k[nx % kStages], nx * kBN);
-            issue(vbase, sm.v[nx % kStages], nx * kBN);
-        }
+        if (nx < ntiles) issue_kv(nx, nx % kStages);
         if (live(it)) {
             scores(it, sc);
             finish(it, sc);
@@ -375,10 +449,11 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
 #pragma unroll
     for (int cb = 0; cb < kNC; ++cb) {
         const int qi = q0 + 32 * cb + col;
-        if (qi >= p.Tq) continue;
+        if (qi >= Tq) continue;
         const float l_tot = halves_sum(l_run[cb]);
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t *orow = p.out + (((size_t)b * p.Hq + head) * p.Tq + qi) * D;
+        uint16_t *orow = VAR ? p.out + (size_t)head * p.o_sh + (size_t)(sq0 + qi) * p.o_st
+                             : p.out + (((size_t)b * p.Hq + head) * p.Tq + qi) * D;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
@@ -401,10 +476,14 @@ int launch_fwd_bf16(const FwdArgs &a, int D, hipStream_t stream)
     const long long nblk = (long long)a.n_units * a.n_qt;
     if (nblk <= 0 || nblk > 0x7fffffffLL) return -1;
     dim3 grid((unsigned)nblk), block(kThreads);
-    if (D == 128)
-        hipLaunchKernelGGL(fwd_bf16_kernel<128>, grid, block, 0, stream, a);
+    if (D == 128 && !a.varlen)
+        hipLaunchKernelGGL((fwd_bf16_kernel<128, false>), grid, block, 0, stream, a);
+    else if (D == 64 && !a.varlen)
+        hipLaunchKernelGGL((fwd_bf16_kernel<64, false>), grid, block, 0, stream, a);
+    else if (D == 128)
+        hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), grid, block, 0, stream, a);
     else if (D == 64)
-        hipLaunchKernelGGL(fwd_bf16_kernel<64>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, stream, a);
     else
         return -1;
     return 0;

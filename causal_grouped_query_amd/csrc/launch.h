@@ -22,6 +22,14 @@ struct FwdArgs {
     int n_units; // B * Hkv * n_hblk
     int causal;
     float c;     // scale * log2(e), > 0
+    // packed variable-length mode (varlen != 0): B sequences, sequence b owns
+    // query tokens cu_q[b] .. cu_q[b+1]-1 and key tokens cu_k[b] .. cu_k[b+1]-1;
+    // element (h, t, d) of q sits at q + h*q_sh + t*q_st + d (likewise k, v,
+    // out); Tq = largest query count (grid); window > 0: keys p-w+1 .. p only
+    int varlen;
+    const int *cu_q, *cu_k;
+    long long q_sh, q_st, k_sh, k_st, v_sh, v_st, o_sh, o_st;
+    int window;
 };
 
 int launch_fwd_bf16(const FwdArgs &a, int D, hipStream_t stream);

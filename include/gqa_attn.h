@@ -20,7 +20,7 @@
  * MQA over a 576-wide shared latent key whose first 512 columns are the value.
  *
  * Conventions for every entry point
- *  - Pointers q, k, v, out, seq_lens and workspace are DEVICE pointers
+ *  - Pointers q, k, v, out, seq_lens, cu_seqlens and workspace are DEVICE pointers
  *    (hipMalloc'd or torch CUDA tensors).  The caller owns all buffers; the
  *    library never allocates, frees or synchronises.
  *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
@@ -36,6 +36,7 @@
  *
  * Supported head dims (anything else returns GQA_ERR_UNSUPPORTED):
  *    gqa_attn_fwd:     (Dk, Dv) = (64, 64) or (128, 128), bf16 or fp32
+ *    gqa_attn_fwd_varlen: (64, 64) or (128, 128), bf16
  *    gqa_attn_decode:  (64, 64) or (128, 128), bf16 or fp32;
  *                      (576, 512) bf16 (the absorbed-MLA shape)
  */
@@ -74,6 +75,49 @@ enum {
  */
 int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv,
                  int Tq, int Tk, int Dk, int Dv, float scale, int causal, int dtype, void *stream);
+
+/*
+ * Forward over packed variable-length sequences, with an optional sliding
+ * window.  The "Attention variants" page (section on masks and incremental
+ * positions) lists padding / packed-segment masks and sliding-window
+ * patterns among the masks a real implementation has to handle; cu_seqlens
+ * marks packed sequence boundaries ("Attention Architecture Evolution", GDN
+ * code section); SWA keeps direct access to the most recent w positions ("A
+ * Visual Guide to Attention", section on which positions are visible).
+ *
+ * num_seqs sequences are stored back to back along the token axis.
+ * cu_seqlens_q / cu_seqlens_k: DEVICE int32 arrays of num_seqs + 1
+ * non-decreasing offsets; sequence i owns query tokens cu_seqlens_q[i] ..
+ * cu_seqlens_q[i+1]-1 and key tokens cu_seqlens_k[i] .. cu_seqlens_k[i+1]-1.
+ * Element (h, t, d) of each tensor sits at ptr + h*X_sh + t*X_st + d
+ * (element strides; d is unit-stride): q (Hq heads, Dk), k (Hkv, Dk),
+ * v (Hkv, Dv), out (Hq, Dv).  [total, H, D] row-major has X_sh = D,
+ * X_st = H*D; [H, total, D] has X_sh = total*D, X_st = D.  Tokens attend only
+ * within their own sequence; inside a sequence with Tq_i queries and Tk_i
+ * keys the rules of gqa_attn_fwd apply (query j at position Tk_i - Tq_i + j).
+ * causal = 1 with window = w > 0: query at position p sees keys
+ * max(0, p-w+1) .. p (the w most recent positions, its own included).
+ * window = 0: no window.  A query with no visible key (causal and
+ * Tq_i > Tk_i: the first Tq_i - Tk_i queries) gets a zero row.
+ *
+ * total_q is the number of packed query tokens, cu_seqlens_q[num_seqs]; it
+ * sizes the grid (sum_i ceil(Tq_i / tile) <= total_q / tile + num_seqs), and
+ * total_q = 0 returns GQA_OK with nothing enqueued.  The offsets are device
+ * data and cannot be checked on the host: they must lie inside the buffers
+ * and agree with total_q.  Query rows of out are written in
+ * full; out must not overlap itself or the inputs.
+ * Requirements (else GQA_ERR_INVALID_ARG): q, k, v 16-byte aligned, out 8,
+ * cu arrays 4; q/k/v head and token strides positive multiples of 8
+ * elements, out strides positive multiples of 4; window >= 0 and only with
+ * causal = 1; total_q >= 0.  bf16 only, (Dk, Dv) = (64, 64) or (128, 128); fp32 and other
+ * dims return GQA_ERR_UNSUPPORTED, as do key / value token strides st with
+ * 126 * st + 2 * Dk >= 2^31 (tile offsets are 32-bit byte offsets).
+ */
+int gqa_attn_fwd_varlen(const void *q, const void *k, const void *v, void *out, const int *cu_seqlens_q,
+                        const int *cu_seqlens_k, int num_seqs, int Hq, int Hkv, int total_q, int Dk,
+                        int Dv, long long q_sh, long long q_st, long long k_sh, long long k_st, long long v_sh,
+                        long long v_st, long long o_sh, long long o_st, float scale, int causal, int window,
+                        int dtype, void *stream);
 
 /*
  * Split count the decode entry point uses when called with num_splits = 0.

@@ -14,7 +14,10 @@ Recipe (the same for every workload and size):
     position >= len_b is overwritten with NaN, because those slots are not
     part of the input and must not reach the output;
   * the weight-absorbed MLA shape draws only q and k: the value is the first
-    512 columns of the 576-wide key (latent 512 + rope 64), taken as a view.
+    512 columns of the 576-wide key (latent 512 + rope 64), taken as a view;
+  * packed variable-length workloads draw all tokens of all sequences at once
+    in the [total, H, D] layout; cu_seqlens are the running sums of the
+    listed lengths.
 """
 from __future__ import annotations
 
@@ -29,7 +32,7 @@ _DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "fwd", "decode", "mla_decode", "fwd+decode"
+    kind: str  # "fwd", "decode", "mla_decode", "fwd+decode", "fwd_varlen"
     B: int
     Hq: int
     Hkv: int
@@ -62,6 +65,27 @@ MLA_DECODE = Workload("mla_absorbed_decode_b16_hq128_tk32768_dk576_dv512", "mla_
                       32768, 576, 512, "bf16", 4, 1.0 / math.sqrt(192), len_lo=32768, len_hi=32768)
 
 ALL = [TINY_F32, GQA_PREFILL, GQA_DECODE, MQA_SUFFIX, MLA_DECODE]
+
+# Sliding-window prefill over packed sequences of mixed lengths (GQA 32q / 8kv,
+# d128, window 4096: the GQA + SWA pairing the pages name for Mistral 7B).
+# B = number of packed sequences; Tq = Tk = the longest one.
+SWA_VARLEN = Workload("swa_varlen_prefill_hq32_hkv8_d128_w4096_16k_tokens", "fwd_varlen", 8, 32, 8, 8192, 8192,
+                      128, 128, "bf16", 5, 1.0 / math.sqrt(128),
+                      extra={"lens": (8192, 4096, 2048, 1024, 512, 256, 128, 128), "window": 4096})
+
+
+def varlen_inputs(w: Workload):
+    """Packed tokens for a fwd_varlen workload (CPU): q [total, Hq, Dk],
+    k [total, Hkv, Dk], v [total, Hkv, Dv] (drawn q, k, v in that order) and
+    cu_seqlens int32 [B + 1] (the same offsets for queries and keys)."""
+    lens = list(w.extra["lens"])
+    total = sum(lens)
+    g = torch.Generator("cpu").manual_seed(w.seed)
+    q = _randn(g, (total, w.Hq, w.Dk), w.dtype)
+    k = _randn(g, (total, w.Hkv, w.Dk), w.dtype)
+    v = _randn(g, (total, w.Hkv, w.Dv), w.dtype)
+    cu = torch.tensor([0] + [sum(lens[: i + 1]) for i in range(len(lens))], dtype=torch.int32)
+    return q, k, v, cu
 
 
 def _randn(gen: torch.Generator, shape, dtype: str) -> torch.Tensor:
