@@ -171,7 +171,7 @@ def probs(q, k, v, scale: float, causal: bool, b: int, a: int, i: int, kv_lens=N
 
 
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: bool, window: int = 0,
-                     threads: int = 0):
+                     threads: int = 0, seqused_q=None, seqused_k=None):
     """fp64 attention over packed variable-length sequences.
 
     q [total_q, Hq, Dk], k [total_k, Hkv, Dk], v [total_k, Hkv, Dv] hold the
@@ -184,11 +184,30 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: 
     visible key (Tq_i > Tk_i) gets a zero row.  Each sequence is computed by
     attention() on strided views of its own tokens.  Returns out
     [total_q, Hq, Dv] in fp64.
+
+    Padding ("Attention variants", masks section, lists padding masks beside
+    packed-segment masks): with seqused_q / seqused_k given, sequence i uses
+    only the first min(seqused[i], slot length) tokens of its slot; the rest
+    are padding.  Padded keys are invisible, padded query rows are not part of
+    the result (returned as zeros), and the causal offset is taken between the
+    used lengths.  A right-padded batch [B, Tpad, H, D] is then cu_seqlens =
+    0, Tpad, 2 Tpad, ... with seqused = the true lengths.
     """
     cq = [int(x) for x in cu_seqlens_q]
     ck = [int(x) for x in cu_seqlens_k]
     if len(cq) != len(ck) or len(cq) < 2:
         raise ValueError("cu_seqlens_q / cu_seqlens_k must have the same length >= 2")
+
+    def used(cu, u):  # token count of each sequence, padding excluded
+        n = [max(cu[i + 1] - cu[i], 0) for i in range(len(cu) - 1)]
+        if u is None:
+            return n
+        u = [int(x) for x in u]
+        if len(u) != len(n):
+            raise ValueError("seqused must hold one length per sequence")
+        return [min(max(a, 0), b) for a, b in zip(u, n)]
+
+    nq, nk = used(cq, seqused_q), used(ck, seqused_k)
     total_q, Hq, _ = q.shape
     Dv = v.shape[2]
     out = np.zeros((total_q, Hq, Dv), dtype=np.float64)
@@ -203,21 +222,17 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: 
         return np.asarray(x)[s:e].transpose(1, 0, 2)[None]
 
     for i in range(len(cq) - 1):
-        tq, tk = cq[i + 1] - cq[i], ck[i + 1] - ck[i]
-        if tq <= 0:
-            continue
-        if tk <= 0 or (causal and tq > tk):
-            # rows with no visible key stay zero; the others follow attention()
-            if tk <= 0:
-                continue
-            qs = view(q, cq[i] + (tq - tk), cq[i + 1])
-            o = attention(qs, view(k, ck[i], ck[i + 1]), view(v, ck[i], ck[i + 1]), scale, causal,
-                          threads=threads, window=window)
-            out[cq[i] + (tq - tk):cq[i + 1]] = o[0].transpose(1, 0, 2)
-            continue
-        o = attention(view(q, cq[i], cq[i + 1]), view(k, ck[i], ck[i + 1]), view(v, ck[i], ck[i + 1]),
-                      scale, causal, threads=threads, window=window)
-        out[cq[i]:cq[i + 1]] = o[0].transpose(1, 0, 2)
+        tq, tk = nq[i], nk[i]
+        qe, ke = cq[i] + tq, ck[i] + tk  # ends of the used tokens
+        if tq <= 0 or tk <= 0:
+            continue  # no query row, or no key: rows stay zero
+        qs = cq[i]
+        if causal and tq > tk:
+            # the first tq - tk queries sit before key 0: zero rows
+            qs = cq[i] + (tq - tk)
+        o = attention(view(q, qs, qe), view(k, ck[i], ke), view(v, ck[i], ke), scale, causal,
+                      threads=threads, window=window)
+        out[qs:qe] = o[0].transpose(1, 0, 2)
     return out
 
 

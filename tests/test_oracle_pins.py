@@ -444,9 +444,10 @@ def test_window_needs_causal_and_positive_width():
 # implementation needs padding / packed-segment masks.  Reading: tokens attend
 # only within their own sequence.
 
-def _packed_mask_reference(q, k, v, cq, ck, scale, causal, w):
+def _packed_mask_reference(q, k, v, cq, ck, scale, causal, w, uq=None, uk=None):
     """Whole packed problem as one masked softmax over all tokens (independent
-    of the per-sequence slicing): allowed(i, j) iff same sequence and the
+    of the per-sequence slicing): allowed(i, j) iff same sequence, neither
+    token is padding (index within the sequence >= its used length) and the
     causal / window rules hold inside it.  Rows with no allowed key are zero."""
     tq, tk = cq[-1], ck[-1]
     seq_q = np.searchsorted(cq, np.arange(tq), side="right") - 1
@@ -454,10 +455,12 @@ def _packed_mask_reference(q, k, v, cq, ck, scale, causal, w):
     same = seq_q[:, None] == seq_k[None, :]
     lq = np.arange(tq) - np.asarray(cq)[seq_q]           # index within its sequence
     lk = np.arange(tk) - np.asarray(ck)[seq_k]
-    Tq_i = np.diff(cq)[seq_q]
-    Tk_i = np.diff(ck)[seq_q]
+    nq = np.diff(cq) if uq is None else np.asarray(uq)
+    nk = np.diff(ck) if uk is None else np.asarray(uk)
+    Tq_i = nq[seq_q]
+    Tk_i = nk[seq_q]
     pos = (Tk_i - Tq_i + lq)[:, None]
-    allowed = same.copy()
+    allowed = same & (lq < Tq_i)[:, None] & (lk < nk[seq_k])[None, :]
     if causal:
         allowed &= lk[None, :] <= pos
         if w > 0:
@@ -504,3 +507,53 @@ def test_varlen_more_queries_than_keys_gives_zero_rows():
     assert np.all(ours[:2] == 0.0)
     ref = _packed_mask_reference(q, k, v, cq, ck, 0.5, True, 0)
     np.testing.assert_allclose(ours, ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- padding
+# "Attention variants", masks section: padding masks.  Reading: sequence i
+# uses the first seqused[i] tokens of its slot; padded keys are invisible,
+# padded query rows are not computed (zero in the oracle's result).
+
+@pytest.mark.parametrize("causal,w", [(True, 0), (True, 4), (False, 0)])
+def test_padding_equals_explicit_padding_mask(causal, w):
+    Tpad, lens_q, lens_k = 12, [12, 3, 0, 7], [12, 9, 5, 7]
+    cu = [i * Tpad for i in range(5)]
+    q = _rand((4 * Tpad, 4, 8), 110)
+    k = _rand((4 * Tpad, 2, 8), 111)
+    v = _rand((4 * Tpad, 2, 6), 112)
+    ours = O.attention_varlen(q, k, v, cu, cu, 0.5, causal, window=w, seqused_q=lens_q, seqused_k=lens_k)
+    ref = _packed_mask_reference(q, k, v, cu, cu, 0.5, causal, w, lens_q, lens_k)
+    np.testing.assert_allclose(ours, ref, rtol=0, atol=1e-12)
+
+
+def test_padding_content_is_ignored_and_matches_packed():
+    """A right-padded batch gives the packed batch of the same tokens, and
+    nothing in the padding changes any used row."""
+    Tpad, lens = 10, [10, 4, 7]
+    cu = [0, 10, 20, 30]
+    q = _rand((30, 2, 8), 113)
+    k = _rand((30, 1, 8), 114)
+    v = _rand((30, 1, 8), 115)
+    pad = O.attention_varlen(q, k, v, cu, cu, 0.6, True, seqused_q=lens, seqused_k=lens)
+    idx = np.concatenate([np.arange(c, c + n) for c, n in zip(cu, lens)])
+    cp = [0] + np.cumsum(lens).tolist()
+    packed = O.attention_varlen(q[idx], k[idx], v[idx], cp, cp, 0.6, True)
+    np.testing.assert_array_equal(pad[idx], packed)
+    keep = np.zeros(30, dtype=bool)
+    keep[idx] = True
+    assert np.all(pad[~keep] == 0.0)
+    q2, k2, v2 = q.clone(), k.clone(), v.clone()
+    for t in np.flatnonzero(~keep):
+        q2[t], k2[t], v2[t] = 1e3, -1e3, float("nan")
+    pad2 = O.attention_varlen(q2, k2, v2, cu, cu, 0.6, True, seqused_q=lens, seqused_k=lens)
+    np.testing.assert_array_equal(pad2, pad)
+
+
+def test_seqused_longer_than_slot_is_clamped():
+    cu = [0, 5, 9]
+    q = _rand((9, 2, 8), 116)
+    k = _rand((9, 2, 8), 117)
+    v = _rand((9, 2, 8), 118)
+    a = O.attention_varlen(q, k, v, cu, cu, 0.5, True, seqused_q=[50, 4], seqused_k=[5, 99])
+    b = O.attention_varlen(q, k, v, cu, cu, 0.5, True)
+    np.testing.assert_array_equal(a, b)
