@@ -53,7 +53,7 @@ def lib() -> ctypes.CDLL:
         L.gqa_attn_fwd.restype = I
         L.gqa_attn_fwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, F, I, I, P]
         L.gqa_attn_fwd_varlen.restype = I
-        L.gqa_attn_fwd_varlen.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, LL, LL, LL, LL, LL, LL, LL, LL, F,
+        L.gqa_attn_fwd_varlen.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, LL, LL, LL, LL, LL, LL, LL, LL, F,
                                           I, I, I, P]
         L.gqa_attn_decode_splits.restype = I
         L.gqa_attn_decode_splits.argtypes = [I, I, I, I, I, I, I]
@@ -132,13 +132,15 @@ def _token_strides(t, name):
 
 
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float | None = None, causal: bool = True,
-                     window: int = 0, out=None):
+                     window: int = 0, out=None, seqused_q=None, seqused_k=None):
     """Packed variable-length forward.  q [total_q, Hq, Dk], k [total_k, Hkv, Dk],
     v [total_k, Hkv, Dv] (any strides with unit-stride D), bfloat16; sequence i
     owns tokens cu_seqlens[i] .. cu_seqlens[i+1]-1 (int32 device tensors of
     num_seqs + 1 offsets).  window = w > 0 (causal only): each query sees its
     w most recent positions.  cu_seqlens_q[-1] must equal q.shape[0].
-    Returns out [total_q, Hq, Dv].
+    seqused_q / seqused_k (int32 device tensors of num_seqs entries, optional):
+    only the first seqused[i] tokens of slot i are used, the rest is padding;
+    padded query rows of out are not written.  Returns out [total_q, Hq, Dv].
     """
     import torch
     _check_cuda(q, k, v, cu_seqlens_q, cu_seqlens_k)
@@ -150,6 +152,15 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float | None = 
         raise ValueError("cu_seqlens_q / cu_seqlens_k must be 1-D with the same num_seqs + 1 entries")
     if not (cu_seqlens_q.is_contiguous() and cu_seqlens_k.is_contiguous()):
         raise ValueError("cu_seqlens must be contiguous")
+    used = []
+    for u in (seqused_q, seqused_k):
+        if u is None:
+            used.append(None)
+            continue
+        _check_cuda(u)
+        if u.dtype != torch.int32 or u.dim() != 1 or u.numel() != cu_seqlens_q.numel() - 1 or not u.is_contiguous():
+            raise ValueError("seqused must be a contiguous int32 tensor of num_seqs entries")
+        used.append(u.data_ptr())
     q_sh, q_st = _token_strides(q, "q")
     k_sh, k_st = _token_strides(k, "k")
     v_sh, v_st = _token_strides(v, "v")
@@ -169,7 +180,7 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float | None = 
         return out  # no query token (an empty tensor has no storage to pass)
     o_sh, o_st = _token_strides(out, "out")
     rc = lib().gqa_attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                   cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), n, Hq, Hkv,
+                                   cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), used[0], used[1], n, Hq, Hkv,
                                    total_q, Dk, Dv, q_sh, q_st, k_sh, k_st, v_sh, v_st, o_sh, o_st,
                                    float(scale), int(bool(causal)), int(window), _dtype_code(q), _stream())
     if rc != GQA_OK:

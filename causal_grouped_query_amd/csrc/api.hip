@@ -190,7 +190,8 @@ GQA_API int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out,
 }
 
 GQA_API int gqa_attn_fwd_varlen(const void *q, const void *k, const void *v, void *out,
-                                const int *cu_seqlens_q, const int *cu_seqlens_k, int num_seqs, int Hq,
+                                const int *cu_seqlens_q, const int *cu_seqlens_k,
+                                const int *seqused_q, const int *seqused_k, int num_seqs, int Hq,
                                 int Hkv, int total_q, int Dk, int Dv, long long q_sh, long long q_st,
                                 long long k_sh, long long k_st, long long v_sh, long long v_st,
                                 long long o_sh, long long o_st, float scale, int causal, int window,
@@ -207,7 +208,8 @@ GQA_API int gqa_attn_fwd_varlen(const void *q, const void *k, const void *v, voi
         if (st <= 0 || st % 8 != 0) return GQA_ERR_INVALID_ARG;  // 16-byte rows
     if (o_sh <= 0 || o_st <= 0 || o_sh % 4 != 0 || o_st % 4 != 0) return GQA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 8) ||
-        !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4))
+        !aligned(cu_seqlens_q, 4) || !aligned(cu_seqlens_k, 4) || !aligned(seqused_q, 4) ||
+        !aligned(seqused_k, 4))
         return GQA_ERR_INVALID_ARG;
     if (dtype != GQA_BF16 || !head_dims_fwd(Dk, Dv)) return GQA_ERR_UNSUPPORTED;
     // per-lane tile offsets are 32-bit: 63 rows of the larger key stride
@@ -232,6 +234,8 @@ GQA_API int gqa_attn_fwd_varlen(const void *q, const void *k, const void *v, voi
     a.varlen = 1;
     a.cu_q = cu_seqlens_q;
     a.cu_k = cu_seqlens_k;
+    a.used_q = seqused_q;  // null: the whole slot
+    a.used_k = seqused_k;
     a.q_sh = q_sh;
     a.q_st = q_st;
     a.k_sh = k_sh;

@@ -42,7 +42,9 @@
 //  * Packed variable-length sequences (cu_seqlens) with an optional sliding
 //    window are the same kernel (template flag VAR): per-sequence bounds,
 //    strided token rows, a key loop that starts at the window's first tile
-//    and a lower mask bound per lane.
+//    and a lower mask bound per lane.  Optional used lengths per sequence
+//    turn the tail of each slot into padding (a right-padded batch): padded
+//    keys are never read, padded query rows never written.
 #include "device_common.h"
 #include "launch.h"
 
@@ -85,6 +87,14 @@ struct FwdSmem {
 // VAR: packed variable-length sequences (cu_seqlens), strided tensors and an
 // optional sliding window; false: the dense [B,H,T,D] problem (every VAR term
 // below folds away).
+// tokens of packed sequence b: its slot length, or the used length when
+// given (clamped to the slot; the rest of the slot is padding)
+__device__ __forceinline__ int used_len(const int *cu, const int *used, int b)
+{
+    const int n = max(cu[b + 1] - cu[b], 0);
+    return used ? min(max(used[b], 0), n) : n;
+}
+
 template <int D, bool VAR>
 __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArgs p)
 {
@@ -120,7 +130,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
         int base = 0, bsel = -1, fb1 = 0;
         for (int b0 = 0; b0 < p.B; b0 += 64) {
             const int bb = b0 + lane0;
-            const int nt = bb < p.B ? (max(p.cu_q[bb + 1] - p.cu_q[bb], 0) + p.Pt - 1) / p.Pt : 0;
+            const int nt = bb < p.B ? (used_len(p.cu_q, p.used_q, bb) + p.Pt - 1) / p.Pt : 0;
             int incl = nt;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
@@ -157,8 +167,8 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
     if (VAR) {
         sq0 = p.cu_q[b];
         sk0 = p.cu_k[b];
-        Tq = max(p.cu_q[b + 1] - sq0, 0);
-        Tk = max(p.cu_k[b + 1] - sk0, 0);
+        Tq = used_len(p.cu_q, p.used_q, b);
+        Tk = used_len(p.cu_k, p.used_k, b);
         if (qt * p.Pt >= Tq) return;  // the whole workgroup (no barrier passed yet)
     }
     const int win = VAR ? p.window : 0;  // > 0: keys p-w+1 .. p only

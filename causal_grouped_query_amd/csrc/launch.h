@@ -23,11 +23,15 @@ struct FwdArgs {
     int causal;
     float c;     // scale * log2(e), > 0
     // packed variable-length mode (varlen != 0): B sequences, sequence b owns
-    // query tokens cu_q[b] .. cu_q[b+1]-1 and key tokens cu_k[b] .. cu_k[b+1]-1;
-    // element (h, t, d) of q sits at q + h*q_sh + t*q_st + d (likewise k, v,
-    // out); Tq = largest query count (grid); window > 0: keys p-w+1 .. p only
+    // the slots of query tokens cu_q[b] .. cu_q[b+1]-1 and key tokens
+    // cu_k[b] .. cu_k[b+1]-1, of which the first used_q[b] / used_k[b]
+    // (clamped to the slot; all of it when the pointer is null) are tokens and
+    // the rest padding; element (h, t, d) of q sits at q + h*q_sh + t*q_st + d
+    // (likewise k, v, out); n_qt = bound on the query tiles of all sequences;
+    // window > 0: keys p-w+1 .. p only
     int varlen;
     const int *cu_q, *cu_k;
+    const int *used_q, *used_k;
     long long q_sh, q_st, k_sh, k_st, v_sh, v_st, o_sh, o_st;
     int window;
 };

@@ -100,21 +100,30 @@ int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out, int B, 
  * window = 0: no window.  A query with no visible key (causal and
  * Tq_i > Tk_i: the first Tq_i - Tk_i queries) gets a zero row.
  *
- * total_q is the number of packed query tokens, cu_seqlens_q[num_seqs]; it
+ * Padding (the same page's padding masks): seqused_q / seqused_k, DEVICE
+ * int32 arrays of num_seqs entries or NULL.  When given, sequence i uses only
+ * the first min(max(seqused[i], 0), slot length) tokens of its slot and the
+ * rest is padding: padded keys are never read, padded query rows of out are
+ * never written (left as they were), and Tq_i / Tk_i above are the used
+ * lengths.  A right-padded batch [B, Tpad, H, D] is cu_seqlens = 0, Tpad,
+ * 2*Tpad, ... with seqused = the true lengths.  NULL: every slot is used.
+ *
+ * total_q is the number of packed query slots, cu_seqlens_q[num_seqs]; it
  * sizes the grid (sum_i ceil(Tq_i / tile) <= total_q / tile + num_seqs), and
  * total_q = 0 returns GQA_OK with nothing enqueued.  The offsets are device
  * data and cannot be checked on the host: they must lie inside the buffers
- * and agree with total_q.  Query rows of out are written in
+ * and agree with total_q.  Used query rows of out are written in
  * full; out must not overlap itself or the inputs.
  * Requirements (else GQA_ERR_INVALID_ARG): q, k, v 16-byte aligned, out 8,
- * cu arrays 4; q/k/v head and token strides positive multiples of 8
+ * cu and seqused arrays 4; q/k/v head and token strides positive multiples of 8
  * elements, out strides positive multiples of 4; window >= 0 and only with
  * causal = 1; total_q >= 0.  bf16 only, (Dk, Dv) = (64, 64) or (128, 128); fp32 and other
  * dims return GQA_ERR_UNSUPPORTED, as do key / value token strides st with
  * 126 * st + 2 * Dk >= 2^31 (tile offsets are 32-bit byte offsets).
  */
 int gqa_attn_fwd_varlen(const void *q, const void *k, const void *v, void *out, const int *cu_seqlens_q,
-                        const int *cu_seqlens_k, int num_seqs, int Hq, int Hkv, int total_q, int Dk,
+                        const int *cu_seqlens_k, const int *seqused_q, const int *seqused_k,
+                        int num_seqs, int Hq, int Hkv, int total_q, int Dk,
                         int Dv, long long q_sh, long long q_st, long long k_sh, long long k_st, long long v_sh,
                         long long v_st, long long o_sh, long long o_st, float scale, int causal, int window,
                         int dtype, void *stream);

@@ -70,11 +70,12 @@ def test_fwd_rejects_on_host(kw, code):
 
 def _fwd_varlen(**kw):
     H, D = 4, 128
-    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, cq=FAKE, ck=FAKE, n=2, Hq=H, Hkv=2, maxq=16, Dk=D, Dv=D,
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, cq=FAKE, ck=FAKE, uq=None, uk=None, n=2, Hq=H, Hkv=2, maxq=16, Dk=D, Dv=D,
              qsh=D, qst=H * D, ksh=D, kst=2 * D, vsh=D, vst=2 * D, osh=D, ost=H * D, scale=0.1, causal=1,
              window=0, dtype=BF16)
     a.update(kw)
-    return gqa.lib().gqa_attn_fwd_varlen(a["q"], a["k"], a["v"], a["out"], a["cq"], a["ck"], a["n"], a["Hq"],
+    return gqa.lib().gqa_attn_fwd_varlen(a["q"], a["k"], a["v"], a["out"], a["cq"], a["ck"], a["uq"], a["uk"],
+                                         a["n"], a["Hq"],
                                          a["Hkv"], a["maxq"], a["Dk"], a["Dv"], a["qsh"], a["qst"], a["ksh"],
                                          a["kst"], a["vsh"], a["vst"], a["osh"], a["ost"], a["scale"],
                                          a["causal"], a["window"], a["dtype"], None)
@@ -85,7 +86,8 @@ def _fwd_varlen(**kw):
     (dict(maxq=-1), INVALID), (dict(Hq=6, Hkv=4), INVALID), (dict(causal=2), INVALID),
     (dict(window=-1), INVALID), (dict(window=4, causal=0), INVALID), (dict(qst=100), INVALID),
     (dict(kst=0), INVALID), (dict(vsh=-8), INVALID), (dict(ost=6), INVALID), (dict(k=FAKE + 8), INVALID),
-    (dict(cq=FAKE + 2), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(cq=FAKE + 2), INVALID), (dict(uq=FAKE + 2), INVALID), (dict(uk=FAKE + 1), INVALID),
+    (dict(scale=float("nan")), INVALID),
     (dict(dtype=F32), UNSUP), (dict(Dk=96, Dv=96), UNSUP), (dict(Dk=576, Dv=512), UNSUP),
     (dict(kst=1 << 25), UNSUP), (dict(vst=1 << 25), UNSUP),
 ])

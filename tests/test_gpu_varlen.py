@@ -169,3 +169,59 @@ def test_varlen_no_query_tokens_is_a_no_op():
     ck = torch.tensor([0, 10], dtype=torch.int32, device="cuda")
     out = gqa.attention_varlen(q, k, k, cq, ck)
     assert out.shape == (0, 4, 128)
+
+
+@pytest.mark.parametrize("causal,window,used_q,used_k", [
+    (True, 0, [300, 1, 0, 129, 64], [300, 1, 7, 129, 64]),
+    (True, 50, [300, 200, 65, 2, 256], [300, 200, 65, 2, 256]),
+    (True, 0, [10, 64, 1, 0, 33], [290, 64, 100, 8, 300]),     # suffix queries inside padded slots
+    (True, 0, [90, 3, 256], [40, 3, 0]),                        # more queries than keys: zero rows
+    (False, 0, [17, 300, 0], [300, 5, 44]),
+])
+def test_varlen_right_padded_batch(causal, window, used_q, used_k):
+    """A right-padded batch [B, Tpad, H, D] through cu_seqlens = multiples of
+    Tpad and the used lengths: padded keys hold NaN and are never read, padded
+    query rows keep what out held before (a sentinel), used rows match the
+    oracle."""
+    B, Tpad, Hq, Hkv, D = len(used_q), 300, 8, 2, 128
+    seed = 100 + sum(used_q)
+    q = _rand((B * Tpad, Hq, D), seed)
+    k = _rand((B * Tpad, Hkv, D), seed + 1)
+    v = _rand((B * Tpad, Hkv, D), seed + 2)
+    cu = [i * Tpad for i in range(B + 1)]
+    keep_q = np.zeros(B * Tpad, dtype=bool)
+    keep_k = np.zeros(B * Tpad, dtype=bool)
+    for i in range(B):
+        keep_q[cu[i]:cu[i] + used_q[i]] = True
+        keep_k[cu[i]:cu[i] + used_k[i]] = True
+    kd, vd = k.clone(), v.clone()
+    kd[~keep_k] = float("nan")
+    vd[~keep_k] = float("nan")
+    cud = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    uq = torch.tensor(used_q, dtype=torch.int32, device="cuda")
+    uk = torch.tensor(used_k, dtype=torch.int32, device="cuda")
+    out = torch.full((B * Tpad, Hq, D), 7.0, dtype=torch.bfloat16, device="cuda")
+    gqa.attention_varlen(q.cuda(), kd.cuda(), vd.cuda(), cud, cud, causal=causal, window=window, out=out,
+                         seqused_q=uq, seqused_k=uk)
+    ref = O.attention_varlen(q, k, v, cu, cu, 1.0 / np.sqrt(D), causal, window=window,
+                             seqused_q=used_q, seqused_k=used_k)
+    got = out.cpu()
+    assert torch.all(got[torch.from_numpy(~keep_q)] == 7.0), "padded query rows were written"
+    _check(got[torch.from_numpy(keep_q)], ref[keep_q], f"padded batch causal={causal} w={window}")
+
+
+def test_varlen_padding_equals_packed():
+    """The padded batch and the packed batch of the same tokens give
+    bit-identical rows (same arithmetic, different addressing)."""
+    Tpad, lens = 260, [260, 70, 129, 1]
+    B, Hq, Hkv, D = len(lens), 4, 1, 64
+    q = _rand((B * Tpad, Hq, D), 120).cuda()
+    k = _rand((B * Tpad, Hkv, D), 121).cuda()
+    v = _rand((B * Tpad, Hkv, D), 122).cuda()
+    cu = torch.tensor([i * Tpad for i in range(B + 1)], dtype=torch.int32, device="cuda")
+    used = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    pad = gqa.attention_varlen(q, k, v, cu, cu, causal=True, window=33, seqused_q=used, seqused_k=used)
+    idx = torch.cat([torch.arange(i * Tpad, i * Tpad + n) for i, n in enumerate(lens)]).cuda()
+    cp = torch.tensor([0] + np.cumsum(lens).tolist(), dtype=torch.int32, device="cuda")
+    packed = gqa.attention_varlen(q[idx], k[idx], v[idx], cp, cp, causal=True, window=33)
+    assert torch.equal(pad[idx], packed)
