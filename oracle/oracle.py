@@ -236,6 +236,54 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float, causal: 
     return out
 
 
+def decode_topk(q, kv, kv_lens, indices, scale: float, Dv: int, threads: int = 0):
+    """fp64 single-token decode over a selected subset of the cached keys.
+
+    DeepSeek Sparse Attention on the absorbed MLA ("Attention Architecture
+    Evolution", DSA section): an indexer picks for each query token a set J
+    of cached positions, and the main attention keeps only those: the index
+    mask is -inf everywhere except 0 at the listed positions, added to the
+    scores before the softmax.  Written, as the page's production target
+    describes it, as a gather of the listed latent rows followed by ordinary
+    attention over them (masked keys carry weight exactly 0, so the two
+    orders give the same result).
+
+    q [B, Hq, 1, Dk]; kv [B, 1, Tmax, Dk] is the latent cache, whose first Dv
+    columns are the value (MLA: V is the latent prefix of K); kv_lens [B]
+    valid cache lengths; indices [B, topk] integer positions.  J_b is the SET
+    of listed positions inside [0, kv_lens[b]) (the mask is a scatter, so a
+    repeated position counts once; entries outside the range, such as -1
+    padding, select nothing).  An empty J_b gives a zero row.  Returns
+    [B, Hq, 1, Dv] in fp64.
+    """
+    try:
+        import torch
+        is_torch = isinstance(kv, torch.Tensor)
+    except ImportError:  # pragma: no cover
+        is_torch = False
+    B, Hq, one, Dk = q.shape
+    if one != 1 or kv.shape[0] != B or kv.shape[1] != 1 or kv.shape[3] != Dk or not 0 < Dv <= Dk:
+        raise ValueError("decode_topk: q [B,Hq,1,Dk], kv [B,1,Tmax,Dk], 0 < Dv <= Dk")
+    def host(x):  # torch tensor or array-like -> int64 numpy
+        return np.asarray(x.cpu() if hasattr(x, "cpu") else x, dtype=np.int64)
+
+    idx, lens = host(indices), host(kv_lens)
+    if idx.ndim != 2 or idx.shape[0] != B or lens.shape != (B,):
+        raise ValueError("decode_topk: indices [B, topk], kv_lens [B]")
+    Tmax = kv.shape[2]
+    out = np.zeros((B, Hq, 1, Dv), dtype=np.float64)
+    for b in range(B):
+        n = min(max(int(lens[b]), 0), Tmax)
+        J = sorted({int(j) for j in idx[b] if 0 <= j < n})
+        if not J:
+            continue
+        sel = torch.as_tensor(J) if is_torch else np.asarray(J)
+        kj = kv[b:b + 1, :, sel, :]        # gathered [1, 1, |J|, Dk]
+        vj = kj[..., :Dv]
+        out[b:b + 1] = attention(q[b:b + 1], kj, vj, scale, False, threads=threads)
+    return out
+
+
 def lse_merge(o_parts, lse_parts):
     """Exact merge of partial results over disjoint key ranges.
 

@@ -557,3 +557,82 @@ def test_seqused_longer_than_slot_is_clamped():
     a = O.attention_varlen(q, k, v, cu, cu, 0.5, True, seqused_q=[50, 4], seqused_k=[5, 99])
     b = O.attention_varlen(q, k, v, cu, cu, 0.5, True)
     np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------------------- DSA top-k decode
+# "Attention Architecture Evolution", DSA section: the indexer's top-k
+# positions become a mask that is -inf except at the selected positions
+# (scattered zeros), added to the absorbed MLA scores before the softmax.
+
+def _dsa_dense_mask_reference(q, kv, lens, idx, scale, Dv):
+    """The page's reference order: dense scores over every cached position,
+    plus an index mask built by scattering zeros into -inf, softmax, then the
+    latent aggregation (independent of the gather in the oracle)."""
+    qq, kk = q.double().numpy(), kv.double().numpy()
+    B, Hq = qq.shape[0], qq.shape[1]
+    out = np.zeros((B, Hq, 1, Dv))
+    for b in range(B):
+        n = int(lens[b])
+        s = scale * qq[b, :, 0, :] @ kk[b, 0, :n, :].T          # [Hq, n]
+        mask = np.full(n, -np.inf)
+        sel = [int(j) for j in idx[b] if 0 <= j < n]
+        mask[sel] = 0.0
+        s = s + mask[None, :]
+        if not sel:
+            continue
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        p = e / e.sum(axis=1, keepdims=True)
+        out[b, :, 0, :] = p @ kk[b, 0, :n, :Dv]
+    return out
+
+
+def test_dsa_topk_equals_dense_scores_plus_index_mask():
+    B, Hq, Tmax, Dk, Dv = 3, 4, 40, 24, 16
+    q = _rand((B, Hq, 1, Dk), 130)
+    kv = _rand((B, 1, Tmax, Dk), 131)
+    lens = [40, 17, 33]
+    rng = np.random.default_rng(132)
+    idx = np.stack([rng.choice(n, 9, replace=False) for n in lens])
+    ours = O.decode_topk(q, kv, lens, idx, 0.3, Dv)
+    ref = _dsa_dense_mask_reference(q, kv, lens, idx, 0.3, Dv)
+    np.testing.assert_allclose(ours, ref, rtol=0, atol=1e-12)
+
+
+def test_dsa_all_positions_selected_is_dense_decode():
+    B, Hq, Tmax, Dk, Dv = 2, 6, 30, 16, 12
+    q = _rand((B, Hq, 1, Dk), 133)
+    kv = _rand((B, 1, Tmax, Dk), 134)
+    lens = [30, 11]
+    rng = np.random.default_rng(135)
+    idx = np.full((B, 30), -1)
+    for b, n in enumerate(lens):
+        idx[b, :n] = rng.permutation(n)
+    ours = O.decode_topk(q, kv, lens, idx, 0.25, Dv)
+    dense = O.attention(q, kv, kv[..., :Dv], 0.25, True, kv_lens=lens)
+    np.testing.assert_allclose(ours, dense, rtol=0, atol=1e-12)
+
+
+def test_dsa_single_selected_position_returns_its_latent():
+    q = _rand((2, 3, 1, 16), 136)
+    kv = _rand((2, 1, 20, 16), 137)
+    idx = np.array([[7, -1, 25], [-3, 19, 19]])          # one valid position each
+    ours = O.decode_topk(q, kv, [20, 20], idx, 0.5, 10)
+    np.testing.assert_array_equal(ours[0, :, 0], np.broadcast_to(kv[0, 0, 7, :10].double().numpy(), (3, 10)))
+    np.testing.assert_array_equal(ours[1, :, 0], np.broadcast_to(kv[1, 0, 19, :10].double().numpy(), (3, 10)))
+
+
+def test_dsa_invalid_duplicate_and_order_of_indices():
+    """Entries outside [0, len) select nothing, a repeated position counts
+    once (the mask is a scatter), the list order does not matter, and an
+    empty selection gives a zero row."""
+    q = _rand((2, 4, 1, 16), 138)
+    kv = _rand((2, 1, 24, 16), 139)
+    lens = [24, 10]
+    base = np.array([[3, 9, 20, 1], [0, 4, 9, 2]])
+    noisy = np.array([[20, -1, 3, 9, 3, 24, 1, 1], [9, 10, 2, 4, -7, 0, 0, 4]])
+    a = O.decode_topk(q, kv, lens, base, 0.4, 16)
+    b = O.decode_topk(q, kv, lens, noisy, 0.4, 16)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+    empty = O.decode_topk(q, kv, lens, np.array([[-1, 30], [10, 11]]), 0.4, 16)
+    assert np.all(empty == 0.0)
