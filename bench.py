@@ -67,6 +67,12 @@ def decode_bytes(w, lens) -> float:
     return float(sum(lens)) * w.Hkv * per_key * 2
 
 
+def topk_bytes(w, sel_rows) -> float:
+    """Latent rows a top-k decode must gather: the selected positions of each
+    sequence, 576 bf16 values each (the value is inside the key)."""
+    return float(sum(sel_rows)) * w.Dk * 2
+
+
 def decode_flops(w, lens) -> float:
     return 2.0 * (w.Dk + w.Dv) * float(sum(lens)) * w.Hq
 
@@ -332,6 +338,32 @@ def extra_workloads(torch, gqa, W, dev):
                    "frac_hbm_peak": round(b / sec / 1e9 / PEAK_HBM_GBPS, 4),
                    "TFLOP/s": round(f / sec / 1e12, 1), "splits": S}
     del q, kc, out, ws
+
+    w = W.MLA_TOPK
+    q, kc, _, lens = W.decode_inputs(w, nan_tail=False)
+    q, kc, lens_d = q.to(dev), kc.to(dev), lens.to(dev)
+    # eight selections in turn (302 MB of rows in all): one selection (38 MB)
+    # would be served from the Infinity Cache after the first call
+    sels = [W.topk_indices(dataclasses.replace(w, seed=w.seed + 10 * i), lens).to(dev) for i in range(8)]
+    out = torch.empty((w.B, w.Hq, 1, w.Dv), dtype=torch.bfloat16, device=dev)
+    S = gqa.decode_topk_splits(w.B, w.Hq, w.extra["topk"], w.Dk, w.Dv, gqa.GQA_BF16)
+    ws = torch.empty(gqa.decode_workspace_size(w.B, w.Hq, w.Dv, S), dtype=torch.uint8, device=dev)
+    turn = [0]
+
+    def topk():
+        idx = sels[turn[0] % len(sels)]
+        turn[0] += 1
+        gqa.decode_topk(q, kc, lens_d, idx, scale=w.scale, num_splits=S, out=out, workspace=ws)
+
+    sec = _time(torch, topk, reps=16, warm=8)
+    sel_rows = [min(w.extra["topk"], n) for n in lens.tolist()]
+    b = topk_bytes(w, sel_rows)
+    f = decode_flops(w, sel_rows)
+    res[w.name] = {"us": round(sec * 1e6, 1), "GB/s": round(b / sec / 1e9, 1),
+                   "frac_hbm_peak": round(b / sec / 1e9 / PEAK_HBM_GBPS, 4),
+                   "TFLOP/s": round(f / sec / 1e12, 2), "splits": S, "topk": w.extra["topk"],
+                   "kv_bytes_per_launch": b}
+    del q, kc, out, ws, sels
 
     w = W.TINY_F32
     q, k, v = (t.to(dev) for t in W.fwd_inputs(w))

@@ -8,6 +8,7 @@ stream.  There is no fallback: if the library is missing, every call raises.
     attention_varlen(q, k, v, cu_q, cu_k, scale=None, causal=True, window=0)
                                                       packed variable-length forward, sliding window
     decode(q, k_cache, v_cache, seq_lens, scale=None) split-KV single-token decode
+    decode_topk(q, kv_cache, seq_lens, indices)       top-k sparse (DSA) decode, absorbed MLA
 
 Shapes follow the C header include/gqa_attn.h: q [B,Hq,Tq,Dk], k [B,Hkv,Tk,Dk],
 v [B,Hkv,Tk,Dv]; decode caches [B,Hkv,Tmax,D] with any element strides whose
@@ -21,7 +22,7 @@ import os
 
 __all__ = [
     "LIB_PATH", "GQA_BF16", "GQA_F32", "GQAError", "lib", "attention", "attention_varlen", "decode",
-    "decode_splits", "decode_workspace_size", "strerror",
+    "decode_splits", "decode_workspace_size", "decode_topk", "decode_topk_splits", "strerror",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_attn.so")
@@ -29,7 +30,8 @@ GQA_BF16, GQA_F32 = 0, 1
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP = 0, -1, -2, -3, -4
 
 EXPORTS = ("gqa_attn_fwd", "gqa_attn_fwd_varlen", "gqa_attn_decode", "gqa_attn_decode_splits",
-           "gqa_attn_decode_workspace_size", "gqa_attn_strerror")
+           "gqa_attn_decode_workspace_size", "gqa_attn_decode_topk", "gqa_attn_decode_topk_splits",
+           "gqa_attn_strerror")
 
 _lib = None
 
@@ -62,6 +64,10 @@ def lib() -> ctypes.CDLL:
         L.gqa_attn_decode.restype = I
         L.gqa_attn_decode.argtypes = [P, P, P, P, P, I, I, I, I, I, I, LL, LL, LL, LL, LL, LL, F, I, P, SZ,
                                       I, P]
+        L.gqa_attn_decode_topk_splits.restype = I
+        L.gqa_attn_decode_topk_splits.argtypes = [I, I, I, I, I, I]
+        L.gqa_attn_decode_topk.restype = I
+        L.gqa_attn_decode_topk.argtypes = [P, P, P, P, P, I, I, I, I, I, I, LL, LL, F, I, P, SZ, I, P]
         L.gqa_attn_strerror.restype = ctypes.c_char_p
         L.gqa_attn_strerror.argtypes = [I]
         _lib = L
@@ -243,4 +249,56 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float | None = None, num_splits
                                workspace.numel() * workspace.element_size(), code, _stream())
     if rc != GQA_OK:
         raise GQAError(rc, "gqa_attn_decode")
+    return out
+
+
+def decode_topk_splits(B: int, Hq: int, topk: int, Dk: int, Dv: int, dtype_code: int) -> int:
+    s = lib().gqa_attn_decode_topk_splits(B, Hq, topk, Dk, Dv, dtype_code)
+    if s < 0:
+        raise GQAError(s, "gqa_attn_decode_topk_splits")
+    return s
+
+
+def decode_topk(q, kv_cache, seq_lens, indices, Dv: int = 512, scale: float | None = None,
+                num_splits: int = 0, out=None, workspace=None):
+    """Top-k sparse decode on the absorbed-MLA cache: q [B,Hq,1,Dk] attends
+    only to the cache positions listed in indices [B, topk] (int32; entries
+    outside [0, seq_lens[b]) select nothing).  kv_cache [B,1,Tmax,Dk] (or
+    [B,Tmax,Dk]); the value is its first Dv columns.  Returns [B,Hq,1,Dv]."""
+    import torch
+    _check_cuda(q, kv_cache, seq_lens, indices)
+    if q.dim() != 4 or q.shape[2] != 1 or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, Hq, 1, Dk] tensor")
+    kv = kv_cache[:, 0] if kv_cache.dim() == 4 else kv_cache
+    if kv.dim() != 3 or (kv_cache.dim() == 4 and kv_cache.shape[1] != 1) or kv.stride(2) != 1:
+        raise ValueError("kv_cache must be [B, 1, Tmax, Dk] or [B, Tmax, Dk] with a unit-stride last dim")
+    if q.dtype != kv.dtype:
+        raise ValueError("q and the cache must share a dtype")
+    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 tensor [B]")
+    if indices.dtype != torch.int32 or indices.dim() != 2 or not indices.is_contiguous():
+        raise ValueError("indices must be a contiguous int32 tensor [B, topk]")
+    B, Hq, _, Dk = q.shape
+    if kv.shape[0] != B or kv.shape[2] != Dk or seq_lens.shape[0] != B or indices.shape[0] != B:
+        raise ValueError("inconsistent q / cache / seq_lens / indices shapes")
+    Tmax, topk = kv.shape[1], indices.shape[1]
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dk)
+    S = num_splits if num_splits else decode_topk_splits(B, Hq, topk, Dk, Dv, code)
+    need = decode_workspace_size(B, Hq, Dv, S)
+    if need == 0:
+        raise GQAError(GQA_ERR_INVALID_ARG, "gqa_attn_decode_workspace_size")
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, 1, Dv), dtype=q.dtype, device=q.device)
+    elif out.shape != (B, Hq, 1, Dv) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B,Hq,1,Dv] tensor of q's dtype")
+    rc = lib().gqa_attn_decode_topk(q.data_ptr(), kv.data_ptr(), out.data_ptr(), seq_lens.data_ptr(),
+                                    indices.data_ptr(), B, Hq, Tmax, topk, Dk, Dv, kv.stride(0), kv.stride(1),
+                                    float(scale), int(S), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), code, _stream())
+    if rc != GQA_OK:
+        raise GQAError(rc, "gqa_attn_decode_topk")
     return out

@@ -258,6 +258,100 @@ GQA_API int gqa_attn_decode_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int
     return default_splits(B, Hq, Hkv, Tmax, Dk, dtype);
 }
 
+// Top-k sparse decode: splits when the caller leaves the choice to the
+// library.  A workgroup covers 128 heads of one sequence and one slice of the
+// index list; aim at one workgroup per CU (256) with slices of at least 64
+// entries, and never a slice longer than the kernel can stage.
+static int topk_default_splits(int B, int Hq, int topk)
+{
+    const long long groups = (long long)B * ((Hq + 127) / 128);
+    long long s = (256 + groups - 1) / groups;
+    const long long cap = (topk + 63) / 64;
+    if (s > cap) s = cap;
+    const long long need = (topk + gqa::mla_topk_max_chunk() - 1) / gqa::mla_topk_max_chunk();
+    if (s < need) s = need;
+    if (s < 1) s = 1;
+    return (int)s;
+}
+
+static int topk_shape_check(int B, int Hq, int topk, int Dk, int Dv, int dtype)
+{
+    int rc = check_common(B, Hq, 1, Dk, Dv, 1.f, dtype);
+    if (rc != GQA_OK) return rc;
+    if (topk <= 0) return GQA_ERR_INVALID_ARG;
+    if (dtype != GQA_BF16 || Dk != 576 || Dv != 512) return GQA_ERR_UNSUPPORTED;
+    if ((long long)topk > (long long)kMaxSplits * gqa::mla_topk_max_chunk()) return GQA_ERR_UNSUPPORTED;
+    return GQA_OK;
+}
+
+GQA_API int gqa_attn_decode_topk_splits(int B, int Hq, int topk, int Dk, int Dv, int dtype)
+{
+    int rc = topk_shape_check(B, Hq, topk, Dk, Dv, dtype);
+    if (rc != GQA_OK) return rc;
+    return topk_default_splits(B, Hq, topk);
+}
+
+GQA_API int gqa_attn_decode_topk(const void *q, const void *kv, void *out, const int *seq_lens,
+                                 const int *indices, int B, int Hq, int Tmax, int topk, int Dk, int Dv,
+                                 long long kv_sb, long long kv_st, float scale, int num_splits,
+                                 void *workspace, size_t workspace_bytes, int dtype, void *stream)
+{
+    if (!q || !kv || !out || !seq_lens || !indices) return GQA_ERR_INVALID_ARG;
+    int rc = check_common(B, Hq, 1, Dk, Dv, scale, dtype);
+    if (rc != GQA_OK) return rc;
+    if (Tmax <= 0 || topk <= 0) return GQA_ERR_INVALID_ARG;
+    if (kv_sb <= 0 || kv_st < Dk || kv_sb % 8 || kv_st % 8) return GQA_ERR_INVALID_ARG;
+    if (num_splits < 0 || num_splits > kMaxSplits) return GQA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 8) || !aligned(seq_lens, 4) ||
+        !aligned(indices, 4))
+        return GQA_ERR_INVALID_ARG;
+    rc = topk_shape_check(B, Hq, topk, Dk, Dv, dtype);
+    if (rc != GQA_OK) return rc;
+
+    const int S = num_splits ? num_splits : topk_default_splits(B, Hq, topk);
+    int chunk = (topk + S - 1) / S;
+    chunk = (chunk + 31) / 32 * 32;
+    if (chunk > gqa::mla_topk_max_chunk()) return GQA_ERR_UNSUPPORTED;  // too few splits for topk
+    const size_t need = ws_bytes(B, Hq, Dv, S);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return GQA_ERR_WORKSPACE;
+    if ((long long)S * B > 0x7fffffffLL || (Hq + 127) / 128 > 65535) return GQA_ERR_UNSUPPORTED;
+
+    gqa::DecodeArgs a = {};
+    a.q = q;
+    a.k = kv;
+    a.v = kv;
+    a.lens = seq_lens;
+    a.part_o = (float *)workspace;
+    a.part_lse = (float *)workspace + (size_t)B * Hq * S * Dv;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = 1;
+    a.Tmax = Tmax;
+    a.G = Hq;
+    a.k_sb = a.v_sb = kv_sb;
+    a.k_sh = a.v_sh = kv_sb;  // one KV head
+    a.k_st = a.v_st = kv_st;
+    a.S = S;
+    a.chunk = chunk;
+    a.n_hblk = (Hq + 127) / 128;
+    a.c = folded_scale(scale);
+    a.idx = indices;
+    a.topk = topk;
+    hipStream_t st = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (gqa::launch_mla_decode_topk(a, st) != 0) return GQA_ERR_UNSUPPORTED;
+    gqa::CombineArgs c;
+    c.part_o = a.part_o;
+    c.part_lse = a.part_lse;
+    c.out = out;
+    c.B = B;
+    c.Hq = Hq;
+    c.S = S;
+    c.Dv = Dv;
+    c.out_bf16 = 1;
+    return launch_status(gqa::launch_combine(c, st));
+}
+
 GQA_API size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_splits)
 {
     if (B <= 0 || Hq <= 0 || Dv <= 0 || num_splits <= 0 || num_splits > kMaxSplits) return 0;
@@ -303,7 +397,7 @@ GQA_API int gqa_attn_decode(const void *q, const void *k, const void *v, void *o
     int chunk = (Tmax + S - 1) / S;
     chunk = (chunk + tile - 1) / tile * tile;
 
-    gqa::DecodeArgs a;
+    gqa::DecodeArgs a = {};
     a.q = q;
     a.k = k;
     a.v = v;

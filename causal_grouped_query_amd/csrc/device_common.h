@@ -175,6 +175,15 @@ __device__ __forceinline__ void g2lds16(const void *gptr, void *lds_wave_base)
                  : "memory");
 }
 
+// 4 bytes per lane (global_load_lds_dword): lane l's word lands at
+// lds_wave_base + 4*l.
+__device__ __forceinline__ void g2lds4(const void *gptr, void *lds_wave_base)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr),
+                 "s"(lds_u32(lds_wave_base))
+                 : "memory");
+}
+
 // Same copy from a workgroup-uniform base plus a per-lane unsigned byte
 // offset (scalar-base form: no per-lane 64-bit address arithmetic).
 __device__ __forceinline__ void g2lds16(const void *uniform_base, unsigned byte_off, void *lds_wave_base)

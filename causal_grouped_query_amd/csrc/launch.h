@@ -56,11 +56,19 @@ struct DecodeArgs {
     int n_hblk;          // head blocks per KV head
     float c;             // scale * log2(e)
     int n_wg;            // > 0: balanced (flat) schedule with this many workgroups
+    // top-k sparse decode (absorbed MLA): idx [B, topk] int32 cache positions;
+    // the key axis of the split is the index list, entries outside
+    // [0, lens[b]) select nothing
+    const int *idx;
+    int topk;
 };
 
 int launch_decode_bf16(const DecodeArgs &a, int Dk, int Dv, hipStream_t stream);
 // Absorbed-MLA shape (Dk 576, Dv 512, V = latent prefix of K), 128 heads per block.
 int launch_mla_decode(const DecodeArgs &a, hipStream_t stream);
+// The same over the positions listed in a.idx; chunk <= mla_topk_max_chunk().
+int launch_mla_decode_topk(const DecodeArgs &a, hipStream_t stream);
+int mla_topk_max_chunk();
 int decode_bf16_key_tile();
 // Flat (persistent, balanced) decode for Dk = Dv <= 128: workgroups to launch.
 int decode_bf16_flat_workgroups(int Dk);

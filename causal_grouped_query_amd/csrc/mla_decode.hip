@@ -21,6 +21,16 @@
 // No scores are exchanged between waves, so the tile loop has one barrier.
 // Partial outputs and log-sum-exp values go to the workspace exactly as for
 // the other decode kernels; combine.hip merges them.
+//
+// Top-k sparse flavour (SPARSE = true; DeepSeek Sparse Attention on the
+// absorbed MLA, "Attention Architecture Evolution", DSA section): the key
+// axis a split walks is the list of selected cache positions instead of the
+// positions themselves.  The workgroup copies its slice of the list HBM ->
+// LDS first (the same asynchronous copy as the key tiles), then each row of
+// a key tile is copied from the position its entry names.  An entry outside
+// [0, len) (or past the slice) fetches a clamped, valid row and is masked to
+// -inf, so it weighs nothing and never brings in memory past len.
+// Everything after the copy is the dense kernel.
 #include "device_common.h"
 #include "launch.h"
 
@@ -41,16 +51,19 @@ constexpr int kStages = 3;
 constexpr int kCPR = kDK / 8;   // 72 16-byte chunks per key row
 constexpr int kKS = kDK / 32;   // 18 contraction steps of 32 dims
 constexpr int kDB = kDV / 16;   // 32 output blocks of 16 dims
+constexpr int kMaxChunk = 4096;  // index-list entries one sparse workgroup stages
 static_assert(kTK * kCPR % 64 == 0, "tile is whole wave copies");
 
 struct MlaSmem {
     uint16_t k[kStages][kTK * kDK];
 };
 
+template <bool SPARSE>
 __global__ __launch_bounds__(kNT, 1) void mla_decode_kernel(DecodeArgs p)
 {
     constexpr int NCOPY = kTK * kCPR / 64;  // 36 wave-copies per tile, spread over 8 waves
     __shared__ __attribute__((aligned(1024))) MlaSmem sm;
+    __shared__ __attribute__((aligned(16))) int sidx[SPARSE ? kMaxChunk : 4];  // staged index slice
 
     // chunk-major order, as in the other decode kernel
     const int nbk = p.B * p.Hkv;
@@ -69,10 +82,23 @@ __global__ __launch_bounds__(kNT, 1) void mla_decode_kernel(DecodeArgs p)
     int len = p.lens[b];
     len = len < 0 ? 0 : (len > p.Tmax ? p.Tmax : len);
     const int kbeg = split * p.chunk;
-    const int kend = min(len, kbeg + p.chunk);
-    const int ntiles = kend > kbeg ? (kend - kbeg + kTK - 1) / kTK : 0;
+    // dense: cache positions [kbeg, kend); sparse: index-list entries
+    const int kend = min(SPARSE ? p.topk : len, kbeg + p.chunk);
+    int ntiles = kend > kbeg ? (kend - kbeg + kTK - 1) / kTK : 0;
 
     const uint16_t *kb = (const uint16_t *)p.k + (size_t)b * p.k_sb + (size_t)kvh * p.k_sh;
+
+    // sparse: copy entries [kbeg, kbeg + 32 ntiles) of the list to LDS
+    // (addresses clamped into the list; what lies past kend is never used
+    // unmasked).  A sequence of length 0 has nothing to read.
+    if constexpr (SPARSE) {
+        if (len == 0) ntiles = 0;
+        const int *il = p.idx + (size_t)b * p.topk;
+        for (int e0 = w * 64; e0 < ntiles * kTK; e0 += kNT)
+            g2lds4(il + min(kbeg + e0 + lane, p.topk - 1), &sidx[e0]);
+        wait_vmem();
+        lds_barrier();  // the slice is visible to every wave
+    }
 
     // wave copy j covers LDS chunks [64 j, 64 j + 64); waves take j = w, w + 8, ...
     // (36 copies: waves 0-3 do 5, waves 4-7 do 4; the count per wave is fixed)
@@ -82,13 +108,19 @@ __global__ __launch_bounds__(kNT, 1) void mla_decode_kernel(DecodeArgs p)
         for (int j = w; j < NCOPY; j += kNW) {
             int row, chunk;
             Tile::slot_source(j * 64 + lane, row, chunk);
-            g2lds16(kb + (size_t)min(k0 + row, kend - 1) * p.k_st + chunk * 8, &sm.k[slot][j * 64 * 8]);
+            int pos;
+            if (SPARSE) {
+                pos = min(max(sidx[k0 - kbeg + row], 0), len - 1);  // in range for any entry
+            } else {
+                pos = min(k0 + row, kend - 1);
+            }
+            g2lds16(kb + (size_t)pos * p.k_st + chunk * 8, &sm.k[slot][j * 64 * 8]);
         }
     };
 
     // Q^T (B operand): head r16 of this wave, dims 32 ks + 8 g .. + 7
     u32x4 qreg[kKS];
-    {
+    auto load_q = [&]() {
         const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)b * p.Hq + head) * kDK + 8 * g;
 #pragma unroll
         for (int ks = 0; ks < kKS; ++ks) {
@@ -97,7 +129,10 @@ __global__ __launch_bounds__(kNT, 1) void mla_decode_kernel(DecodeArgs p)
         }
 #pragma unroll
         for (int ks = 0; ks < kKS; ++ks) hold_reg(qreg[ks]);
-    }
+    };
+    // dense: the query first; sparse: after the first tiles' copies, so the
+    // query latency overlaps theirs (the list copy already took one latency)
+    if constexpr (!SPARSE) load_q();
 
     f32x4 o[kDB];
 #pragma unroll
@@ -122,6 +157,7 @@ __global__ __launch_bounds__(kNT, 1) void mla_decode_kernel(DecodeArgs p)
 #pragma unroll
     for (int s = 0; s < kStages - 1; ++s)
         if (s < ntiles) issue_tile(kbeg + s * kTK, s);
+    if constexpr (SPARSE) load_q();
 
     const float c = p.c;
     for (int it = 0; it < ntiles; ++it) {
@@ -156,7 +192,18 @@ __global__ __launch_bounds__(kNT, 1) void mla_decode_kernel(DecodeArgs p)
         __builtin_amdgcn_sched_group_barrier(0x008, GQA_MLA_PF, 0);
 #endif
         // element i of s0 / s1: key 4 g + i / 16 + 4 g + i, head r16
-        if (k0 + kTK > kend) {
+        if (SPARSE) {
+            // entry k0 + j selects a key iff it lies in the slice and names a
+            // position in [0, len)
+            const int4 e0 = *(const int4 *)&sidx[k0 - kbeg + 4 * g];
+            const int4 e1 = *(const int4 *)&sidx[k0 - kbeg + 16 + 4 * g];
+            const int a0[4] = {e0.x, e0.y, e0.z, e0.w}, a1[4] = {e1.x, e1.y, e1.z, e1.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (k0 + 4 * g + i >= kend || (unsigned)a0[i] >= (unsigned)len) s0[i] = -INFINITY;
+                if (k0 + 16 + 4 * g + i >= kend || (unsigned)a1[i] >= (unsigned)len) s1[i] = -INFINITY;
+            }
+        } else if (k0 + kTK > kend) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if (k0 + 4 * g + i >= kend) s0[i] = -INFINITY;
@@ -229,7 +276,17 @@ __global__ __launch_bounds__(kNT, 1) void mla_decode_kernel(DecodeArgs p)
 int launch_mla_decode(const DecodeArgs &a, hipStream_t stream)
 {
     dim3 grid(a.S * a.B * a.Hkv, a.n_hblk), block(kNT);
-    hipLaunchKernelGGL(mla_decode_kernel, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(mla_decode_kernel<false>, grid, block, 0, stream, a);
+    return 0;
+}
+
+int mla_topk_max_chunk() { return kMaxChunk; }
+
+int launch_mla_decode_topk(const DecodeArgs &a, hipStream_t stream)
+{
+    if (!a.idx || a.topk <= 0 || a.chunk <= 0 || a.chunk % kTK || a.chunk > kMaxChunk) return -1;
+    dim3 grid(a.S * a.B * a.Hkv, a.n_hblk), block(kNT);
+    hipLaunchKernelGGL(mla_decode_kernel<true>, grid, block, 0, stream, a);
     return 0;
 }
 

@@ -39,6 +39,7 @@
  *    gqa_attn_fwd_varlen: (64, 64) or (128, 128), bf16
  *    gqa_attn_decode:  (64, 64) or (128, 128), bf16 or fp32;
  *                      (576, 512) bf16 (the absorbed-MLA shape)
+ *    gqa_attn_decode_topk: (576, 512) bf16
  */
 #ifndef GQA_ATTN_H
 #define GQA_ATTN_H
@@ -181,6 +182,49 @@ int gqa_attn_decode(const void *q, const void *k, const void *v, void *out, cons
                     long long k_st, long long v_sb, long long v_sh, long long v_st, float scale,
                     int num_splits, void *workspace, size_t workspace_bytes, int dtype,
                     void *stream);
+
+/*
+ * Split count gqa_attn_decode_topk uses when called with num_splits = 0
+ * (shape only, host-only): >= 1, or a negative GQA_ERR_* code.
+ */
+int gqa_attn_decode_topk_splits(int B, int Hq, int topk, int Dk, int Dv, int dtype);
+
+/*
+ * Top-k sparse single-token decode on the absorbed-MLA cache: DeepSeek Sparse
+ * Attention ("Attention Architecture Evolution", DSA section).  An indexer
+ * (not part of this library) selects for each sequence's query a list of
+ * cached positions; the main attention keeps only those (the page's index
+ * mask: -inf everywhere except 0 at the selected positions, added to the
+ * absorbed scores q_C' c_KV^T + q_R k_R^T before the softmax), and the output
+ * aggregates the selected latent rows.
+ *
+ *   q        [B, Hq, 1, Dk]  contiguous (one KV head shared by all Hq heads)
+ *   kv       latent cache, element (b, t, d) at kv[b*kv_sb + t*kv_st + d]
+ *            (d unit-stride, t < Tmax); the value is its first Dv columns.
+ *            Strides multiples of 8 elements, kv_st >= Dk, kv 16-byte aligned.
+ *   out      [B, Hq, 1, Dv]  contiguous, written in full
+ *   seq_lens device int32[B]: valid cache length of sequence b (clamped to
+ *            [0, Tmax] on the device).
+ *   indices  device int32[B, topk], row-major: the selected positions of
+ *            sequence b.  Entries outside [0, seq_lens[b]) select nothing
+ *            (use -1 to pad a shorter selection); such entries are never
+ *            used as addresses.  The listed positions must be distinct (as a
+ *            top-k produces them): a repeated position is counted once per
+ *            occurrence, where the page's mask counts it once.  The order of
+ *            the list does not matter.  A sequence with no valid entry gets
+ *            a zero output row.
+ *   num_splits  slices of the index list, 1 .. 1024, or 0 for
+ *            gqa_attn_decode_topk_splits(); each slice may hold at most 4096
+ *            entries (else GQA_ERR_UNSUPPORTED).
+ *   workspace   device buffer of gqa_attn_decode_workspace_size(B, Hq, Dv,
+ *            splits) bytes (same layout and rules as for gqa_attn_decode).
+ * Supported: bf16, (Dk, Dv) = (576, 512); anything else GQA_ERR_UNSUPPORTED.
+ * Same error rules as gqa_attn_decode (host checks, nothing enqueued on error).
+ */
+int gqa_attn_decode_topk(const void *q, const void *kv, void *out, const int *seq_lens,
+                         const int *indices, int B, int Hq, int Tmax, int topk, int Dk, int Dv,
+                         long long kv_sb, long long kv_st, float scale, int num_splits,
+                         void *workspace, size_t workspace_bytes, int dtype, void *stream);
 
 /* Static, thread-safe description of a GQA_* return code. */
 const char *gqa_attn_strerror(int code);

@@ -143,3 +143,35 @@ def test_python_binding_rejects_cpu_tensors():
     q = torch.zeros(1, 2, 4, 64)
     with pytest.raises(ValueError):
         gqa.attention(q, q[:, :1], q[:, :1])
+
+
+def _topk(**kw):
+    a = dict(q=FAKE, kv=FAKE, out=FAKE, lens=FAKE, idx=FAKE, B=2, Hq=128, Tmax=4096, topk=2048, Dk=576, Dv=512,
+             ksb=4096 * 576, kst=576, scale=0.07, S=0, ws=FAKE, wsb=1 << 30, dtype=BF16)
+    a.update(kw)
+    return gqa.lib().gqa_attn_decode_topk(a["q"], a["kv"], a["out"], a["lens"], a["idx"], a["B"], a["Hq"],
+                                          a["Tmax"], a["topk"], a["Dk"], a["Dv"], a["ksb"], a["kst"], a["scale"],
+                                          a["S"], a["ws"], a["wsb"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), INVALID), (dict(kv=0), INVALID), (dict(idx=0), INVALID), (dict(lens=0), INVALID),
+    (dict(out=0), INVALID), (dict(B=0), INVALID), (dict(topk=0), INVALID), (dict(Tmax=0), INVALID),
+    (dict(kst=512), INVALID), (dict(kst=580), INVALID), (dict(ksb=0), INVALID), (dict(S=-1), INVALID),
+    (dict(S=1025), INVALID), (dict(idx=FAKE + 2), INVALID), (dict(kv=FAKE + 8), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(dtype=F32), UNSUP), (dict(Dk=128, Dv=128), UNSUP), (dict(topk=10000, S=2), UNSUP),
+    (dict(ws=0), WS), (dict(wsb=1024), WS),
+])
+def test_decode_topk_rejects_on_host(kw, code):
+    assert _topk(**kw) == code
+
+
+def test_decode_topk_default_splits():
+    # one 128-head workgroup per (sequence, slice): about 256 workgroups,
+    # slices of >= 64 entries, never more than 4096 entries per slice
+    assert gqa.decode_topk_splits(16, 128, 2048, 576, 512, BF16) == 16
+    assert gqa.decode_topk_splits(1, 128, 2048, 576, 512, BF16) == 32
+    assert gqa.decode_topk_splits(512, 128, 2048, 576, 512, BF16) == 1
+    assert gqa.decode_topk_splits(512, 128, 100000, 576, 512, BF16) == 25
+    assert gqa.lib().gqa_attn_decode_topk_splits(2, 128, 64, 128, 128, BF16) == UNSUP

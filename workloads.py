@@ -17,7 +17,12 @@ Recipe (the same for every workload and size):
     512 columns of the 576-wide key (latent 512 + rope 64), taken as a view;
   * packed variable-length workloads draw all tokens of all sequences at once
     in the [total, H, D] layout; cu_seqlens are the running sums of the
-    listed lengths.
+    listed lengths;
+  * top-k sparse decode draws the selected positions from a third CPU
+    generator seeded with seed + 2000: for each sequence the first
+    min(topk, len_b) entries of ``randperm(len_b)`` (distinct positions in
+    random order, as a top-k over indexer scores returns them), padded
+    with -1 when len_b < topk.
 """
 from __future__ import annotations
 
@@ -32,7 +37,7 @@ _DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "fwd", "decode", "mla_decode", "fwd+decode", "fwd_varlen"
+    kind: str  # "fwd", "decode", "mla_decode", "mla_topk_decode", "fwd+decode", "fwd_varlen"
     B: int
     Hq: int
     Hkv: int
@@ -88,6 +93,14 @@ def varlen_inputs(w: Workload):
     return q, k, v, cu
 
 
+# DeepSeek Sparse Attention decode on the absorbed MLA cache: each query keeps
+# the 2048 cached positions an indexer selected (the DeepSeek-V3.2 setting);
+# cache lengths uniform on [4096, 32768].
+MLA_TOPK = Workload("mla_dsa_topk2048_decode_b16_hq128_tk32768_dk576_dv512", "mla_topk_decode", 16, 128, 1, 1,
+                    32768, 576, 512, "bf16", 6, 1.0 / math.sqrt(192), len_lo=4096, len_hi=32768,
+                    extra={"topk": 2048})
+
+
 def _randn(gen: torch.Generator, shape, dtype: str) -> torch.Tensor:
     return torch.randn(*shape, generator=gen, dtype=torch.float32).to(_DT[dtype])
 
@@ -119,7 +132,7 @@ def decode_inputs(w: Workload, nan_tail: bool = True):
     g = torch.Generator("cpu").manual_seed(w.seed)
     q = _randn(g, (w.B, w.Hq, 1, w.Dk), w.dtype)
     k = _randn(g, (w.B, w.Hkv, w.Tk, w.Dk), w.dtype)
-    if w.kind == "mla_decode":
+    if w.kind in ("mla_decode", "mla_topk_decode"):
         v = None
     else:
         v = _randn(g, (w.B, w.Hkv, w.Tk, w.Dv), w.dtype)
@@ -131,3 +144,14 @@ def decode_inputs(w: Workload, nan_tail: bool = True):
     if v is None:
         v = k[..., : w.Dv]
     return q, k, v, lens
+
+
+def topk_indices(w: Workload, lens: torch.Tensor) -> torch.Tensor:
+    """Selected positions int32 [B, topk] (CPU) for a top-k decode workload."""
+    topk = w.extra["topk"]
+    g = torch.Generator("cpu").manual_seed(w.seed + 2000)
+    idx = torch.full((w.B, topk), -1, dtype=torch.int32)
+    for b, n in enumerate(lens.tolist()):
+        sel = torch.randperm(n, generator=g)[:topk]
+        idx[b, : sel.numel()] = sel.to(torch.int32)
+    return idx
