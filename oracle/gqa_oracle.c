@@ -42,6 +42,18 @@
  * softmax partials over disjoint key ranges, used by the tests to pin the
  * split-KV decode reading (the merge is a rewrite of step 5 over a partition
  * of J, exact in real arithmetic).
+ *
+ * Quantised caches: K and V may be stored as FP8 E4M3 codes with one fp32
+ * scale per (b, h, t) row (oracle_attention_e4m3kv).  The value an element
+ * stands for is decode(code) * scale, the dequantisation of a block-scaled
+ * FP8 cache ("Attention Architecture Evolution", DSA section: the indexer
+ * keeps FP8 keys with per-block scales; "Attention variants" lists the
+ * scale granularity of quantised K/V as a deployment concern).  decode()
+ * follows the OCP 8-bit floating point definition of E4M3: sign bit, four
+ * exponent bits with bias 7, three mantissa bits; exponent 0 holds the
+ * subnormals m * 2^-9; exponent 15 with mantissa 7 is NaN; there are no
+ * infinities (largest finite value 448).  The product is formed in fp64,
+ * where it is exact.
  */
 #include <math.h>
 #include <stdint.h>
@@ -51,14 +63,26 @@
 #include <omp.h>
 #endif
 
-enum { ORACLE_BF16 = 0, ORACLE_F32 = 1, ORACLE_F64 = 2 };
+enum { ORACLE_BF16 = 0, ORACLE_F32 = 1, ORACLE_F64 = 2, ORACLE_E4M3 = 3 };
 
 /* A 4-D tensor view: element (b, h, t, d) lives at base[b*s0 + h*s1 + t*s2 + d*s3]. */
 typedef struct {
     const void *base;
     long long s0, s1, s2, s3;
     int dtype;
+    const float *sc;         /* ORACLE_E4M3: one scale per (b, h, t) */
+    long long ss0, ss1, ss2; /* its element strides */
 } view4;
+
+/* Value of an OCP FP8 E4M3 code. */
+static double e4m3_value(uint8_t c)
+{
+    int sign = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7) return NAN;
+    /* normal: (1 + m/8) * 2^(e-7) = (8 + m) * 2^(e-10); subnormal: m * 2^-9 */
+    double mag = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+    return sign ? -mag : mag;
+}
 
 static double widen(const view4 *v, int b, int h, int t, int d)
 {
@@ -73,6 +97,10 @@ static double widen(const view4 *v, int b, int h, int t, int d)
     }
     if (v->dtype == ORACLE_F32)
         return (double)((const float *)v->base)[idx];
+    if (v->dtype == ORACLE_E4M3) {
+        double s = (double)v->sc[(long long)b * v->ss0 + (long long)h * v->ss1 + (long long)t * v->ss2];
+        return e4m3_value(((const uint8_t *)v->base)[idx]) * s;
+    }
     return ((const double *)v->base)[idx];
 }
 
@@ -175,6 +203,8 @@ static view4 make_view(const void *base, const long long *st, int dtype)
     v.s2 = st[2];
     v.s3 = st[3];
     v.dtype = dtype;
+    v.sc = NULL;
+    v.ss0 = v.ss1 = v.ss2 = 0;
     return v;
 }
 
@@ -191,6 +221,9 @@ static view4 make_view(const void *base, const long long *st, int dtype)
  * rows: NULL, or nrows flattened row ids r = ((b*Hq) + a)*Tq + i.
  * Returns 0, or -1 for an inconsistent problem.
  */
+static int run_rows(const problem *P, const long long *rows, long long nrows, double *out,
+                    double *lse, int nthreads);
+
 int oracle_attention(const void *q, const long long *qs, int q_dt, const void *k,
                      const long long *ks, int k_dt, const void *v, const long long *vs,
                      int v_dt, const int *kv_lens, int B, int Hq, int Hkv, int Tq, int Tk,
@@ -213,7 +246,14 @@ int oracle_attention(const void *q, const long long *qs, int q_dt, const void *k
     P.causal = causal;
     P.window = window;
     if (check_problem(&P)) return -1;
+    return run_rows(&P, rows, nrows, out, lse, nthreads);
+}
 
+/* Every row, or the listed rows, of a checked problem. */
+static int run_rows(const problem *P, const long long *rows, long long nrows, double *out,
+                    double *lse, int nthreads)
+{
+    const int B = P->B, Hq = P->Hq, Tq = P->Tq, Tk = P->Tk, Dk = P->Dk, Dv = P->Dv;
     long long total = rows ? nrows : (long long)B * Hq * Tq;
     int bad = 0;
 #ifdef _OPENMP
@@ -239,7 +279,7 @@ int oracle_attention(const void *q, const long long *qs, int q_dt, const void *k
                 int i = (int)(id % Tq);
                 int a = (int)((id / Tq) % Hq);
                 int b = (int)(id / ((long long)Tq * Hq));
-                attend_row(&P, b, a, i, s, out + r * Dv, lse ? lse + r : NULL, NULL);
+                attend_row(P, b, a, i, s, out + r * Dv, lse ? lse + r : NULL, NULL);
             }
             free(s);
         }
@@ -308,6 +348,54 @@ void oracle_lse_merge(const double *o_parts, const double *lse_parts, int S, lon
         }
         lse[r] = L;
     }
+}
+
+/*
+ * oracle_attention over a quantised cache: k and v hold E4M3 codes (one byte
+ * each, element strides ks / vs), k_scale / v_scale one fp32 scale per
+ * (b, h, t) with element strides kss / vss[3].  q is read as for
+ * oracle_attention (q_dt).
+ */
+int oracle_attention_e4m3kv(const void *q, const long long *qs, int q_dt, const void *k,
+                            const long long *ks, const float *k_scale, const long long *kss,
+                            const void *v, const long long *vs, const float *v_scale,
+                            const long long *vss, const int *kv_lens, int B, int Hq, int Hkv,
+                            int Tq, int Tk, int Dk, int Dv, double scale, int causal,
+                            const long long *rows, long long nrows, double *out, double *lse,
+                            int nthreads)
+{
+    problem P;
+    P.q = make_view(q, qs, q_dt);
+    P.k = make_view(k, ks, ORACLE_E4M3);
+    P.v = make_view(v, vs, ORACLE_E4M3);
+    if (!k_scale || !v_scale) return -1;
+    P.k.sc = k_scale;
+    P.k.ss0 = kss[0];
+    P.k.ss1 = kss[1];
+    P.k.ss2 = kss[2];
+    P.v.sc = v_scale;
+    P.v.ss0 = vss[0];
+    P.v.ss1 = vss[1];
+    P.v.ss2 = vss[2];
+    P.kv_lens = kv_lens;
+    P.B = B;
+    P.Hq = Hq;
+    P.Hkv = Hkv;
+    P.Tq = Tq;
+    P.Tk = Tk;
+    P.Dk = Dk;
+    P.Dv = Dv;
+    P.scale = scale;
+    P.causal = causal;
+    P.window = 0;
+    if (check_problem(&P)) return -1;
+    return run_rows(&P, rows, nrows, out, lse, nthreads);
+}
+
+/* The 256 E4M3 code values (for checking the decoder). */
+void oracle_e4m3_table(double *out)
+{
+    for (int c = 0; c < 256; ++c) out[c] = e4m3_value((uint8_t)c);
 }
 
 int oracle_max_threads(void)

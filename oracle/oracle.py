@@ -58,6 +58,13 @@ def _load():
             P, LLP, I, P, LLP, I, P, LLP, I, P,
             I, I, I, I, I, I, I, ctypes.c_double, I, I, I, I, I, P, P,
         ]
+        lib.oracle_attention_e4m3kv.restype = I
+        lib.oracle_attention_e4m3kv.argtypes = [
+            P, LLP, I, P, LLP, P, LLP, P, LLP, P, LLP, P,
+            I, I, I, I, I, I, I, ctypes.c_double, I, P, ctypes.c_longlong, P, P, I,
+        ]
+        lib.oracle_e4m3_table.restype = None
+        lib.oracle_e4m3_table.argtypes = [P]
         lib.oracle_lse_merge.restype = None
         lib.oracle_lse_merge.argtypes = [P, P, I, ctypes.c_longlong, I, P, P]
         lib.oracle_max_threads.restype = I
@@ -149,6 +156,84 @@ def attention(q, k, v, scale: float, causal: bool, kv_lens=None, rows=None, thre
     if rc != 0:
         raise ValueError("oracle rejected the problem (shapes, head grouping or Tq > Tk with causal)")
     return (out, lse) if with_lse else out
+
+
+def e4m3_table() -> np.ndarray:
+    """Values of the 256 FP8 E4M3 codes (NaN for the two NaN codes)."""
+    out = np.empty(256, dtype=np.float64)
+    _load().oracle_e4m3_table(out.ctypes.data)
+    return out
+
+
+def _host_u8_4d(x, name):
+    """A 4-D array of one-byte codes (torch uint8 / float8_e4m3fn or numpy
+    uint8) as (pointer, element strides, keep-alive, shape)."""
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            if x.device.type != "cpu" or x.dim() != 4 or x.element_size() != 1:
+                raise ValueError(f"{name}: a 4-D one-byte host tensor is required")
+            return x.data_ptr(), (ctypes.c_longlong * 4)(*x.stride()), x, tuple(x.shape)
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.asarray(x)
+    if a.ndim != 4 or a.dtype != np.uint8:
+        raise ValueError(f"{name}: a 4-D uint8 array is required")
+    return a.ctypes.data, (ctypes.c_longlong * 4)(*(st // 1 for st in a.strides)), a, a.shape
+
+
+def _host_f32_3d(x, name):
+    try:
+        import torch
+        if isinstance(x, torch.Tensor):
+            if x.device.type != "cpu" or x.dim() != 3 or x.dtype != torch.float32:
+                raise ValueError(f"{name}: a 3-D float32 host tensor is required")
+            return x.data_ptr(), (ctypes.c_longlong * 3)(*x.stride()), x, tuple(x.shape)
+    except ImportError:  # pragma: no cover
+        pass
+    a = np.asarray(x)
+    if a.ndim != 3 or a.dtype != np.float32:
+        raise ValueError(f"{name}: a 3-D float32 array is required")
+    return a.ctypes.data, (ctypes.c_longlong * 3)(*(st // 4 for st in a.strides)), a, a.shape
+
+
+def attention_e4m3kv(q, k_codes, k_scale, v_codes, v_scale, scale: float, causal: bool, kv_lens=None,
+                     rows=None, threads: int = 0):
+    """fp64 attention over an FP8 E4M3 cache with one scale per row.
+
+    k_codes [B,Hkv,Tk,Dk] and v_codes [B,Hkv,Tk,Dv] hold E4M3 codes (uint8
+    or float8_e4m3fn storage); k_scale / v_scale [B,Hkv,Tk] float32.  Element
+    (b,h,t,d) stands for e4m3(code) * scale[b,h,t], formed exactly in fp64;
+    everything else is attention() (q as bf16 / fp32 / fp64).
+    """
+    Q = _Operand(q)
+    kp, ks, kkeep, kshape = _host_u8_4d(k_codes, "k_codes")
+    vp, vs, vkeep, vshape = _host_u8_4d(v_codes, "v_codes")
+    ksp, kss, kskeep, ksshape = _host_f32_3d(k_scale, "k_scale")
+    vsp, vss, vskeep, vsshape = _host_f32_3d(v_scale, "v_scale")
+    B, Hq, Tq, Dk = Q.shape
+    _, Hkv, Tk, Dk2 = kshape
+    Dv = vshape[3]
+    if (kshape[0] != B or vshape[:3] != kshape[:3] or Dk != Dk2 or ksshape != kshape[:3]
+            or vsshape != kshape[:3]):
+        raise ValueError("inconsistent q / code / scale shapes")
+    lens, lens_ptr = _lens_arg(kv_lens, B)
+    if rows is None:
+        out = np.empty((B, Hq, Tq, Dv), dtype=np.float64)
+        rows_ptr, nrows = None, 0
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows_arr.size
+        out = np.empty((nrows, Dv), dtype=np.float64)
+        rows_ptr = rows_arr.ctypes.data
+    rc = _load().oracle_attention_e4m3kv(
+        Q.ptr, Q.strides, Q.code, kp, ks, ksp, kss, vp, vs, vsp, vss, lens_ptr,
+        B, Hq, Hkv, Tq, Tk, Dk, Dv, float(scale), int(bool(causal)), rows_ptr, nrows,
+        out.ctypes.data, None, int(threads),
+    )
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+    return out
 
 
 def probs(q, k, v, scale: float, causal: bool, b: int, a: int, i: int, kv_lens=None, window: int = 0):

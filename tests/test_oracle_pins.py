@@ -636,3 +636,70 @@ def test_dsa_invalid_duplicate_and_order_of_indices():
     np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
     empty = O.decode_topk(q, kv, lens, np.array([[-1, 30], [10, 11]]), 0.4, 16)
     assert np.all(empty == 0.0)
+
+
+# ---------------------------------------------------------------- FP8 E4M3 cache
+# "Attention Architecture Evolution", DSA section: FP8 keys with per-block
+# scales; "Attention variants": scale granularity of quantised K/V.  The
+# value of a cached element is e4m3(code) * scale of its row.
+
+def test_e4m3_decoder_matches_format_and_library():
+    """All 256 codes against torch's independent float8_e4m3fn decoding, plus
+    closed forms of the OCP E4M3 format."""
+    t = O.e4m3_table()
+    lib = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    np.testing.assert_array_equal(t, lib)                      # NaN positions must agree too
+    assert t[0x38] == 1.0 and t[0x7E] == 448.0 and t[0x01] == 2.0 ** -9 and t[0x08] == 2.0 ** -6
+    assert t[0x07] == 7 * 2.0 ** -9 and t[0x00] == 0.0 and np.signbit(t[0x80]) and t[0x80] == 0.0
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF]) and np.isfinite(np.delete(t, [0x7F, 0xFF])).all()
+    pos = t[:0x7F]
+    assert np.all(np.diff(pos) > 0)                             # codes order the values
+    np.testing.assert_array_equal(t[0x80:0xFF], -pos)          # sign bit negates
+
+
+def _fp8_problem(B, Hq, Hkv, T, D, seed):
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn(B, Hq, 1, D, generator=g, dtype=torch.float64).to(torch.bfloat16)
+    def codes():
+        x = (torch.randn(B, Hkv, T, D, generator=g) * 64).clamp(-448, 448)
+        return x.to(torch.float8_e4m3fn).view(torch.uint8)
+    kc, vc = codes(), codes()
+    ks = torch.exp2(-8 + 3 * torch.rand(B, Hkv, T, generator=g))
+    vs = torch.exp2(-8 + 3 * torch.rand(B, Hkv, T, generator=g))
+    return q, kc, ks, vc, vs
+
+
+def _dequant_with_library(codes, sc):
+    return codes.view(torch.float8_e4m3fn).to(torch.float64) * sc.double()[..., None]
+
+
+def test_e4m3kv_attention_is_attention_of_dequantised_cache():
+    """Against attention() on a cache dequantised with torch's decoder, for
+    strided (transposed-storage) codes and scales and ragged lengths."""
+    B, Hq, Hkv, T, D = 2, 4, 2, 37, 16
+    q, kc, ks, vc, vs = _fp8_problem(B, Hq, Hkv, T, D, 140)
+    kc_t = kc.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)   # [B,T,H,D] storage
+    ks_t = ks.permute(0, 2, 1).contiguous().permute(0, 2, 1)
+    lens = [37, 9]
+    ours = O.attention_e4m3kv(q, kc_t, ks_t, vc, vs, 0.3, True, kv_lens=lens)
+    ref = O.attention(q, _dequant_with_library(kc, ks), _dequant_with_library(vc, vs), 0.3, True, kv_lens=lens)
+    np.testing.assert_allclose(ours, ref, rtol=0, atol=1e-13)
+
+
+def test_e4m3kv_scales_act_linearly():
+    """Scaling every key scale by c is scaling the softmax scale by c; scaling
+    every value scale by c scales the output by c."""
+    q, kc, ks, vc, vs = _fp8_problem(1, 4, 1, 25, 16, 141)
+    base = O.attention_e4m3kv(q, kc, ks, vc, vs, 0.2, True)
+    np.testing.assert_allclose(O.attention_e4m3kv(q, kc, ks * 4, vc, vs, 0.05, True), base, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(O.attention_e4m3kv(q, kc, ks, vc, vs * 8, 0.2, True), 8 * base, rtol=0, atol=1e-12)
+    # a row scale enters only its own key: doubling key 3's value scale moves
+    # the output by exactly p_3 * v_3 (probabilities from the dense form)
+    vs2 = vs.clone()
+    vs2[0, 0, 3] *= 2
+    moved = O.attention_e4m3kv(q, kc, ks, vc, vs2, 0.2, True)
+    K = _dequant_with_library(kc, ks)
+    V = _dequant_with_library(vc, vs)
+    for a in range(4):
+        p_row, _ = O.probs(q, K, V, 0.2, True, 0, a, 0)
+        np.testing.assert_allclose(moved[0, a, 0] - base[0, a, 0], p_row[3] * V[0, 0, 3].numpy(), rtol=0, atol=1e-12)
