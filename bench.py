@@ -67,6 +67,12 @@ def decode_bytes(w, lens) -> float:
     return float(sum(lens)) * w.Hkv * per_key * 2
 
 
+def fp8_decode_bytes(w, lens) -> float:
+    """Bytes an FP8-cache decode must read: one byte per cached element of K
+    and V, plus one fp32 scale per K row and per V row."""
+    return float(sum(lens)) * w.Hkv * ((w.Dk + w.Dv) * 1 + 2 * 4)
+
+
 def topk_bytes(w, sel_rows) -> float:
     """Latent rows a top-k decode must gather: the selected positions of each
     sequence, 576 bf16 values each (the value is inside the key)."""
@@ -338,6 +344,20 @@ def extra_workloads(torch, gqa, W, dev):
                    "frac_hbm_peak": round(b / sec / 1e9 / PEAK_HBM_GBPS, 4),
                    "TFLOP/s": round(f / sec / 1e12, 1), "splits": S}
     del q, kc, out, ws
+
+    w = W.GQA_DECODE_FP8
+    q, kc, vc, ks, vs, lens = W.fp8_decode_inputs(w, nan_tail=False)
+    q, kc, vc, ks, vs, lens_d = (t.to(dev) for t in (q, kc, vc, ks, vs, lens))
+    out = torch.empty((w.B, w.Hq, 1, w.Dv), dtype=torch.bfloat16, device=dev)
+    S = gqa.decode_splits(w.B, w.Hq, w.Hkv, w.Tk, w.Dk, w.Dv, gqa.GQA_BF16)
+    ws = torch.empty(gqa.decode_workspace_size(w.B, w.Hq, w.Dv, S), dtype=torch.uint8, device=dev)
+    sec = _time(torch, lambda: gqa.decode_fp8(q, kc, vc, ks, vs, lens_d, scale=w.scale, num_splits=S, out=out,
+                                              workspace=ws))
+    b = fp8_decode_bytes(w, lens.tolist())
+    res[w.name] = {"us": round(sec * 1e6, 1), "GB/s": round(b / sec / 1e9, 1),
+                   "frac_hbm_peak": round(b / sec / 1e9 / PEAK_HBM_GBPS, 4), "splits": S,
+                   "kv_bytes_per_launch": b, "tokens_per_s": round(float(sum(lens.tolist())) / sec, 1)}
+    del q, kc, vc, ks, vs, out, ws
 
     w = W.MLA_TOPK
     q, kc, _, lens = W.decode_inputs(w, nan_tail=False)

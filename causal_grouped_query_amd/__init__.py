@@ -9,6 +9,8 @@ stream.  There is no fallback: if the library is missing, every call raises.
                                                       packed variable-length forward, sliding window
     decode(q, k_cache, v_cache, seq_lens, scale=None) split-KV single-token decode
     decode_topk(q, kv_cache, seq_lens, indices)       top-k sparse (DSA) decode, absorbed MLA
+    decode_fp8(q, k_codes, v_codes, k_scale, v_scale, seq_lens)
+                                                      decode over an FP8 E4M3 cache with row scales
 
 Shapes follow the C header include/gqa_attn.h: q [B,Hq,Tq,Dk], k [B,Hkv,Tk,Dk],
 v [B,Hkv,Tk,Dv]; decode caches [B,Hkv,Tmax,D] with any element strides whose
@@ -22,7 +24,7 @@ import os
 
 __all__ = [
     "LIB_PATH", "GQA_BF16", "GQA_F32", "GQAError", "lib", "attention", "attention_varlen", "decode",
-    "decode_splits", "decode_workspace_size", "decode_topk", "decode_topk_splits", "strerror",
+    "decode_splits", "decode_workspace_size", "decode_topk", "decode_topk_splits", "decode_fp8", "strerror",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_attn.so")
@@ -31,7 +33,7 @@ GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP
 
 EXPORTS = ("gqa_attn_fwd", "gqa_attn_fwd_varlen", "gqa_attn_decode", "gqa_attn_decode_splits",
            "gqa_attn_decode_workspace_size", "gqa_attn_decode_topk", "gqa_attn_decode_topk_splits",
-           "gqa_attn_strerror")
+           "gqa_attn_decode_fp8", "gqa_attn_strerror")
 
 _lib = None
 
@@ -68,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.gqa_attn_decode_topk_splits.argtypes = [I, I, I, I, I, I]
         L.gqa_attn_decode_topk.restype = I
         L.gqa_attn_decode_topk.argtypes = [P, P, P, P, P, I, I, I, I, I, I, LL, LL, F, I, P, SZ, I, P]
+        L.gqa_attn_decode_fp8.restype = I
+        L.gqa_attn_decode_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I] + [LL] * 12 + [F, I, P, SZ, P]
         L.gqa_attn_strerror.restype = ctypes.c_char_p
         L.gqa_attn_strerror.argtypes = [I]
         _lib = L
@@ -301,4 +305,53 @@ def decode_topk(q, kv_cache, seq_lens, indices, Dv: int = 512, scale: float | No
                                     workspace.numel() * workspace.element_size(), code, _stream())
     if rc != GQA_OK:
         raise GQAError(rc, "gqa_attn_decode_topk")
+    return out
+
+
+def decode_fp8(q, k_codes, v_codes, k_scale, v_scale, seq_lens, scale: float | None = None, num_splits: int = 0,
+               out=None, workspace=None):
+    """Single-token decode over an FP8 E4M3 cache: k_codes / v_codes
+    [B,Hkv,Tmax,D] (uint8 or float8_e4m3fn storage, unit-stride last dim),
+    k_scale / v_scale [B,Hkv,Tmax] float32 row scales; element (b,h,t,d)
+    stands for e4m3(code) * scale[b,h,t].  q [B,Hq,1,D] bfloat16.  Returns
+    [B,Hq,1,D] bfloat16."""
+    import torch
+    _check_cuda(q, k_codes, v_codes, k_scale, v_scale, seq_lens)
+    if q.dim() != 4 or q.shape[2] != 1 or not q.is_contiguous() or q.dtype != torch.bfloat16:
+        raise ValueError("q must be a contiguous bfloat16 [B, Hq, 1, D] tensor")
+    for c in (k_codes, v_codes):
+        if c.dim() != 4 or c.element_size() != 1 or c.stride(3) != 1:
+            raise ValueError("code caches must be 4-D one-byte tensors with a unit-stride last dim")
+    for sc in (k_scale, v_scale):
+        if sc.dim() != 3 or sc.dtype != torch.float32:
+            raise ValueError("scales must be float32 [B, Hkv, Tmax]")
+    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1 or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 tensor [B]")
+    B, Hq, _, Dk = q.shape
+    _, Hkv, Tmax, Dk2 = k_codes.shape
+    Dv = v_codes.shape[3]
+    if (k_codes.shape[0] != B or Dk2 != Dk or v_codes.shape[:3] != k_codes.shape[:3]
+            or k_scale.shape != k_codes.shape[:3] or v_scale.shape != k_codes.shape[:3]
+            or seq_lens.shape[0] != B):
+        raise ValueError("inconsistent q / code / scale / seq_lens shapes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dk)
+    S = num_splits if num_splits else decode_splits(B, Hq, Hkv, Tmax, Dk, Dv, GQA_BF16)
+    need = decode_workspace_size(B, Hq, Dv, S)
+    if need == 0:
+        raise GQAError(GQA_ERR_INVALID_ARG, "gqa_attn_decode_workspace_size")
+    if workspace is None:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, Hq, 1, Dv), dtype=q.dtype, device=q.device)
+    elif out.shape != (B, Hq, 1, Dv) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B,Hq,1,Dv] bfloat16 tensor")
+    ks, vs, kss, vss = k_codes.stride(), v_codes.stride(), k_scale.stride(), v_scale.stride()
+    rc = lib().gqa_attn_decode_fp8(q.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(), k_scale.data_ptr(),
+                                   v_scale.data_ptr(), out.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, Tmax, Dk,
+                                   Dv, ks[0], ks[1], ks[2], vs[0], vs[1], vs[2], kss[0], kss[1], kss[2], vss[0],
+                                   vss[1], vss[2], float(scale), int(S), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), _stream())
+    if rc != GQA_OK:
+        raise GQAError(rc, "gqa_attn_decode_fp8")
     return out

@@ -352,6 +352,87 @@ GQA_API int gqa_attn_decode_topk(const void *q, const void *kv, void *out, const
     return launch_status(gqa::launch_combine(c, st));
 }
 
+GQA_API int gqa_attn_decode_fp8(const void *q, const void *k, const void *v, const float *k_scale,
+                                const float *v_scale, void *out, const int *seq_lens, int B, int Hq,
+                                int Hkv, int Tmax, int Dk, int Dv, long long k_sb, long long k_sh,
+                                long long k_st, long long v_sb, long long v_sh, long long v_st,
+                                long long ks_sb, long long ks_sh, long long ks_st, long long vs_sb,
+                                long long vs_sh, long long vs_st, float scale, int num_splits,
+                                void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!q || !k || !v || !k_scale || !v_scale || !out || !seq_lens) return GQA_ERR_INVALID_ARG;
+    int rc = check_common(B, Hq, Hkv, Dk, Dv, scale, GQA_BF16);
+    if (rc != GQA_OK) return rc;
+    if (Tmax <= 0) return GQA_ERR_INVALID_ARG;
+    const long long cs[6] = {k_sb, k_sh, k_st, v_sb, v_sh, v_st};
+    for (long long st : cs)
+        if (st <= 0 || st % 16 != 0) return GQA_ERR_INVALID_ARG;  // 16-byte rows of codes
+    if (k_st < Dk || v_st < Dv) return GQA_ERR_INVALID_ARG;      // rows may not overlap
+    const long long ss[6] = {ks_sb, ks_sh, ks_st, vs_sb, vs_sh, vs_st};
+    for (long long st : ss)
+        if (st <= 0) return GQA_ERR_INVALID_ARG;
+    if (num_splits < 0 || num_splits == 1 || num_splits == 2 || num_splits > kMaxSplits)
+        return GQA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 8) || !aligned(k_scale, 4) ||
+        !aligned(v_scale, 4) || !aligned(seq_lens, 4))
+        return GQA_ERR_INVALID_ARG;
+    if (Dk != Dv || (Dk != 64 && Dk != 128)) return GQA_ERR_UNSUPPORTED;
+    // a 32-row tile is addressed with 32-bit byte offsets
+    if (k_st > (1LL << 25) || v_st > (1LL << 25)) return GQA_ERR_UNSUPPORTED;
+
+    const int S = num_splits ? num_splits : default_splits(B, Hq, Hkv, Tmax, Dk, GQA_BF16);
+    const size_t need = ws_bytes(B, Hq, Dv, S);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return GQA_ERR_WORKSPACE;
+
+    const int G = Hq / Hkv;
+    gqa::DecodeArgs a = {};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.lens = seq_lens;
+    a.part_o = (float *)workspace;
+    a.part_lse = (float *)workspace + (size_t)B * Hq * S * Dv;
+    a.B = B;
+    a.Hq = Hq;
+    a.Hkv = Hkv;
+    a.Tmax = Tmax;
+    a.G = G;
+    a.k_sb = k_sb;
+    a.k_sh = k_sh;
+    a.k_st = k_st;
+    a.v_sb = v_sb;
+    a.v_sh = v_sh;
+    a.v_st = v_st;
+    a.S = S;
+    a.chunk = 0;
+    const int hpb = gqa::decode_bf16_heads_per_block(Dk, G);
+    a.n_hblk = (G + hpb - 1) / hpb;
+    a.n_wg = gqa::decode_bf16_flat_workgroups(Dk);
+    a.c = folded_scale(scale);
+    a.fp8 = 1;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.ks_sb = ks_sb;
+    a.ks_sh = ks_sh;
+    a.ks_st = ks_st;
+    a.vs_sb = vs_sb;
+    a.vs_sh = vs_sh;
+    a.vs_st = vs_st;
+    hipStream_t st = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (gqa::launch_decode_fp8(a, Dk, Dv, st) != 0) return GQA_ERR_UNSUPPORTED;
+    gqa::CombineArgs c;
+    c.part_o = a.part_o;
+    c.part_lse = a.part_lse;
+    c.out = out;
+    c.B = B;
+    c.Hq = Hq;
+    c.S = S;
+    c.Dv = Dv;
+    c.out_bf16 = 1;
+    return launch_status(gqa::launch_combine(c, st));
+}
+
 GQA_API size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_splits)
 {
     if (B <= 0 || Hq <= 0 || Dv <= 0 || num_splits <= 0 || num_splits > kMaxSplits) return 0;

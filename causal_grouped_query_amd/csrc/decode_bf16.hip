@@ -23,6 +23,19 @@
 // sequence into S equal chunks (one workgroup each), decode_bf16_flat_kernel
 // shares all key tiles of all sequences out evenly over a fixed number of
 // workgroups (used for S >= 3; ragged lengths then cost no balance).
+//
+// The flat kernel also reads an FP8 cache (template flag F8): E4M3 codes
+// with one fp32 scale per (b, h, t) row, the block-scaled FP8 form of
+// "Attention Architecture Evolution" (DSA section) with a block of a whole
+// row.  The raw tile (half the bytes) and its 64 row scales come in through
+// the same copy ring; the wave then converts the codes exactly to bf16
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1: every E4M3 value is a bf16
+// value) into the bf16 tile layout the MFMA reads use: K before the scores,
+// then V into the same tile before P V.  Scores are multiplied by
+// the key's scale; the value scale is folded into the bf16 weight of the
+// P V product, and the normaliser sums the unscaled fp32 weights.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -39,6 +52,16 @@ template <int DK, int DV, int STAGES>
 struct DecSmem {
     uint16_t k[STAGES][kTK * DK];
     uint16_t v[STAGES][kTK * DV];
+};
+
+// FP8 flat decode: a ring of raw tiles (codes and row scales) and one
+// converted bf16 tile, holding K for the scores and then V for P V
+template <int DK, int DV, int STAGES>
+struct DecSmemF8 {
+    uint8_t kq[STAGES][kTK * DK];
+    uint8_t vq[STAGES][kTK * DV];
+    float sc[STAGES][2 * kTK];  // key scales of the tile's 32 rows, then value scales
+    uint16_t k[1][kTK * (DK > DV ? DK : DV)];
 };
 
 template <int DK, int DV, int NW, int STAGES>
@@ -267,19 +290,22 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kern
 // capped so that no stream is cut into more than S pieces: consecutive cuts
 // are at least floor(T / N) tiles apart, so a stream of n tiles has at most
 // (n - 2) / floor(T / N) + 2 pieces.
-template <int DK, int DV, int STAGES>
+template <int DK, int DV, int STAGES, bool F8>
 __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
 {
     constexpr int NT = 64;
-    constexpr int CPRK = DK / 8, CPRV = DV / 8;
+    constexpr int EB = F8 ? 1 : 2;                  // bytes per cached element
+    constexpr int CPRK = DK * EB / 16, CPRV = DV * EB / 16;  // 16-byte copies per row
     constexpr int KS = DK / 16;
     constexpr int DT = DV / 32;
     constexpr int KINS = kTK * CPRK / NT;
     constexpr int VINS = kTK * CPRV / NT;
-    constexpr int NI = KINS + VINS;
+    constexpr int NI = KINS + VINS + (F8 ? 1 : 0);  // + one copy of the tile's row scales
+    static_assert(kTK * CPRK % NT == 0 && kTK * CPRV % NT == 0, "tile must split evenly");
     static_assert(STAGES >= 2 && (STAGES - 2) * NI < 64, "ring depth");
 
-    __shared__ __attribute__((aligned(1024))) DecSmem<DK, DV, STAGES> sm;
+    using Smem = typename std::conditional<F8, DecSmemF8<DK, DV, STAGES>, DecSmem<DK, DV, STAGES>>::type;
+    __shared__ __attribute__((aligned(1024))) Smem sm;
 
     const int lane = threadIdx.x;
     const int col = lane & 31, hi = lane >> 5;
@@ -400,51 +426,83 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
     };
 
     using Tile = PlaneTile<kTK>;
+    // Source (row, 16-byte chunk) of each of this lane's copies: the bf16
+    // tile in plane layout, or (F8) the raw tile row-major, slot q at byte
+    // 16 q (row q / CPR, chunk q % CPR).
+    auto src_of = [&](int q, int cpr, int &row, int &chunk) {
+        if constexpr (F8) {
+            row = q / cpr;
+            chunk = q % cpr;
+        } else {
+            (void)cpr;
+            Tile::slot_source(q, row, chunk);
+        }
+    };
     int krow_[KINS], vrow_[VINS];
     unsigned koff_[KINS], voff_[VINS];
 #pragma unroll
     for (int j = 0; j < KINS; ++j) {
         int row, chunk;
-        Tile::slot_source(j * 64 + lane, row, chunk);
+        src_of(j * 64 + lane, CPRK, row, chunk);
         krow_[j] = row;
-        koff_[j] = (unsigned)(row * p.k_st + chunk * 8) * 2u;
+        koff_[j] = F8 ? (unsigned)(row * p.k_st + chunk * 16) : (unsigned)(row * p.k_st + chunk * 8) * 2u;
     }
 #pragma unroll
     for (int j = 0; j < VINS; ++j) {
         int row, chunk;
-        Tile::slot_source(j * 64 + lane, row, chunk);
+        src_of(j * 64 + lane, CPRV, row, chunk);
         vrow_[j] = row;
-        voff_[j] = (unsigned)(row * p.v_st + chunk * 8) * 2u;
+        voff_[j] = F8 ? (unsigned)(row * p.v_st + chunk * 16) : (unsigned)(row * p.v_st + chunk * 8) * 2u;
     }
+    // LDS destinations of copy j (a wave writes 64 consecutive 16-byte slots)
+    auto kdst = [&](int slot, int j) -> void * {
+        if constexpr (F8) return &sm.kq[slot][j * 64 * 16];
+        else return &sm.k[slot][j * 64 * 8];
+    };
+    auto vdst = [&](int slot, int j) -> void * {
+        if constexpr (F8) return &sm.vq[slot][j * 64 * 16];
+        else return &sm.v[slot][j * 64 * 8];
+    };
     // copy the tile under cursor c into ring slot `slot`
+    // element type of the cached rows: bf16, or one-byte codes
+    using Elem = typename std::conditional<F8, uint8_t, uint16_t>::type;
     auto issue_tile = [&](const Cur &c, int slot) {
         const int kvh = c.s / p.n_hblk;
         const int len = c.len;
         const int k0 = c.u * kTK;
-        const uint16_t *kb = (const uint16_t *)p.k + (size_t)c.b * p.k_sb + (size_t)kvh * p.k_sh;
-        const uint16_t *vb = (const uint16_t *)p.v + (size_t)c.b * p.v_sb + (size_t)kvh * p.v_sh;
+        const Elem *kb = (const Elem *)p.k + (size_t)c.b * p.k_sb + (size_t)kvh * p.k_sh;
+        const Elem *vb = (const Elem *)p.v + (size_t)c.b * p.v_sb + (size_t)kvh * p.v_sh;
         if (k0 + kTK <= len) {
-            const uint16_t *k0p = kb + (size_t)k0 * p.k_st;
-            const uint16_t *v0p = vb + (size_t)k0 * p.v_st;
+            const Elem *k0p = kb + (size_t)k0 * p.k_st;
+            const Elem *v0p = vb + (size_t)k0 * p.v_st;
 #pragma unroll
-            for (int j = 0; j < KINS; ++j) g2lds16(k0p, koff_[j], &sm.k[slot][j * 64 * 8]);
+            for (int j = 0; j < KINS; ++j) g2lds16(k0p, koff_[j], kdst(slot, j));
 #pragma unroll
-            for (int j = 0; j < VINS; ++j) g2lds16(v0p, voff_[j], &sm.v[slot][j * 64 * 8]);
+            for (int j = 0; j < VINS; ++j) g2lds16(v0p, voff_[j], vdst(slot, j));
         } else {
             // ragged last tile: rows past the sequence end re-read its last
             // key (in bounds; masked below)
 #pragma unroll
             for (int j = 0; j < KINS; ++j) {
                 const int row = min(k0 + krow_[j], len - 1);
-                g2lds16((const char *)(kb + (size_t)row * p.k_st) + (koff_[j] - (unsigned)(krow_[j] * p.k_st) * 2u),
-                        &sm.k[slot][j * 64 * 8]);
+                g2lds16((const char *)(kb + (size_t)row * p.k_st) + (koff_[j] - (unsigned)(krow_[j] * p.k_st) * (unsigned)EB),
+                        kdst(slot, j));
             }
 #pragma unroll
             for (int j = 0; j < VINS; ++j) {
                 const int row = min(k0 + vrow_[j], len - 1);
-                g2lds16((const char *)(vb + (size_t)row * p.v_st) + (voff_[j] - (unsigned)(vrow_[j] * p.v_st) * 2u),
-                        &sm.v[slot][j * 64 * 8]);
+                g2lds16((const char *)(vb + (size_t)row * p.v_st) + (voff_[j] - (unsigned)(vrow_[j] * p.v_st) * (unsigned)EB),
+                        vdst(slot, j));
             }
+        }
+        if constexpr (F8) {
+            // row scales: lanes 0-31 the keys', 32-63 the values' (rows past
+            // the sequence end re-read its last row)
+            const int r = min(k0 + (lane & 31), len - 1);
+            const float *sp = lane < 32
+                ? p.k_scale + (size_t)c.b * p.ks_sb + (size_t)kvh * p.ks_sh + (size_t)r * p.ks_st
+                : p.v_scale + (size_t)c.b * p.vs_sb + (size_t)kvh * p.vs_sh + (size_t)r * p.vs_st;
+            g2lds4(sp, &sm.sc[slot][0]);
         }
     };
 
@@ -508,7 +566,43 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
         const int kend = cc.len;
         const int k0 = cc.u * kTK;
 
-        const char *ks_ = (const char *)sm.k[slot];
+        // F8: raw tile -> bf16 tile: each lane converts 16 codes (one 16-byte
+        // slot, dims 16 c .. 16 c + 15 of a row) per step into the two bf16
+        // chunks 2 c, 2 c + 1 of that row; the conversion is exact.  The same
+        // wave reads the tile next (a wave's LDS operations complete in order).
+        auto convert = [&](const uint8_t *raw, uint16_t *dst, int cpr, int nslot) {
+            if constexpr (F8) {
+#pragma unroll 1
+                for (int j = 0; j < nslot / 64; ++j) {
+                    const int q = j * 64 + lane;
+                    const int row = q / cpr, c2 = 2 * (q % cpr);
+                    const u32x4 x = *(const u32x4 *)(raw + 16 * q);
+                    u32x4 lo, hi4;
+                    lo.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false));
+                    lo.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true));
+                    lo.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false));
+                    lo.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true));
+                    hi4.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.z, 1.0f, false));
+                    hi4.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.z, 1.0f, true));
+                    hi4.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.w, 1.0f, false));
+                    hi4.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.w, 1.0f, true));
+                    *(u32x4 *)((char *)dst + Tile::offset(row, c2)) = lo;
+                    *(u32x4 *)((char *)dst + Tile::offset(row, c2 + 1)) = hi4;
+                }
+            }
+        };
+        if constexpr (F8) convert(sm.kq[slot], sm.k[0], CPRK, kTK * CPRK);
+        // element e of the score accumulator is key acc_key(0, e, hi): keys
+        // 8 hi + 0..7 and 16 + 8 hi + 0..7 of the tile
+        auto row_scales = [&](int base, float (&dst)[16]) {
+            if constexpr (F8) {
+                const float *sc = &sm.sc[slot][base];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) dst[e] = sc[acc_key(0, e, hi)];
+            }
+        };
+
+        const char *ks_ = (const char *)sm.k[F8 ? 0 : slot];
         f32x16 s;
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[e] = 0.f;
@@ -516,6 +610,14 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
         for (int ks = 0; ks < KS; ++ks) {
             const int off_ = ((ks & 1) ? kbase_odd : kbase_even) + (ks >> 1) * Tile::PLANE_BYTES;
             s = mfma32x32x16(*(const u32x4 *)(ks_ + off_), qreg[ks], s);
+        }
+        if constexpr (F8) {
+            // the tile now takes V (the score reads above were issued first)
+            convert(sm.vq[slot], sm.k[0], CPRV, kTK * CPRV);
+            float ksc[16];  // the keys' row scales
+            row_scales(0, ksc);
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[e] *= ksc[e];
         }
         if (k0 + kTK > kend) {
 #pragma unroll
@@ -538,6 +640,8 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
                 for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
         }
         const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+        float vsc[16];  // F8: the values' row scales
+        if constexpr (F8) row_scales(kTK, vsc);
         u32x4 pb[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -545,13 +649,23 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h + e], c, -m_use));
+            if constexpr (F8) {
+                // value scales ride on the weights; the normaliser takes the
+                // unscaled ones
+#pragma unroll
+                for (int e = 0; e < 8; ++e) l_run += pv[e];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pv[e] *= vsc[8 * h + e];
+            }
             pb[h].x = pack_bf16x2(pv[0], pv[1]);
             pb[h].y = pack_bf16x2(pv[2], pv[3]);
             pb[h].z = pack_bf16x2(pv[4], pv[5]);
             pb[h].w = pack_bf16x2(pv[6], pv[7]);
-            l_run = sum_bf16x8(pb[h], l_run);
+            if constexpr (!F8) l_run = sum_bf16x8(pb[h], l_run);
         }
-        const char *vs_ = (const char *)sm.v[slot];
+        const char *vs_;
+        if constexpr (F8) vs_ = (const char *)sm.k[0];
+        else vs_ = (const char *)sm.v[slot];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
 #pragma unroll
@@ -625,12 +739,24 @@ int decode_bf16_flat_workgroups(int Dk)
     return 8 * 256;
 }
 
-template <int DK, int DV, int STAGES>
+template <int DK, int DV, int STAGES, bool F8 = false>
 int launch_flat(const DecodeArgs &a, hipStream_t stream)
 {
     dim3 grid(a.n_wg), block(64);
-    hipLaunchKernelGGL((decode_bf16_flat_kernel<DK, DV, STAGES>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL((decode_bf16_flat_kernel<DK, DV, STAGES, F8>), grid, block, 0, stream, a);
     return 0;
+}
+
+#ifndef GQA_DEC_F8_STAGES
+#define GQA_DEC_F8_STAGES 2  // raw-tile ring depth of the FP8 flat decode (128-dim)
+#endif
+
+int launch_decode_fp8(const DecodeArgs &a, int Dk, int Dv, hipStream_t stream)
+{
+    if (!a.fp8 || a.n_wg <= 0 || a.S < 3 || !a.k_scale || !a.v_scale) return -1;
+    if (Dk == 128 && Dv == 128) return launch_flat<128, 128, GQA_DEC_F8_STAGES, true>(a, stream);
+    if (Dk == 64 && Dv == 64) return launch_flat<64, 64, 3, true>(a, stream);
+    return -1;
 }
 
 int launch_decode_bf16(const DecodeArgs &a, int Dk, int Dv, hipStream_t stream)

@@ -61,9 +61,16 @@ struct DecodeArgs {
     // [0, lens[b]) select nothing
     const int *idx;
     int topk;
+    // FP8 E4M3 cache (fp8 != 0): k / v hold one-byte codes (strides in
+    // elements = bytes); the value of (b, h, t, d) is code * scale[b, h, t]
+    int fp8;
+    const float *k_scale, *v_scale;
+    long long ks_sb, ks_sh, ks_st, vs_sb, vs_sh, vs_st;
 };
 
 int launch_decode_bf16(const DecodeArgs &a, int Dk, int Dv, hipStream_t stream);
+// Flat decode over an FP8 E4M3 cache (a.fp8 = 1, a.n_wg > 0, a.S >= 3).
+int launch_decode_fp8(const DecodeArgs &a, int Dk, int Dv, hipStream_t stream);
 // Absorbed-MLA shape (Dk 576, Dv 512, V = latent prefix of K), 128 heads per block.
 int launch_mla_decode(const DecodeArgs &a, hipStream_t stream);
 // The same over the positions listed in a.idx; chunk <= mla_topk_max_chunk().

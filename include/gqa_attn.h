@@ -40,6 +40,7 @@
  *    gqa_attn_decode:  (64, 64) or (128, 128), bf16 or fp32;
  *                      (576, 512) bf16 (the absorbed-MLA shape)
  *    gqa_attn_decode_topk: (576, 512) bf16
+ *    gqa_attn_decode_fp8:  (64, 64) or (128, 128), FP8 E4M3 cache, bf16 q / out
  */
 #ifndef GQA_ATTN_H
 #define GQA_ATTN_H
@@ -182,6 +183,43 @@ int gqa_attn_decode(const void *q, const void *k, const void *v, void *out, cons
                     long long k_st, long long v_sb, long long v_sh, long long v_st, float scale,
                     int num_splits, void *workspace, size_t workspace_bytes, int dtype,
                     void *stream);
+
+/*
+ * Single-token decode over an FP8 KV cache.  The cache holds OCP FP8 E4M3
+ * codes (one byte per element: sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits, no infinities) with one fp32 scale per (b, h, t) row, the
+ * block-scaled FP8 form the "Attention Architecture Evolution" page shows
+ * for the DSA indexer's key cache (one scale per block of 128 features: a
+ * whole row for the head dims here); the "Attention variants" page lists
+ * the scale granularity of quantised K/V among the deployment concerns.
+ * Element (b, h, t, d) stands for e4m3(code) * scale[b, h, t]; the result
+ * is attention over those values, as gqa_attn_decode computes it for bf16.
+ *
+ *   q        [B, Hq, 1, Dk] bf16, contiguous, 16-byte aligned
+ *   k, v     codes: element (b, h, t, d) at k[b*k_sb + h*k_sh + t*k_st + d]
+ *            (strides in elements = bytes, positive multiples of 16;
+ *            k_st >= Dk, v_st >= Dv; 16-byte aligned bases)
+ *   k_scale, v_scale  fp32, the scale of row (b, h, t) at
+ *            k_scale[b*ks_sb + h*ks_sh + t*ks_st] (strides > 0)
+ *   out      [B, Hq, 1, Dv] bf16, contiguous
+ *   seq_lens, workspace: as for gqa_attn_decode (workspace of
+ *            gqa_attn_decode_workspace_size(B, Hq, Dv, splits) bytes)
+ *   num_splits  0 (the value of gqa_attn_decode_splits(..., GQA_BF16)) or
+ *            3 .. 1024: the bound on the pieces one sequence's keys are cut
+ *            into by the balanced schedule; 1 and 2 return
+ *            GQA_ERR_INVALID_ARG.
+ * Rows at t >= seq_lens[b] are never read (codes and scales there may hold
+ * anything).  Codes of rows that are read must not be NaN.
+ * Supported: Dk = Dv = 64 or 128 (else GQA_ERR_UNSUPPORTED), row strides up
+ * to 2^25 bytes.  Same error rules as gqa_attn_decode.
+ */
+int gqa_attn_decode_fp8(const void *q, const void *k, const void *v, const float *k_scale,
+                        const float *v_scale, void *out, const int *seq_lens, int B, int Hq, int Hkv,
+                        int Tmax, int Dk, int Dv, long long k_sb, long long k_sh, long long k_st,
+                        long long v_sb, long long v_sh, long long v_st, long long ks_sb,
+                        long long ks_sh, long long ks_st, long long vs_sb, long long vs_sh,
+                        long long vs_st, float scale, int num_splits, void *workspace,
+                        size_t workspace_bytes, void *stream);
 
 /*
  * Split count gqa_attn_decode_topk uses when called with num_splits = 0

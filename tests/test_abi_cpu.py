@@ -175,3 +175,28 @@ def test_decode_topk_default_splits():
     assert gqa.decode_topk_splits(512, 128, 2048, 576, 512, BF16) == 1
     assert gqa.decode_topk_splits(512, 128, 100000, 576, 512, BF16) == 25
     assert gqa.lib().gqa_attn_decode_topk_splits(2, 128, 64, 128, 128, BF16) == UNSUP
+
+
+def _f8(**kw):
+    D, H, T = 128, 8, 64
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, out=FAKE, lens=FAKE, B=2, Hq=32, Hkv=H, Tmax=T, Dk=D, Dv=D,
+             ksb=H * T * D, ksh=T * D, kst=D, vsb=H * T * D, vsh=T * D, vst=D, ssb=H * T, ssh=T, sst=1,
+             tsb=H * T, tsh=T, tst=1, scale=0.1, S=0, ws=FAKE, wsb=1 << 30)
+    a.update(kw)
+    return gqa.lib().gqa_attn_decode_fp8(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["out"], a["lens"], a["B"],
+                                         a["Hq"], a["Hkv"], a["Tmax"], a["Dk"], a["Dv"], a["ksb"], a["ksh"], a["kst"],
+                                         a["vsb"], a["vsh"], a["vst"], a["ssb"], a["ssh"], a["sst"], a["tsb"],
+                                         a["tsh"], a["tst"], a["scale"], a["S"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), INVALID), (dict(k=0), INVALID), (dict(ks=0), INVALID), (dict(vs=0), INVALID),
+    (dict(lens=0), INVALID), (dict(Hq=30), INVALID), (dict(Tmax=0), INVALID), (dict(kst=120), INVALID),
+    (dict(kst=64), INVALID), (dict(vsh=8), INVALID), (dict(sst=0), INVALID), (dict(tsh=-1), INVALID),
+    (dict(S=1), INVALID), (dict(S=2), INVALID), (dict(S=1025), INVALID), (dict(ks=FAKE + 2), INVALID),
+    (dict(k=FAKE + 8), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(Dk=96, Dv=96), UNSUP), (dict(Dk=128, Dv=64), UNSUP), (dict(kst=1 << 26), UNSUP),
+    (dict(ws=0), WS), (dict(wsb=4096), WS),
+])
+def test_decode_fp8_rejects_on_host(kw, code):
+    assert _f8(**kw) == code

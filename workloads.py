@@ -18,6 +18,13 @@ Recipe (the same for every workload and size):
   * packed variable-length workloads draw all tokens of all sequences at once
     in the [total, H, D] layout; cu_seqlens are the running sums of the
     listed lengths;
+  * FP8 decode caches: after q, the generator draws the key values, then
+    the value values, as ``randn * 64`` clamped to the E4M3 range +-448 and
+    cast by torch to float8_e4m3fn (round to nearest even; the codes are
+    kept as bytes), then the key scales, then the value scales, one per
+    (b, h, t) row, as 2^u with u uniform on [-8, -5] (so dequantised values
+    are about N(0, 1)); rows at or past len_b hold the NaN code 0x7F and a
+    NaN scale in parity runs;
   * top-k sparse decode draws the selected positions from a third CPU
     generator seeded with seed + 2000: for each sequence the first
     min(topk, len_b) entries of ``randperm(len_b)`` (distinct positions in
@@ -37,7 +44,7 @@ _DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "fwd", "decode", "mla_decode", "mla_topk_decode", "fwd+decode", "fwd_varlen"
+    kind: str  # "fwd", "decode", "fp8_decode", "mla_decode", "mla_topk_decode", "fwd+decode", "fwd_varlen"
     B: int
     Hq: int
     Hkv: int
@@ -101,6 +108,11 @@ MLA_TOPK = Workload("mla_dsa_topk2048_decode_b16_hq128_tk32768_dk576_dv512", "ml
                     extra={"topk": 2048})
 
 
+# The GQA decode shape over an FP8 E4M3 cache with one scale per row.
+GQA_DECODE_FP8 = Workload("gqa_decode_fp8kv_b64_hq32_hkv8_tmax8192_d128", "fp8_decode", 64, 32, 8, 1, 8192, 128, 128,
+                          "bf16", 7, 1.0 / math.sqrt(128), len_lo=1024, len_hi=8192)
+
+
 def _randn(gen: torch.Generator, shape, dtype: str) -> torch.Tensor:
     return torch.randn(*shape, generator=gen, dtype=torch.float32).to(_DT[dtype])
 
@@ -155,3 +167,27 @@ def topk_indices(w: Workload, lens: torch.Tensor) -> torch.Tensor:
         sel = torch.randperm(n, generator=g)[:topk]
         idx[b, : sel.numel()] = sel.to(torch.int32)
     return idx
+
+
+def fp8_decode_inputs(w: Workload, nan_tail: bool = True):
+    """q [B,Hq,1,Dk] bf16; key / value codes uint8 [B,Hkv,Tmax,D]; key / value
+    row scales float32 [B,Hkv,Tmax]; lengths int32 [B] (all CPU)."""
+    g = torch.Generator("cpu").manual_seed(w.seed)
+    q = _randn(g, (w.B, w.Hq, 1, w.Dk), "bf16")
+
+    def codes(d):
+        x = torch.randn(w.B, w.Hkv, w.Tk, d, generator=g, dtype=torch.float32).mul_(64.0).clamp_(-448.0, 448.0)
+        return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+    kc = codes(w.Dk)
+    vc = codes(w.Dv)
+    ks = torch.exp2(torch.rand(w.B, w.Hkv, w.Tk, generator=g, dtype=torch.float32).mul_(3.0).sub_(8.0))
+    vs = torch.exp2(torch.rand(w.B, w.Hkv, w.Tk, generator=g, dtype=torch.float32).mul_(3.0).sub_(8.0))
+    lens = decode_lengths(w)
+    if nan_tail:
+        for b, n in enumerate(lens.tolist()):
+            kc[b, :, n:] = 0x7F
+            vc[b, :, n:] = 0x7F
+            ks[b, :, n:] = float("nan")
+            vs[b, :, n:] = float("nan")
+    return q, kc, vc, ks, vs, lens
