@@ -407,7 +407,7 @@ GQA_API int gqa_attn_decode_fp8(const void *q, const void *k, const void *v, con
     a.chunk = 0;
     const int hpb = gqa::decode_bf16_heads_per_block(Dk, G);
     a.n_hblk = (G + hpb - 1) / hpb;
-    a.n_wg = gqa::decode_bf16_flat_workgroups(Dk);
+    a.n_wg = gqa::decode_fp8_flat_workgroups(Dk);
     a.c = folded_scale(scale);
     a.fp8 = 1;
     a.k_scale = k_scale;

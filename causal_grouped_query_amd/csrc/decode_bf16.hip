@@ -47,6 +47,9 @@ constexpr int kTK = 32;  // keys per tile
 #ifndef GQA_DEC_STAGES
 #define GQA_DEC_STAGES 2  // K/V ring depth for the 128-dim kernel
 #endif
+#ifndef GQA_DEC_F8_UNROLL
+#define GQA_DEC_F8_UNROLL 4  // FP8 tile conversion: 16-byte slots converted per loop step
+#endif
 
 template <int DK, int DV, int STAGES>
 struct DecSmem {
@@ -572,7 +575,7 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
         // wave reads the tile next (a wave's LDS operations complete in order).
         auto convert = [&](const uint8_t *raw, uint16_t *dst, int cpr, int nslot) {
             if constexpr (F8) {
-#pragma unroll 1
+#pragma unroll GQA_DEC_F8_UNROLL
                 for (int j = 0; j < nslot / 64; ++j) {
                     const int q = j * 64 + lane;
                     const int row = q / cpr, c2 = 2 * (q % cpr);
@@ -737,6 +740,19 @@ int decode_bf16_flat_workgroups(int Dk)
     // and clearly slower at 1280 (258 us) and above 2048 (244 .. 251 us).
     (void)Dk;
     return 8 * 256;
+}
+
+// FP8 flat decode: one resident round of workgroups.  At ~24.5 KiB of LDS
+// six fit a compute unit; measured on the GQA decode workload, 6 per CU
+// (1536) takes 142 us, 5 per CU 152 us, 7 and 8 per CU (a second, partial
+// round) 195 and 187 us.
+#ifndef GQA_DEC_F8_WG_PER_CU
+#define GQA_DEC_F8_WG_PER_CU 6
+#endif
+int decode_fp8_flat_workgroups(int Dk)
+{
+    (void)Dk;
+    return GQA_DEC_F8_WG_PER_CU * 256;
 }
 
 template <int DK, int DV, int STAGES, bool F8 = false>

@@ -79,6 +79,7 @@ int mla_topk_max_chunk();
 int decode_bf16_key_tile();
 // Flat (persistent, balanced) decode for Dk = Dv <= 128: workgroups to launch.
 int decode_bf16_flat_workgroups(int Dk);
+int decode_fp8_flat_workgroups(int Dk);
 int decode_bf16_heads_per_block(int Dk, int G);
 
 // fp32 VALU paths (small head dims; exactness-first).
