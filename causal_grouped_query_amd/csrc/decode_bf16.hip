@@ -28,12 +28,17 @@
 // with one fp32 scale per (b, h, t) row, the block-scaled FP8 form of
 // "Attention Architecture Evolution" (DSA section) with a block of a whole
 // row.  The raw tile (half the bytes) and its 64 row scales come in through
-// the same copy ring; the wave then converts the codes exactly to bf16
-// (v_cvt_scalef32_pk_bf16_fp8 with scale 1: every E4M3 value is a bf16
-// value) into the bf16 tile layout the MFMA reads use: K before the scores,
-// then V into the same tile before P V.  Scores are multiplied by
-// the key's scale; the value scale is folded into the bf16 weight of the
-// P V product, and the normaliser sums the unscaled fp32 weights.
+// the same copy ring, row-major with the 16-byte chunks of row r rotated by
+// XOR with (r >> 1) so that the operand reads below spread over the LDS
+// banks.  MFMA operands are read straight from the codes and converted
+// exactly to bf16 in registers (v_cvt_scalef32_pk_bf16_fp8 with scale 1:
+// every E4M3 value is a bf16 value): K rows as 8-byte reads, V^T with the
+// 8-bit transpose read ds_read_b64_tr_b8 (in each 16-lane group, lane i
+// receives byte i & 7 of the 8-byte chunks addressed by lanes 2 r + (i >> 3),
+// r = 0..7, in that order; checked with an in-bounds probe).  Scores are
+// multiplied by the key's scale; the value scale is folded into the bf16
+// weight of the P V product, and the normaliser sums the unscaled fp32
+// weights.
 #include <type_traits>
 
 #include "device_common.h"
@@ -47,9 +52,6 @@ constexpr int kTK = 32;  // keys per tile
 #ifndef GQA_DEC_STAGES
 #define GQA_DEC_STAGES 2  // K/V ring depth for the 128-dim kernel
 #endif
-#ifndef GQA_DEC_F8_UNROLL
-#define GQA_DEC_F8_UNROLL 4  // FP8 tile conversion: 16-byte slots converted per loop step
-#endif
 
 template <int DK, int DV, int STAGES>
 struct DecSmem {
@@ -57,15 +59,32 @@ struct DecSmem {
     uint16_t v[STAGES][kTK * DV];
 };
 
-// FP8 flat decode: a ring of raw tiles (codes and row scales) and one
-// converted bf16 tile, holding K for the scores and then V for P V
+// FP8 flat decode: a ring of raw tiles (codes and row scales)
 template <int DK, int DV, int STAGES>
 struct DecSmemF8 {
     uint8_t kq[STAGES][kTK * DK];
     uint8_t vq[STAGES][kTK * DV];
     float sc[STAGES][2 * kTK];  // key scales of the tile's 32 rows, then value scales
-    uint16_t k[1][kTK * (DK > DV ? DK : DV)];
 };
+
+// E4M3 codes -> bf16, exact: 8 codes (bytes of x, then of y) to 8 bf16
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16(u32x2 c)
+{
+    u32x4 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, false));
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.x, 1.0f, true));
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, false));
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c.y, 1.0f, true));
+    return r;
+}
+
+// 8-bit transpose read (ds_read_b64_tr_b8), lane layout in the header comment
+__device__ __forceinline__ u32x2 lds_read_tr8(const void *lds_addr)
+{
+    typedef int i32x2 __attribute__((ext_vector_type(2)));
+    i32x2 r = __builtin_amdgcn_ds_read_tr8_b64_v2i32((GQA_LDS i32x2 *)lds_addr);
+    return __builtin_bit_cast(u32x2, r);
+}
 
 template <int DK, int DV, int NW, int STAGES>
 __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kernel(DecodeArgs p)
@@ -431,11 +450,12 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
     using Tile = PlaneTile<kTK>;
     // Source (row, 16-byte chunk) of each of this lane's copies: the bf16
     // tile in plane layout, or (F8) the raw tile row-major, slot q at byte
-    // 16 q (row q / CPR, chunk q % CPR).
+    // 16 q: row q / CPR, and position q % CPR holds chunk position ^ sw(row),
+    // sw(row) = (row >> 1) mod CPR.
     auto src_of = [&](int q, int cpr, int &row, int &chunk) {
         if constexpr (F8) {
             row = q / cpr;
-            chunk = q % cpr;
+            chunk = (q % cpr) ^ ((row >> 1) & (cpr - 1));
         } else {
             (void)cpr;
             Tile::slot_source(q, row, chunk);
@@ -516,6 +536,12 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
     const int vrow = 8 * (vg >> 1) + (vi >> 2), vchunk = 2 * (vg & 1) + ((vi >> 1) & 1);
     const int vb_h0 = Tile::offset(vrow, vchunk) + 8 * (vi & 1);
     const int vb_h1 = Tile::offset(vrow + 4, vchunk) + 8 * (vi & 1);
+    // F8 operand reads from the raw (swizzled) tiles: K row krow, half hi;
+    // V^T lane roles (group g = lane >> 4, i = lane & 15: r = i >> 1, h = i & 1)
+    const int k8_base = krow * DK + 8 * hi;
+    const int k8_sw = (krow >> 1) & (CPRK - 1);
+    const int v8_row = 8 * (vg >> 1) + (vi >> 1);
+    const int v8_h = vi & 1, v8_g1 = vg & 1;
     const float c = p.c;
 
     const int ntl = (int)(hi_t - lo);  // tiles of this workgroup
@@ -569,32 +595,6 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
         const int kend = cc.len;
         const int k0 = cc.u * kTK;
 
-        // F8: raw tile -> bf16 tile: each lane converts 16 codes (one 16-byte
-        // slot, dims 16 c .. 16 c + 15 of a row) per step into the two bf16
-        // chunks 2 c, 2 c + 1 of that row; the conversion is exact.  The same
-        // wave reads the tile next (a wave's LDS operations complete in order).
-        auto convert = [&](const uint8_t *raw, uint16_t *dst, int cpr, int nslot) {
-            if constexpr (F8) {
-#pragma unroll GQA_DEC_F8_UNROLL
-                for (int j = 0; j < nslot / 64; ++j) {
-                    const int q = j * 64 + lane;
-                    const int row = q / cpr, c2 = 2 * (q % cpr);
-                    const u32x4 x = *(const u32x4 *)(raw + 16 * q);
-                    u32x4 lo, hi4;
-                    lo.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false));
-                    lo.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true));
-                    lo.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false));
-                    lo.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true));
-                    hi4.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.z, 1.0f, false));
-                    hi4.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.z, 1.0f, true));
-                    hi4.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.w, 1.0f, false));
-                    hi4.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.w, 1.0f, true));
-                    *(u32x4 *)((char *)dst + Tile::offset(row, c2)) = lo;
-                    *(u32x4 *)((char *)dst + Tile::offset(row, c2 + 1)) = hi4;
-                }
-            }
-        };
-        if constexpr (F8) convert(sm.kq[slot], sm.k[0], CPRK, kTK * CPRK);
         // element e of the score accumulator is key acc_key(0, e, hi): keys
         // 8 hi + 0..7 and 16 + 8 hi + 0..7 of the tile
         auto row_scales = [&](int base, float (&dst)[16]) {
@@ -605,18 +605,27 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
             }
         };
 
-        const char *ks_ = (const char *)sm.k[F8 ? 0 : slot];
         f32x16 s;
 #pragma unroll
         for (int e = 0; e < 16; ++e) s[e] = 0.f;
+        if constexpr (F8) {
+            // K operand: lane (col, hi) takes dims 16 ks + 8 hi .. + 7 of key
+            // row krow: 8 codes of chunk ks, stored at position ks ^ sw(krow)
+            const char *kq_ = (const char *)sm.kq[slot];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int off_ = ((ks & 1) ? kbase_odd : kbase_even) + (ks >> 1) * Tile::PLANE_BYTES;
-            s = mfma32x32x16(*(const u32x4 *)(ks_ + off_), qreg[ks], s);
+            for (int ks = 0; ks < KS; ++ks) {
+                const u32x2 c8 = *(const u32x2 *)(kq_ + k8_base + ((ks ^ k8_sw) << 4));
+                s = mfma32x32x16(e4m3x8_to_bf16(c8), qreg[ks], s);
+            }
+        } else {
+            const char *ks_ = (const char *)sm.k[slot];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int off_ = ((ks & 1) ? kbase_odd : kbase_even) + (ks >> 1) * Tile::PLANE_BYTES;
+                s = mfma32x32x16(*(const u32x4 *)(ks_ + off_), qreg[ks], s);
+            }
         }
         if constexpr (F8) {
-            // the tile now takes V (the score reads above were issued first)
-            convert(sm.vq[slot], sm.k[0], CPRV, kTK * CPRV);
             float ksc[16];  // the keys' row scales
             row_scales(0, ksc);
 #pragma unroll
@@ -666,18 +675,36 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
             pb[h].w = pack_bf16x2(pv[6], pv[7]);
             if constexpr (!F8) l_run = sum_bf16x8(pb[h], l_run);
         }
-        const char *vs_;
-        if constexpr (F8) vs_ = (const char *)sm.k[0];
-        else vs_ = (const char *)sm.v[slot];
+        if constexpr (F8) {
+            // V^T operand of step st, dims 32 dt ..: in 16-lane group g, lane
+            // 2 r + h points at key row 16 st + 8 (g >> 1) + r, dims
+            // 32 dt + 16 (g & 1) + 8 h .. + 7 (chunk 2 dt + (g & 1), half h);
+            // lane i then holds dim 32 dt + 16 (g & 1) + i of keys
+            // 16 st + 8 (g >> 1) + 0..7, the keys of its P^T slice
+            const char *vq_ = (const char *)sm.vq[slot];
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
+            for (int st = 0; st < 2; ++st) {
+                const int row = 16 * st + v8_row;
+                const int sw = (row >> 1) & (CPRV - 1);
+                const char *rp = vq_ + row * DV + 8 * v8_h;
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int o_ = dt * Tile::PLANE_BYTES + 16 * st * 64;
-                const u32x2 lo2 = lds_read_tr16(vs_ + vb_h0 + o_);
-                const u32x2 hv = lds_read_tr16(vs_ + vb_h1 + o_);
-                u32x4 va = {lo2.x, lo2.y, hv.x, hv.y};
-                o[dt] = mfma32x32x16(va, pb[st], o[dt]);
+                for (int dt = 0; dt < DT; ++dt) {
+                    const u32x2 c8 = lds_read_tr8(rp + (((2 * dt + v8_g1) ^ sw) << 4));
+                    o[dt] = mfma32x32x16(e4m3x8_to_bf16(c8), pb[st], o[dt]);
+                }
+            }
+        } else {
+            const char *vs_ = (const char *)sm.v[slot];
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const int o_ = dt * Tile::PLANE_BYTES + 16 * st * 64;
+                    const u32x2 lo2 = lds_read_tr16(vs_ + vb_h0 + o_);
+                    const u32x2 hv = lds_read_tr16(vs_ + vb_h1 + o_);
+                    u32x4 va = {lo2.x, lo2.y, hv.x, hv.y};
+                    o[dt] = mfma32x32x16(va, pb[st], o[dt]);
+                }
             }
         }
 
@@ -742,12 +769,12 @@ int decode_bf16_flat_workgroups(int Dk)
     return 8 * 256;
 }
 
-// FP8 flat decode: one resident round of workgroups.  At ~24.5 KiB of LDS
-// six fit a compute unit; measured on the GQA decode workload, 6 per CU
-// (1536) takes 142 us, 5 per CU 152 us, 7 and 8 per CU (a second, partial
-// round) 195 and 187 us.
+// FP8 flat decode: one resident round of workgroups.  At 16.5 KiB of LDS
+// and two waves per SIMD, eight fit a compute unit; measured on the GQA
+// decode workload, 6 and 8 per CU take 121 .. 129 us, 9 per CU (a second,
+// partial round) 143 .. 148 us.
 #ifndef GQA_DEC_F8_WG_PER_CU
-#define GQA_DEC_F8_WG_PER_CU 6
+#define GQA_DEC_F8_WG_PER_CU 8
 #endif
 int decode_fp8_flat_workgroups(int Dk)
 {
