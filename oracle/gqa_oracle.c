@@ -111,6 +111,8 @@ typedef struct {
     double scale;
     int causal;
     int window; /* 0: none; w > 0 (causal only): keys p-w+1 .. p */
+    int shard;  /* keys are a shard at other absolute positions: query i sits */
+    long long q_minus_k; /* at key index q_minus_k + i of this shard */
 } problem;
 
 /* Visible keys of query i of batch b: j in [*lo, return value). */
@@ -121,7 +123,8 @@ static int visible_range(const problem *P, int b, int i, int *lo)
     if (tk_b < 0) tk_b = 0;
     *lo = 0;
     if (!P->causal) return tk_b;
-    long long pos = (long long)tk_b - P->Tq + i; /* absolute query position */
+    /* absolute query position, counted in keys of this array */
+    long long pos = P->shard ? P->q_minus_k + i : (long long)tk_b - P->Tq + i;
     long long n = pos + 1;                       /* keys 0..pos are visible */
     if (n > tk_b) n = tk_b;
     if (n < 0) n = 0;
@@ -189,7 +192,7 @@ static int check_problem(const problem *P)
         P->Dv <= 0)
         return -1;
     if (P->Hq % P->Hkv != 0) return -1;
-    if (P->causal && !P->kv_lens && P->Tq > P->Tk) return -1;
+    if (P->causal && !P->kv_lens && !P->shard && P->Tq > P->Tk) return -1;
     if (P->window < 0 || (P->window > 0 && !P->causal)) return -1;
     return 0;
 }
@@ -230,7 +233,7 @@ int oracle_attention(const void *q, const long long *qs, int q_dt, const void *k
                      int Dk, int Dv, double scale, int causal, int window, const long long *rows,
                      long long nrows, double *out, double *lse, int nthreads)
 {
-    problem P;
+    problem P = {0};
     P.q = make_view(q, qs, q_dt);
     P.k = make_view(k, ks, k_dt);
     P.v = make_view(v, vs, v_dt);
@@ -294,7 +297,7 @@ int oracle_probs(const void *q, const long long *qs, int q_dt, const void *k,
                  double scale, int causal, int window, int b, int a, int i, double *probs,
                  double *out_row)
 {
-    problem P;
+    problem P = {0};
     P.q = make_view(q, qs, q_dt);
     P.k = make_view(k, ks, k_dt);
     P.v = make_view(v, vs, v_dt);
@@ -364,7 +367,7 @@ int oracle_attention_e4m3kv(const void *q, const long long *qs, int q_dt, const 
                             const long long *rows, long long nrows, double *out, double *lse,
                             int nthreads)
 {
-    problem P;
+    problem P = {0};
     P.q = make_view(q, qs, q_dt);
     P.k = make_view(k, ks, ORACLE_E4M3);
     P.v = make_view(v, vs, ORACLE_E4M3);
@@ -388,6 +391,43 @@ int oracle_attention_e4m3kv(const void *q, const long long *qs, int q_dt, const 
     P.scale = scale;
     P.causal = causal;
     P.window = 0;
+    if (check_problem(&P)) return -1;
+    return run_rows(&P, rows, nrows, out, lse, nthreads);
+}
+
+/*
+ * Attention of Tq queries over one shard of the keys (context / sequence
+ * parallelism: each device holds a slice of the key axis and produces a
+ * partial result to be merged with oracle_lse_merge).  Query i sits at
+ * absolute position q_pos0 + i, key j of the shard at k_pos0 + j; with
+ * causal, key j is visible iff k_pos0 + j <= q_pos0 + i.  A query that sees
+ * no key of the shard gets a zero row and lse = -inf.  Other arguments as
+ * for oracle_attention (no kv_lens, no window).
+ */
+int oracle_attention_shard(const void *q, const long long *qs, int q_dt, const void *k,
+                           const long long *ks, int k_dt, const void *v, const long long *vs,
+                           int v_dt, int B, int Hq, int Hkv, int Tq, int Tk, int Dk, int Dv,
+                           double scale, int causal, long long q_pos0, long long k_pos0,
+                           const long long *rows, long long nrows, double *out, double *lse,
+                           int nthreads)
+{
+    problem P = {0};
+    P.q = make_view(q, qs, q_dt);
+    P.k = make_view(k, ks, k_dt);
+    P.v = make_view(v, vs, v_dt);
+    P.kv_lens = NULL;
+    P.B = B;
+    P.Hq = Hq;
+    P.Hkv = Hkv;
+    P.Tq = Tq;
+    P.Tk = Tk;
+    P.Dk = Dk;
+    P.Dv = Dv;
+    P.scale = scale;
+    P.causal = causal;
+    P.window = 0;
+    P.shard = 1;
+    P.q_minus_k = q_pos0 - k_pos0;
     if (check_problem(&P)) return -1;
     return run_rows(&P, rows, nrows, out, lse, nthreads);
 }

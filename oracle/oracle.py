@@ -63,6 +63,12 @@ def _load():
             P, LLP, I, P, LLP, P, LLP, P, LLP, P, LLP, P,
             I, I, I, I, I, I, I, ctypes.c_double, I, P, ctypes.c_longlong, P, P, I,
         ]
+        lib.oracle_attention_shard.restype = I
+        lib.oracle_attention_shard.argtypes = [
+            P, LLP, I, P, LLP, I, P, LLP, I,
+            I, I, I, I, I, I, I, ctypes.c_double, I, ctypes.c_longlong, ctypes.c_longlong,
+            P, ctypes.c_longlong, P, P, I,
+        ]
         lib.oracle_e4m3_table.restype = None
         lib.oracle_e4m3_table.argtypes = [P]
         lib.oracle_lse_merge.restype = None
@@ -156,6 +162,40 @@ def attention(q, k, v, scale: float, causal: bool, kv_lens=None, rows=None, thre
     if rc != 0:
         raise ValueError("oracle rejected the problem (shapes, head grouping or Tq > Tk with causal)")
     return (out, lse) if with_lse else out
+
+
+def attention_shard(q, k, v, scale: float, causal: bool, q_pos0: int, k_pos0: int, rows=None,
+                    threads: int = 0):
+    """fp64 attention of q over one shard of the keys (context parallelism).
+
+    Query i sits at absolute position q_pos0 + i, key j of the shard at
+    k_pos0 + j; causal: key j is visible iff k_pos0 + j <= q_pos0 + i.  A
+    query with no visible key in the shard gets a zero row and lse = -inf.
+    Returns (out [B,Hq,Tq,Dv] or [len(rows), Dv], lse natural log), the
+    partial result that lse_merge combines across shards.
+    """
+    Q, K, V = _Operand(q), _Operand(k), _Operand(v)
+    B, Hq, Tq, Dk = Q.shape
+    _, Hkv, Tk, _ = K.shape
+    Dv = V.shape[3]
+    if rows is None:
+        out = np.empty((B, Hq, Tq, Dv), dtype=np.float64)
+        lse = np.empty((B, Hq, Tq), dtype=np.float64)
+        rows_ptr, nrows = None, 0
+    else:
+        rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        nrows = rows_arr.size
+        out = np.empty((nrows, Dv), dtype=np.float64)
+        lse = np.empty((nrows,), dtype=np.float64)
+        rows_ptr = rows_arr.ctypes.data
+    rc = _load().oracle_attention_shard(
+        Q.ptr, Q.strides, Q.code, K.ptr, K.strides, K.code, V.ptr, V.strides, V.code,
+        B, Hq, Hkv, Tq, Tk, Dk, Dv, float(scale), int(bool(causal)), int(q_pos0), int(k_pos0),
+        rows_ptr, nrows, out.ctypes.data, lse.ctypes.data, int(threads),
+    )
+    if rc != 0:
+        raise ValueError("oracle rejected the problem")
+    return out, lse
 
 
 def e4m3_table() -> np.ndarray:

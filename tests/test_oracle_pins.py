@@ -703,3 +703,72 @@ def test_e4m3kv_scales_act_linearly():
     for a in range(4):
         p_row, _ = O.probs(q, K, V, 0.2, True, 0, a, 0)
         np.testing.assert_allclose(moved[0, a, 0] - base[0, a, 0], p_row[3] * V[0, 0, 3].numpy(), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- key shards
+# Sequence / context parallelism (the long-context research ledger page,
+# causal-mainline section: Ring / Context Parallel when one device cannot hold
+# the context): each device attends over its slice of the key axis and the
+# partial results are merged exactly.  A shard's keys sit at absolute
+# positions k_pos0 + j, the queries at q_pos0 + i; causal visibility
+# compares absolute positions.
+
+def _shard_mask_reference(q, k, v, scale, q_pos0, k_pos0):
+    """Explicit causal mask on absolute positions, numpy fp64 (independent of
+    the oracle's visible-range arithmetic)."""
+    qq, kk, vv = q.double().numpy(), k.double().numpy(), v.double().numpy()
+    B, Hq, Tq, _ = qq.shape
+    Hkv, Tk = kk.shape[1], kk.shape[2]
+    allowed = (k_pos0 + np.arange(Tk))[None, :] <= (q_pos0 + np.arange(Tq))[:, None]
+    out = np.zeros((B, Hq, Tq, vv.shape[3]))
+    lse = np.full((B, Hq, Tq), -np.inf)
+    for b in range(B):
+        for a in range(Hq):
+            g = a // (Hq // Hkv)
+            s = np.where(allowed, scale * qq[b, a] @ kk[b, g].T, -np.inf)
+            m = s.max(axis=1)
+            has = np.isfinite(m)
+            e = np.exp(s - np.where(has, m, 0.0)[:, None])
+            l = e.sum(axis=1)
+            out[b, a, has] = (e[has] / l[has, None]) @ vv[b, g]
+            lse[b, a, has] = m[has] + np.log(l[has])
+    return out, lse
+
+
+@pytest.mark.parametrize("q_pos0,k_pos0", [(40, 0), (40, 30), (40, 45), (10, 55), (100, 3)])
+def test_shard_equals_explicit_position_mask(q_pos0, k_pos0):
+    q = _rand((2, 4, 9, 8), 150)
+    k = _rand((2, 2, 21, 8), 151)
+    v = _rand((2, 2, 21, 8), 152)
+    out, lse = O.attention_shard(q, k, v, 0.4, True, q_pos0, k_pos0)
+    ref, ref_lse = _shard_mask_reference(q, k, v, 0.4, q_pos0, k_pos0)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("cuts", [[0, 70], [0, 25, 70], [0, 1, 33, 34, 69, 70], [0, 50, 60, 70]])
+def test_merged_causal_shards_equal_full_attention(cuts):
+    """Causal suffix attention (Tq = 12 queries at positions 58..69 over 70
+    keys) equals the LSE merge of the shards' partial results, for shards
+    before, across and after the queries' positions."""
+    Tq, Tk = 12, 70
+    q = _rand((1, 4, Tq, 16), 153)
+    k = _rand((1, 1, Tk, 16), 154)
+    v = _rand((1, 1, Tk, 16), 155)
+    full, full_lse = O.attention(q, k, v, 0.3, True, with_lse=True)
+    parts, lses = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        o, l = O.attention_shard(q, k[:, :, a:b].contiguous(), v[:, :, a:b].contiguous(), 0.3, True,
+                                 Tk - Tq, a)
+        parts.append(o.reshape(-1, 16))
+        lses.append(l.reshape(-1))
+    merged, merged_lse = O.lse_merge(np.stack(parts), np.stack(lses))
+    np.testing.assert_allclose(merged, full.reshape(-1, 16), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(merged_lse, full_lse.reshape(-1), rtol=0, atol=1e-13)
+
+
+def test_future_shard_gives_zero_rows_and_no_weight():
+    q = _rand((1, 2, 5, 8), 156)
+    k = _rand((1, 1, 6, 8), 157)
+    out, lse = O.attention_shard(q, k, k, 0.5, True, 10, 15)   # keys 15..20, queries 10..14
+    assert np.all(out == 0.0) and np.all(np.isneginf(lse))
