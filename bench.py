@@ -385,6 +385,31 @@ def extra_workloads(torch, gqa, W, dev):
                    "kv_bytes_per_launch": b}
     del q, kc, out, ws, sels
 
+    w = W.CP_SHARD
+    nsh, q_pos0 = w.extra["shards"], w.extra["q_pos0"]
+    q, _, _ = W.fwd_inputs(w)
+    q = q.to(dev)
+    outs = torch.empty((nsh, w.B, w.Hq, w.Tq, w.Dv), dtype=torch.float32, device=dev)
+    lses = torch.empty((nsh, w.B, w.Hq, w.Tq), dtype=torch.float32, device=dev)
+    shards = []
+    for r in range(nsh):  # every device's shard once, for real partials to merge
+        _, k, v = W.fwd_inputs(dataclasses.replace(w, seed=w.seed + 10 * r))
+        k, v = k.to(dev), v.to(dev)
+        gqa.attention_shard(q, k, v, q_pos0, r * w.Tk, scale=w.scale, out=outs[r], lse=lses[r])
+        shards.append((k, v))
+    k0, v0 = shards[0]  # the heaviest shard: every key visible to every query
+    sec = _time(torch, lambda: gqa.attention_shard(q, k0, v0, q_pos0, 0, scale=w.scale, out=outs[0], lse=lses[0]))
+    f = 2.0 * (w.Dk + w.Dv) * w.Tq * w.Tk * w.Hq * w.B
+    merged = torch.empty((w.B, w.Hq, w.Tq, w.Dv), dtype=torch.bfloat16, device=dev)
+    msec = _time(torch, lambda: gqa.merge(outs, lses, out=merged))
+    mb = float(outs.numel() * 4 + lses.numel() * 4 + merged.numel() * 2)
+    res[w.name] = {"shard_us": round(sec * 1e6, 1), "shard_TFLOP/s": round(f / sec / 1e12, 1),
+                   "shard_frac_mfma_peak": round(f / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
+                   "merge_us": round(msec * 1e6, 1), "merge_GB/s": round(mb / msec / 1e9, 1),
+                   "merge_frac_hbm_peak": round(mb / msec / 1e9 / PEAK_HBM_GBPS, 4), "shards": nsh,
+                   "merge_bytes": mb}
+    del q, outs, lses, shards, k0, v0, merged
+
     w = W.TINY_F32
     q, k, v = (t.to(dev) for t in W.fwd_inputs(w))
     sec = _time(torch, lambda: gqa.attention(q, k, v, scale=w.scale))

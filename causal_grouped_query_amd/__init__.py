@@ -11,6 +11,8 @@ stream.  There is no fallback: if the library is missing, every call raises.
     decode_topk(q, kv_cache, seq_lens, indices)       top-k sparse (DSA) decode, absorbed MLA
     decode_fp8(q, k_codes, v_codes, k_scale, v_scale, seq_lens)
                                                       decode over an FP8 E4M3 cache with row scales
+    attention_shard(q, k, v, q_pos0, k_pos0)          one key shard: fp32 partial output + LSE
+    merge(o_parts, lse_parts)                         exact LSE merge of partial results
 
 Shapes follow the C header include/gqa_attn.h: q [B,Hq,Tq,Dk], k [B,Hkv,Tk,Dk],
 v [B,Hkv,Tk,Dv]; decode caches [B,Hkv,Tmax,D] with any element strides whose
@@ -24,7 +26,7 @@ import os
 
 __all__ = [
     "LIB_PATH", "GQA_BF16", "GQA_F32", "GQAError", "lib", "attention", "attention_varlen", "decode",
-    "decode_splits", "decode_workspace_size", "decode_topk", "decode_topk_splits", "decode_fp8", "strerror",
+    "decode_splits", "decode_workspace_size", "decode_topk", "decode_topk_splits", "decode_fp8", "attention_shard", "merge", "strerror",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_attn.so")
@@ -33,7 +35,7 @@ GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP
 
 EXPORTS = ("gqa_attn_fwd", "gqa_attn_fwd_varlen", "gqa_attn_decode", "gqa_attn_decode_splits",
            "gqa_attn_decode_workspace_size", "gqa_attn_decode_topk", "gqa_attn_decode_topk_splits",
-           "gqa_attn_decode_fp8", "gqa_attn_strerror")
+           "gqa_attn_decode_fp8", "gqa_attn_fwd_shard", "gqa_attn_merge", "gqa_attn_strerror")
 
 _lib = None
 
@@ -72,6 +74,10 @@ def lib() -> ctypes.CDLL:
         L.gqa_attn_decode_topk.argtypes = [P, P, P, P, P, I, I, I, I, I, I, LL, LL, F, I, P, SZ, I, P]
         L.gqa_attn_decode_fp8.restype = I
         L.gqa_attn_decode_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I] + [LL] * 12 + [F, I, P, SZ, P]
+        L.gqa_attn_fwd_shard.restype = I
+        L.gqa_attn_fwd_shard.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, LL, LL, F, I, I, P]
+        L.gqa_attn_merge.restype = I
+        L.gqa_attn_merge.argtypes = [P, P, P, I, LL, I, I, P]
         L.gqa_attn_strerror.restype = ctypes.c_char_p
         L.gqa_attn_strerror.argtypes = [I]
         _lib = L
@@ -354,4 +360,58 @@ def decode_fp8(q, k_codes, v_codes, k_scale, v_scale, seq_lens, scale: float | N
                                    workspace.numel() * workspace.element_size(), _stream())
     if rc != GQA_OK:
         raise GQAError(rc, "gqa_attn_decode_fp8")
+    return out
+
+
+def attention_shard(q, k, v, q_pos0: int, k_pos0: int, scale: float | None = None, causal: bool = True,
+                    out=None, lse=None):
+    """Forward over one shard of the keys (context parallelism): q [B,Hq,Tq,Dk]
+    at absolute positions q_pos0 + i, k / v [B,Hkv,Tk,D] at k_pos0 + j, all
+    contiguous bfloat16.  Returns (out fp32 [B,Hq,Tq,Dv], lse fp32 [B,Hq,Tq],
+    natural log, -inf where the shard holds no visible key)."""
+    import torch
+    _check_cuda(q, k, v)
+    for t in (q, k, v):
+        if t.dim() != 4 or not t.is_contiguous() or t.dtype != torch.bfloat16:
+            raise ValueError("q, k, v must be contiguous 4-D bfloat16 tensors")
+    B, Hq, Tq, Dk = q.shape
+    _, Hkv, Tk, _ = k.shape
+    Dv = v.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dk)
+    if out is None:
+        out = torch.empty((B, Hq, Tq, Dv), dtype=torch.float32, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, Tq), dtype=torch.float32, device=q.device)
+    if (out.shape != (B, Hq, Tq, Dv) or out.dtype != torch.float32 or not out.is_contiguous()
+            or lse.shape != (B, Hq, Tq) or lse.dtype != torch.float32 or not lse.is_contiguous()):
+        raise ValueError("out must be fp32 [B,Hq,Tq,Dv] and lse fp32 [B,Hq,Tq], contiguous")
+    rc = lib().gqa_attn_fwd_shard(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq,
+                                  Hkv, Tq, Tk, Dk, Dv, int(q_pos0), int(k_pos0), float(scale), int(bool(causal)),
+                                  GQA_BF16, _stream())
+    if rc != GQA_OK:
+        raise GQAError(rc, "gqa_attn_fwd_shard")
+    return out, lse
+
+
+def merge(o_parts, lse_parts, out_dtype=None, out=None):
+    """Exact log-sum-exp merge: o_parts fp32 [S, ..., Dv], lse_parts fp32
+    [S, ...] (natural log) -> [..., Dv] (bfloat16 by default, or float32)."""
+    import torch
+    _check_cuda(o_parts, lse_parts)
+    if o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32:
+        raise ValueError("partials must be float32")
+    if not (o_parts.is_contiguous() and lse_parts.is_contiguous()) or o_parts.shape[:-1] != lse_parts.shape:
+        raise ValueError("o_parts [S, ..., Dv] and lse_parts [S, ...] must be contiguous and agree")
+    S, Dv = o_parts.shape[0], o_parts.shape[-1]
+    rows = lse_parts[0].numel()
+    out_dtype = torch.bfloat16 if out_dtype is None else out_dtype
+    code = {torch.bfloat16: GQA_BF16, torch.float32: GQA_F32}[out_dtype]
+    if out is None:
+        out = torch.empty(o_parts.shape[1:], dtype=out_dtype, device=o_parts.device)
+    elif out.shape != o_parts.shape[1:] or out.dtype != out_dtype or not out.is_contiguous():
+        raise ValueError("out must be contiguous with the shape of one part")
+    rc = lib().gqa_attn_merge(o_parts.data_ptr(), lse_parts.data_ptr(), out.data_ptr(), S, rows, Dv, code, _stream())
+    if rc != GQA_OK:
+        raise GQAError(rc, "gqa_attn_merge")
     return out

@@ -249,6 +249,61 @@ GQA_API int gqa_attn_fwd_varlen(const void *q, const void *k, const void *v, voi
     return launch_status(gqa::launch_fwd_bf16(a, Dk, (hipStream_t)stream));
 }
 
+GQA_API int gqa_attn_fwd_shard(const void *q, const void *k, const void *v, float *out, float *lse, int B,
+                               int Hq, int Hkv, int Tq, int Tk, int Dk, int Dv, long long q_pos0,
+                               long long k_pos0, float scale, int causal, int dtype, void *stream)
+{
+    if (!q || !k || !v || !out || !lse) return GQA_ERR_INVALID_ARG;
+    int rc = check_common(B, Hq, Hkv, Dk, Dv, scale, dtype);
+    if (rc != GQA_OK) return rc;
+    if (Tq <= 0 || Tk <= 0) return GQA_ERR_INVALID_ARG;
+    if (causal != 0 && causal != 1) return GQA_ERR_INVALID_ARG;
+    if (q_pos0 < 0 || k_pos0 < 0) return GQA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(lse, 4))
+        return GQA_ERR_INVALID_ARG;
+    if (dtype != GQA_BF16 || !head_dims_fwd(Dk, Dv)) return GQA_ERR_UNSUPPORTED;
+    // the kernel counts query positions in keys of the shard with 32-bit ints
+    const long long qmk = q_pos0 - k_pos0;
+    if (qmk > (1LL << 30) || qmk < -(1LL << 30)) return GQA_ERR_UNSUPPORTED;
+
+    gqa::FwdArgs a = {};
+    a.q = (const uint16_t *)q;
+    a.k = (const uint16_t *)k;
+    a.v = (const uint16_t *)v;
+    a.Tk = Tk;
+    if (!fwd_geometry(a, B, Hq, Hkv, Tq)) return GQA_ERR_UNSUPPORTED;
+    a.causal = causal;
+    a.c = folded_scale(scale);
+    a.varlen = 0;
+    a.q_minus_k = (int)qmk;
+    a.out_f32 = out;
+    a.lse = lse;
+    (void)hipGetLastError();
+    return launch_status(gqa::launch_fwd_bf16_shard(a, Dk, (hipStream_t)stream));
+}
+
+GQA_API int gqa_attn_merge(const float *o_parts, const float *lse_parts, void *out, int num_parts,
+                           long long rows, int Dv, int out_dtype, void *stream)
+{
+    if (!o_parts || !lse_parts || !out) return GQA_ERR_INVALID_ARG;
+    if (num_parts <= 0 || rows <= 0 || Dv <= 0) return GQA_ERR_INVALID_ARG;
+    if (out_dtype != GQA_BF16 && out_dtype != GQA_F32) return GQA_ERR_INVALID_ARG;
+    if (!aligned(o_parts, 16) || !aligned(lse_parts, 4) || !aligned(out, out_dtype == GQA_BF16 ? 8 : 16))
+        return GQA_ERR_INVALID_ARG;
+    if (Dv % 4 != 0 || Dv > 512) return GQA_ERR_UNSUPPORTED;
+    if (rows * (Dv / 4) > (1LL << 40) || num_parts > kMaxSplits) return GQA_ERR_UNSUPPORTED;
+    gqa::MergeArgs m;
+    m.o = o_parts;
+    m.lse = lse_parts;
+    m.out = out;
+    m.rows = rows;
+    m.S = num_parts;
+    m.Dv = Dv;
+    m.out_bf16 = out_dtype == GQA_BF16;
+    (void)hipGetLastError();
+    return launch_status(gqa::launch_merge(m, (hipStream_t)stream));
+}
+
 GQA_API int gqa_attn_decode_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int Dv, int dtype)
 {
     int rc = check_common(B, Hq, Hkv, Dk, Dv, 1.f, dtype);

@@ -66,7 +66,68 @@ __global__ __launch_bounds__(kCT) void combine_kernel(CombineArgs p)
     }
 }
 
+// Merge of gathered partial results (sequence-parallel shards): many rows,
+// few parts.  One thread per (row, 4 output dims); the threads of a row each
+// read the row's S lse values (the same addresses) and form the weights
+// themselves, then stream the S partial outputs.
+constexpr int kMT = 256;  // threads per merge workgroup
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(kMT) void merge_kernel(MergeArgs p)
+{
+    const int per_row = p.Dv / 4;
+    const long long t = (long long)blockIdx.x * kMT + threadIdx.x;
+    if (t >= p.rows * per_row) return;
+    const long long row = t / per_row;
+    const int d0 = (int)(t - row * per_row) * 4;
+    constexpr float kLog2e = 1.4426950408889634f;
+    float L = -INFINITY;
+    for (int s = 0; s < p.S; ++s) L = fmaxf(L, p.lse[(size_t)s * p.rows + row] * kLog2e);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    if (L != -INFINITY) {
+        // no data-dependent branch, so the loads of consecutive parts are in
+        // flight together; an empty part (weight 0: lse = -inf) is loaded
+        // (its slot is in bounds) but selected away, whatever it holds
+#pragma unroll 8
+        for (int s = 0; s < p.S; ++s) {
+            const float w = __builtin_amdgcn_exp2f(p.lse[(size_t)s * p.rows + row] * kLog2e - L);
+            const float4 v = *(const float4 *)(p.o + ((size_t)s * p.rows + row) * p.Dv + d0);
+            const bool use = w != 0.f;
+            wsum += w;
+            acc[0] = use ? fmaf(w, v.x, acc[0]) : acc[0];
+            acc[1] = use ? fmaf(w, v.y, acc[1]) : acc[1];
+            acc[2] = use ? fmaf(w, v.z, acc[2]) : acc[2];
+            acc[3] = use ? fmaf(w, v.w, acc[3]) : acc[3];
+        }
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    if (OUT_BF16) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        bf16x4 r = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv), (__bf16)(acc[2] * inv),
+                    (__bf16)(acc[3] * inv)};
+        *(bf16x4 *)((uint16_t *)p.out + row * p.Dv + d0) = r;
+    } else {
+        *(float4 *)((float *)p.out + row * p.Dv + d0) =
+            make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    }
+}
+
 } // namespace
+
+int launch_merge(const MergeArgs &a, hipStream_t stream)
+{
+    if (a.Dv % 4 != 0 || a.Dv <= 0 || a.S <= 0 || a.rows <= 0) return -1;
+    const long long threads = a.rows * (a.Dv / 4);
+    const long long nblk = (threads + kMT - 1) / kMT;
+    if (nblk > 0x7fffffffLL) return -1;
+    dim3 grid((unsigned)nblk), block(kMT);
+    if (a.out_bf16)
+        hipLaunchKernelGGL(merge_kernel<true>, grid, block, 0, stream, a);
+    else
+        hipLaunchKernelGGL(merge_kernel<false>, grid, block, 0, stream, a);
+    return 0;
+}
 
 int launch_combine(const CombineArgs &a, hipStream_t stream)
 {

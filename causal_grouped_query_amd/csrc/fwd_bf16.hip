@@ -95,7 +95,11 @@ __device__ __forceinline__ int used_len(const int *cu, const int *used, int b)
     return used ? min(max(used[b], 0), n) : n;
 }
 
-template <int D, bool VAR>
+// PART: key-shard mode for context parallelism (dense layout only): query i
+// sits at key index q_minus_k + i of the given keys, and the normalised
+// output goes out in fp32 together with its natural-log LSE, the partial
+// result an exact log-sum-exp merge combines across shards.
+template <int D, bool VAR, bool PART = false>
 __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArgs p)
 {
     constexpr int CPR = D / 8;                     // 16-byte chunks per row
@@ -179,7 +183,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
     const int col = lane & 31, hi = lane >> 5;
     const int head = kvh * p.G + hblk * p.Gt + (w % p.Gt);
     const int q0 = qt * p.Pt + (w / p.Gt) * ROWS;  // first query index of this wave
-    const int off = Tk - Tq;                       // absolute position of query 0
+    const int off = PART ? p.q_minus_k : Tk - Tq;  // position of query 0, counted in keys
     const bool wave_active = q0 < Tq;
 
     // keys the workgroup needs: tiles [t0, t0 + ntiles)
@@ -456,6 +460,29 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
     }
 
     if (!wave_active) return;
+    if constexpr (PART) {
+#pragma unroll
+        for (int cb = 0; cb < kNC; ++cb) {
+            const int qi = q0 + 32 * cb + col;
+            if (qi >= Tq) continue;
+            const float l_tot = halves_sum(l_run[cb]);
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            const size_t row = ((size_t)b * p.Hq + head) * p.Tq + qi;
+            float *orow = p.out_f32 + row * D;
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 v4 = {o[cb][dt][4 * j] * inv, o[cb][dt][4 * j + 1] * inv,
+                                      o[cb][dt][4 * j + 2] * inv, o[cb][dt][4 * j + 3] * inv};
+                    *(f32x4 *)(orow + 32 * dt + 8 * j + 4 * hi) = v4;
+                }
+            // lse = ln(sum of exp(scale * s)) = ln 2 * (m + log2 l) in the
+            // kernel's base-2 units; no visible key: -inf (weighs nothing)
+            if (hi == 0) p.lse[row] = l_tot > 0.f ? 0.69314718055994531f * (m_run[cb] + __log2f(l_tot)) : -INFINITY;
+        }
+        return;
+    }
 #pragma unroll
     for (int cb = 0; cb < kNC; ++cb) {
         const int qi = q0 + 32 * cb + col;
@@ -494,6 +521,20 @@ int launch_fwd_bf16(const FwdArgs &a, int D, hipStream_t stream)
         hipLaunchKernelGGL((fwd_bf16_kernel<128, true>), grid, block, 0, stream, a);
     else if (D == 64)
         hipLaunchKernelGGL((fwd_bf16_kernel<64, true>), grid, block, 0, stream, a);
+    else
+        return -1;
+    return 0;
+}
+
+int launch_fwd_bf16_shard(const FwdArgs &a, int D, hipStream_t stream)
+{
+    const long long nblk = (long long)a.n_units * a.n_qt;
+    if (nblk <= 0 || nblk > 0x7fffffffLL || a.varlen || !a.out_f32 || !a.lse) return -1;
+    dim3 grid((unsigned)nblk), block(kThreads);
+    if (D == 128)
+        hipLaunchKernelGGL((fwd_bf16_kernel<128, false, true>), grid, block, 0, stream, a);
+    else if (D == 64)
+        hipLaunchKernelGGL((fwd_bf16_kernel<64, false, true>), grid, block, 0, stream, a);
     else
         return -1;
     return 0;

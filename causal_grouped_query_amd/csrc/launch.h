@@ -34,9 +34,16 @@ struct FwdArgs {
     const int *used_q, *used_k;
     long long q_sh, q_st, k_sh, k_st, v_sh, v_st, o_sh, o_st;
     int window;
+    // key-shard mode (context parallelism): query i sits at key index
+    // q_minus_k + i of this shard; fp32 outputs [B, Hq, Tq, Dv] and
+    // natural-log LSE [B, Hq, Tq] instead of out
+    int q_minus_k;
+    float *out_f32, *lse;
 };
 
 int launch_fwd_bf16(const FwdArgs &a, int D, hipStream_t stream);
+// Key-shard forward (a.q_minus_k, a.out_f32, a.lse; dense layout).
+int launch_fwd_bf16_shard(const FwdArgs &a, int D, hipStream_t stream);
 int fwd_bf16_waves_per_block();
 int fwd_bf16_rows_per_wave();
 
@@ -101,5 +108,16 @@ struct CombineArgs {
     int out_bf16;
 };
 int launch_combine(const CombineArgs &a, hipStream_t stream);
+
+// Exact LSE merge of S gathered partial results (part-major, natural-log LSE).
+struct MergeArgs {
+    const float *o;    // [S, rows, Dv]
+    const float *lse;  // [S, rows]
+    void *out;         // [rows, Dv], bf16 or fp32
+    long long rows;
+    int S, Dv;
+    int out_bf16;
+};
+int launch_merge(const MergeArgs &a, hipStream_t stream);
 
 } // namespace gqa

@@ -37,6 +37,7 @@
  * Supported head dims (anything else returns GQA_ERR_UNSUPPORTED):
  *    gqa_attn_fwd:     (Dk, Dv) = (64, 64) or (128, 128), bf16 or fp32
  *    gqa_attn_fwd_varlen: (64, 64) or (128, 128), bf16
+ *    gqa_attn_fwd_shard: (64, 64) or (128, 128), bf16 in, fp32 out + lse
  *    gqa_attn_decode:  (64, 64) or (128, 128), bf16 or fp32;
  *                      (576, 512) bf16 (the absorbed-MLA shape)
  *    gqa_attn_decode_topk: (576, 512) bf16
@@ -129,6 +130,48 @@ int gqa_attn_fwd_varlen(const void *q, const void *k, const void *v, void *out, 
                         int Dv, long long q_sh, long long q_st, long long k_sh, long long k_st, long long v_sh,
                         long long v_st, long long o_sh, long long o_st, float scale, int causal, int window,
                         int dtype, void *stream);
+
+/*
+ * Forward over one shard of the key axis, for sequence (context) parallelism:
+ * when one device cannot hold the context, each device keeps a slice of the
+ * keys and attends over it, and the partial results are merged exactly
+ * (Ring / Context Parallel in the causal-mainline section of the
+ * long-context research ledger page; the merge is the online-softmax
+ * rescaling of "A Visual Guide to Attention", section on sources and
+ * execution).
+ *
+ *   q   [B, Hq,  Tq, Dk] bf16, contiguous; query i sits at absolute position
+ *       q_pos0 + i
+ *   k   [B, Hkv, Tk, Dk] bf16, contiguous; key j of the shard sits at
+ *       absolute position k_pos0 + j
+ *   v   [B, Hkv, Tk, Dv] bf16, contiguous
+ *   out [B, Hq,  Tq, Dv] fp32: the softmax-normalised output over the
+ *       shard's visible keys (written in full)
+ *   lse [B, Hq,  Tq] fp32: natural log of the shard's softmax normaliser,
+ *       ln sum_j exp(scale * q.k_j); a query that sees no key of the shard
+ *       gets a zero row and lse = -inf
+ * causal = 1: key j is visible iff k_pos0 + j <= q_pos0 + i (any Tq, Tk);
+ * causal = 0: every key.  gqa_attn_merge combines the shards' (out, lse).
+ * Requirements: q_pos0, k_pos0 >= 0 and |q_pos0 - k_pos0| <= 2^30
+ * (else GQA_ERR_INVALID_ARG / GQA_ERR_UNSUPPORTED); q, k, v, out 16-byte
+ * aligned, lse 4.  bf16 only, (Dk, Dv) = (64, 64) or (128, 128).
+ */
+int gqa_attn_fwd_shard(const void *q, const void *k, const void *v, float *out, float *lse, int B,
+                       int Hq, int Hkv, int Tq, int Tk, int Dk, int Dv, long long q_pos0,
+                       long long k_pos0, float scale, int causal, int dtype, void *stream);
+
+/*
+ * Exact log-sum-exp merge of num_parts partial results of the same rows
+ * (e.g. the gathered outputs of gqa_attn_fwd_shard on every device):
+ *   L = ln sum_s exp(lse_s),   out = sum_s exp(lse_s - L) * o_s.
+ *   o_parts   fp32 [num_parts, rows, Dv], part-major, contiguous, 16-byte aligned
+ *   lse_parts fp32 [num_parts, rows], natural log; -inf marks an empty part
+ *   out       [rows, Dv], out_dtype GQA_BF16 (RNE) or GQA_F32
+ * A row whose parts are all empty gets zeros.  Dv a multiple of 4, at most
+ * 512; num_parts 1 .. 1024.
+ */
+int gqa_attn_merge(const float *o_parts, const float *lse_parts, void *out, int num_parts,
+                   long long rows, int Dv, int out_dtype, void *stream);
 
 /*
  * Split count the decode entry point uses when called with num_splits = 0.

@@ -200,3 +200,32 @@ def _f8(**kw):
 ])
 def test_decode_fp8_rejects_on_host(kw, code):
     assert _f8(**kw) == code
+
+
+def _shard(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, lse=FAKE, B=1, Hq=8, Hkv=2, Tq=64, Tk=64, Dk=128, Dv=128,
+             qp=100, kp=0, scale=0.1, causal=1, dtype=BF16)
+    a.update(kw)
+    return gqa.lib().gqa_attn_fwd_shard(a["q"], a["k"], a["v"], a["out"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                                        a["Tq"], a["Tk"], a["Dk"], a["Dv"], a["qp"], a["kp"], a["scale"],
+                                        a["causal"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=0), INVALID), (dict(lse=0), INVALID), (dict(out=0), INVALID), (dict(Tq=0), INVALID),
+    (dict(Tk=-1), INVALID), (dict(causal=3), INVALID), (dict(qp=-1), INVALID), (dict(kp=-5), INVALID),
+    (dict(out=FAKE + 8), INVALID), (dict(lse=FAKE + 2), INVALID), (dict(Hq=7), INVALID),
+    (dict(dtype=F32), UNSUP), (dict(Dk=96, Dv=96), UNSUP), (dict(qp=(1 << 31) + 5), UNSUP),
+])
+def test_fwd_shard_rejects_on_host(kw, code):
+    assert _shard(**kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, FAKE, FAKE, 2, 10, 128, BF16), INVALID), ((FAKE, FAKE, FAKE, 0, 10, 128, BF16), INVALID),
+    ((FAKE, FAKE, FAKE, 2, 0, 128, BF16), INVALID), ((FAKE, FAKE, FAKE, 2, 10, 128, 7), INVALID),
+    ((FAKE + 4, FAKE, FAKE, 2, 10, 128, BF16), INVALID), ((FAKE, FAKE, FAKE, 2, 10, 130, BF16), UNSUP),
+    ((FAKE, FAKE, FAKE, 2, 10, 1024, F32), UNSUP), ((FAKE, FAKE, FAKE, 2000, 10, 128, BF16), UNSUP),
+])
+def test_merge_rejects_on_host(args, code):
+    assert gqa.lib().gqa_attn_merge(*args, None) == code

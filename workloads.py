@@ -44,7 +44,7 @@ _DT = {"bf16": torch.bfloat16, "f32": torch.float32}
 @dataclass(frozen=True)
 class Workload:
     name: str
-    kind: str  # "fwd", "decode", "fp8_decode", "mla_decode", "mla_topk_decode", "fwd+decode", "fwd_varlen"
+    kind: str  # "fwd", "decode", "fp8_decode", "mla_decode", "mla_topk_decode", "fwd+decode", "fwd_varlen", "fwd_shard"
     B: int
     Hq: int
     Hkv: int
@@ -111,6 +111,14 @@ MLA_TOPK = Workload("mla_dsa_topk2048_decode_b16_hq128_tk32768_dk576_dv512", "ml
 # The GQA decode shape over an FP8 E4M3 cache with one scale per row.
 GQA_DECODE_FP8 = Workload("gqa_decode_fp8kv_b64_hq32_hkv8_tmax8192_d128", "fp8_decode", 64, 32, 8, 1, 8192, 128, 128,
                           "bf16", 7, 1.0 / math.sqrt(128), len_lo=1024, len_hi=8192)
+
+
+# One device's share of the MQA suffix shape under sequence (context)
+# parallelism over 8 devices: the 512 queries (positions 15872..16383) and
+# one 2048-key shard; Tk is the shard length.
+CP_SHARD = Workload("context_parallel_shard_mqa_b8_hq64_hkv1_tq512_tk2048_of_16384_d128", "fwd_shard", 8, 64, 1,
+                    512, 2048, 128, 128, "bf16", 8, 1.0 / math.sqrt(128),
+                    extra={"shards": 8, "q_pos0": 16384 - 512})
 
 
 def _randn(gen: torch.Generator, shape, dtype: str) -> torch.Tensor:
