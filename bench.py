@@ -345,6 +345,23 @@ def extra_workloads(torch, gqa, W, dev):
                    "TFLOP/s": round(f / sec / 1e12, 1), "splits": S}
     del q, kc, out, ws
 
+    # the GQA decode shape with a 4096-key sliding window (each query reads
+    # only the last min(len, 4096) keys of its full-length cache)
+    w, win = W.GQA_DECODE, 4096
+    q, kc, vc, lens = W.decode_inputs(w, nan_tail=False)
+    q, kc, vc, lens_d = q.to(dev), kc.to(dev), vc.to(dev), lens.to(dev)
+    out = torch.empty((w.B, w.Hq, 1, w.Dv), dtype=torch.bfloat16, device=dev)
+    S = gqa.decode_splits(w.B, w.Hq, w.Hkv, w.Tk, w.Dk, w.Dv, gqa.GQA_BF16)
+    ws = torch.empty(gqa.decode_workspace_size(w.B, w.Hq, w.Dv, S), dtype=torch.uint8, device=dev)
+    sec = _time(torch, lambda: gqa.decode(q, kc, vc, lens_d, scale=w.scale, num_splits=S, out=out, workspace=ws,
+                                          window=win))
+    wl = [min(n, win) for n in lens.tolist()]
+    b = decode_bytes(w, wl)
+    res["gqa_decode_swa_w4096_b64_hq32_hkv8_tmax8192_d128"] = {
+        "us": round(sec * 1e6, 1), "GB/s": round(b / sec / 1e9, 1), "frac_hbm_peak": round(b / sec / 1e9 / PEAK_HBM_GBPS, 4),
+        "window": win, "kv_bytes_per_launch": b}
+    del q, kc, vc, out, ws
+
     w = W.GQA_DECODE_FP8
     q, kc, vc, ks, vs, lens = W.fp8_decode_inputs(w, nan_tail=False)
     q, kc, vc, ks, vs, lens_d = (t.to(dev) for t in (q, kc, vc, ks, vs, lens))

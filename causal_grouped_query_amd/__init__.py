@@ -35,7 +35,8 @@ GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP
 
 EXPORTS = ("gqa_attn_fwd", "gqa_attn_fwd_varlen", "gqa_attn_decode", "gqa_attn_decode_splits",
            "gqa_attn_decode_workspace_size", "gqa_attn_decode_topk", "gqa_attn_decode_topk_splits",
-           "gqa_attn_decode_fp8", "gqa_attn_fwd_shard", "gqa_attn_merge", "gqa_attn_strerror")
+           "gqa_attn_decode_fp8", "gqa_attn_fwd_shard", "gqa_attn_merge", "gqa_attn_decode_window",
+           "gqa_attn_strerror")
 
 _lib = None
 
@@ -73,7 +74,10 @@ def lib() -> ctypes.CDLL:
         L.gqa_attn_decode_topk.restype = I
         L.gqa_attn_decode_topk.argtypes = [P, P, P, P, P, I, I, I, I, I, I, LL, LL, F, I, P, SZ, I, P]
         L.gqa_attn_decode_fp8.restype = I
-        L.gqa_attn_decode_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I] + [LL] * 12 + [F, I, P, SZ, P]
+        L.gqa_attn_decode_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I] + [LL] * 12 + [F, I, I, P, SZ, P]
+        L.gqa_attn_decode_window.restype = I
+        L.gqa_attn_decode_window.argtypes = [P, P, P, P, P, I, I, I, I, I, I, LL, LL, LL, LL, LL, LL, F, I, I, P,
+                                             SZ, I, P]
         L.gqa_attn_fwd_shard.restype = I
         L.gqa_attn_fwd_shard.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, LL, LL, F, I, I, P]
         L.gqa_attn_merge.restype = I
@@ -216,11 +220,12 @@ def decode_workspace_size(B: int, Hq: int, Dv: int, num_splits: int) -> int:
 
 
 def decode(q, k_cache, v_cache, seq_lens, scale: float | None = None, num_splits: int = 0, out=None,
-           workspace=None):
+           workspace=None, window: int = 0):
     """Single-token decode: q [B,Hq,1,Dk] over caches [B,Hkv,Tmax,D] holding seq_lens[b] keys.
 
     seq_lens: int32 device tensor [B].  Cache slots at or past seq_lens[b] are
     never read into the result.  num_splits = 0 lets the library choose.
+    window = w > 0: only the last min(seq_lens[b], w) keys (sliding window).
     """
     import torch
     _check_cuda(q, k_cache, v_cache, seq_lens)
@@ -253,12 +258,21 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float | None = None, num_splits
     elif out.shape != (B, Hq, 1, Dv) or out.dtype != q.dtype or not out.is_contiguous():
         raise ValueError("out must be a contiguous [B,Hq,1,Dv] tensor of q's dtype")
     ks, vs = k_cache.stride(), v_cache.stride()
-    rc = lib().gqa_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
-                               seq_lens.data_ptr(), B, Hq, Hkv, Tmax, Dk, Dv, ks[0], ks[1], ks[2], vs[0],
-                               vs[1], vs[2], float(scale), int(S), workspace.data_ptr(),
-                               workspace.numel() * workspace.element_size(), code, _stream())
+    if window:
+        rc = lib().gqa_attn_decode_window(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                                          seq_lens.data_ptr(), B, Hq, Hkv, Tmax, Dk, Dv, ks[0], ks[1], ks[2],
+                                          vs[0], vs[1], vs[2], float(scale), int(window), int(S),
+                                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                          code, _stream())
+        where = "gqa_attn_decode_window"
+    else:
+        rc = lib().gqa_attn_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                                   seq_lens.data_ptr(), B, Hq, Hkv, Tmax, Dk, Dv, ks[0], ks[1], ks[2], vs[0],
+                                   vs[1], vs[2], float(scale), int(S), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), code, _stream())
+        where = "gqa_attn_decode"
     if rc != GQA_OK:
-        raise GQAError(rc, "gqa_attn_decode")
+        raise GQAError(rc, where)
     return out
 
 
@@ -315,7 +329,7 @@ def decode_topk(q, kv_cache, seq_lens, indices, Dv: int = 512, scale: float | No
 
 
 def decode_fp8(q, k_codes, v_codes, k_scale, v_scale, seq_lens, scale: float | None = None, num_splits: int = 0,
-               out=None, workspace=None):
+               out=None, workspace=None, window: int = 0):
     """Single-token decode over an FP8 E4M3 cache: k_codes / v_codes
     [B,Hkv,Tmax,D] (uint8 or float8_e4m3fn storage, unit-stride last dim),
     k_scale / v_scale [B,Hkv,Tmax] float32 row scales; element (b,h,t,d)
@@ -356,7 +370,7 @@ def decode_fp8(q, k_codes, v_codes, k_scale, v_scale, seq_lens, scale: float | N
     rc = lib().gqa_attn_decode_fp8(q.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(), k_scale.data_ptr(),
                                    v_scale.data_ptr(), out.data_ptr(), seq_lens.data_ptr(), B, Hq, Hkv, Tmax, Dk,
                                    Dv, ks[0], ks[1], ks[2], vs[0], vs[1], vs[2], kss[0], kss[1], kss[2], vss[0],
-                                   vss[1], vss[2], float(scale), int(S), workspace.data_ptr(),
+                                   vss[1], vss[2], float(scale), int(window), int(S), workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), _stream())
     if rc != GQA_OK:
         raise GQAError(rc, "gqa_attn_decode_fp8")

@@ -412,10 +412,11 @@ GQA_API int gqa_attn_decode_fp8(const void *q, const void *k, const void *v, con
                                 int Hkv, int Tmax, int Dk, int Dv, long long k_sb, long long k_sh,
                                 long long k_st, long long v_sb, long long v_sh, long long v_st,
                                 long long ks_sb, long long ks_sh, long long ks_st, long long vs_sb,
-                                long long vs_sh, long long vs_st, float scale, int num_splits,
-                                void *workspace, size_t workspace_bytes, void *stream)
+                                long long vs_sh, long long vs_st, float scale, int window,
+                                int num_splits, void *workspace, size_t workspace_bytes, void *stream)
 {
     if (!q || !k || !v || !k_scale || !v_scale || !out || !seq_lens) return GQA_ERR_INVALID_ARG;
+    if (window < 0) return GQA_ERR_INVALID_ARG;
     int rc = check_common(B, Hq, Hkv, Dk, Dv, scale, GQA_BF16);
     if (rc != GQA_OK) return rc;
     if (Tmax <= 0) return GQA_ERR_INVALID_ARG;
@@ -473,6 +474,7 @@ GQA_API int gqa_attn_decode_fp8(const void *q, const void *k, const void *v, con
     a.vs_sb = vs_sb;
     a.vs_sh = vs_sh;
     a.vs_st = vs_st;
+    a.window = window;
     hipStream_t st = (hipStream_t)stream;
     (void)hipGetLastError();
     if (gqa::launch_decode_fp8(a, Dk, Dv, st) != 0) return GQA_ERR_UNSUPPORTED;
@@ -494,13 +496,14 @@ GQA_API size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_spl
     return ws_bytes(B, Hq, Dv, num_splits);
 }
 
-GQA_API int gqa_attn_decode(const void *q, const void *k, const void *v, void *out,
-                            const int *seq_lens, int B, int Hq, int Hkv, int Tmax, int Dk, int Dv,
-                            long long k_sb, long long k_sh, long long k_st, long long v_sb,
-                            long long v_sh, long long v_st, float scale, int num_splits,
-                            void *workspace, size_t workspace_bytes, int dtype, void *stream)
+static int decode_impl(const void *q, const void *k, const void *v, void *out, const int *seq_lens, int B,
+                       int Hq, int Hkv, int Tmax, int Dk, int Dv, long long k_sb, long long k_sh,
+                       long long k_st, long long v_sb, long long v_sh, long long v_st, float scale,
+                       int window, int num_splits, void *workspace, size_t workspace_bytes, int dtype,
+                       void *stream)
 {
     if (!q || !k || !v || !out || !seq_lens) return GQA_ERR_INVALID_ARG;
+    if (window < 0) return GQA_ERR_INVALID_ARG;
     int rc = check_common(B, Hq, Hkv, Dk, Dv, scale, dtype);
     if (rc != GQA_OK) return rc;
     if (Tmax <= 0) return GQA_ERR_INVALID_ARG;
@@ -530,7 +533,8 @@ GQA_API int gqa_attn_decode(const void *q, const void *k, const void *v, void *o
 
     const int G = Hq / Hkv;
     const int tile = dtype == GQA_BF16 ? gqa::decode_bf16_key_tile() : 64;
-    int chunk = (Tmax + S - 1) / S;
+    const int Teff = (window > 0 && window < Tmax) ? window : Tmax;  // keys any query can see
+    int chunk = (Teff + S - 1) / S;
     chunk = (chunk + tile - 1) / tile * tile;
 
     gqa::DecodeArgs a = {};
@@ -554,6 +558,7 @@ GQA_API int gqa_attn_decode(const void *q, const void *k, const void *v, void *o
     a.S = S;
     a.chunk = chunk;
     a.n_wg = 0;
+    a.window = window;
     hipStream_t st = (hipStream_t)stream;
 
     if (dtype == GQA_BF16) {
@@ -585,4 +590,25 @@ GQA_API int gqa_attn_decode(const void *q, const void *k, const void *v, void *o
     c.Dv = Dv;
     c.out_bf16 = dtype == GQA_BF16;
     return launch_status(gqa::launch_combine(c, st));
+}
+
+GQA_API int gqa_attn_decode(const void *q, const void *k, const void *v, void *out,
+                            const int *seq_lens, int B, int Hq, int Hkv, int Tmax, int Dk, int Dv,
+                            long long k_sb, long long k_sh, long long k_st, long long v_sb,
+                            long long v_sh, long long v_st, float scale, int num_splits,
+                            void *workspace, size_t workspace_bytes, int dtype, void *stream)
+{
+    return decode_impl(q, k, v, out, seq_lens, B, Hq, Hkv, Tmax, Dk, Dv, k_sb, k_sh, k_st, v_sb, v_sh, v_st,
+                       scale, 0, num_splits, workspace, workspace_bytes, dtype, stream);
+}
+
+GQA_API int gqa_attn_decode_window(const void *q, const void *k, const void *v, void *out,
+                                   const int *seq_lens, int B, int Hq, int Hkv, int Tmax, int Dk,
+                                   int Dv, long long k_sb, long long k_sh, long long k_st,
+                                   long long v_sb, long long v_sh, long long v_st, float scale,
+                                   int window, int num_splits, void *workspace,
+                                   size_t workspace_bytes, int dtype, void *stream)
+{
+    return decode_impl(q, k, v, out, seq_lens, B, Hq, Hkv, Tmax, Dk, Dv, k_sb, k_sh, k_st, v_sb, v_sh, v_st,
+                       scale, window, num_splits, workspace, workspace_bytes, dtype, stream);
 }

@@ -119,12 +119,17 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kern
 
     int len = p.lens[b];
     len = len < 0 ? 0 : (len > p.Tmax ? p.Tmax : len);
+    int kst = 0;  // sliding window: the last `window` keys only, rows kst ..
+    if (p.window > 0 && len > p.window) {
+        kst = len - p.window;
+        len = p.window;
+    }
     const int kbeg = split * p.chunk;
     const int kend = min(len, kbeg + p.chunk);
     const int ntiles = kend > kbeg ? (kend - kbeg + kTK - 1) / kTK : 0;
 
-    const uint16_t *kb = (const uint16_t *)p.k + (size_t)b * p.k_sb + (size_t)kvh * p.k_sh;
-    const uint16_t *vb = (const uint16_t *)p.v + (size_t)b * p.v_sb + (size_t)kvh * p.v_sh;
+    const uint16_t *kb = (const uint16_t *)p.k + (size_t)b * p.k_sb + (size_t)kvh * p.k_sh + (size_t)kst * p.k_st;
+    const uint16_t *vb = (const uint16_t *)p.v + (size_t)b * p.v_sb + (size_t)kvh * p.v_sh + (size_t)kst * p.v_st;
 
     // Async copy of keys [k0, k0 + 32) into ring slot `slot` (plane layout,
     // see PlaneTile); rows past the chunk end re-read its last key (in
@@ -332,10 +337,13 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
     const int lane = threadIdx.x;
     const int col = lane & 31, hi = lane >> 5;
     const int H = p.Hkv * p.n_hblk;  // streams per batch
-    auto ntile = [&](int len) {
+    // keys a sequence's query attends to: the clamped length, or with a
+    // sliding window its last `window` keys
+    auto eff_len = [&](int len) {
         len = len < 0 ? 0 : (len > p.Tmax ? p.Tmax : len);
-        return (len + kTK - 1) / kTK;
+        return (p.window > 0 && len > p.window) ? p.window : len;
     };
+    auto ntile = [&](int len) { return (eff_len(len) + kTK - 1) / kTK; };
 
     // ---- total tiles T and the longest stream (every workgroup computes them) ----
     long long tsum = 0;
@@ -384,7 +392,8 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
     // make the compiler drain the copy ring with vmcnt(0) on every tile)
     struct Cur {
         int b, s, u, n;    // n = tiles per stream of batch b
-        int len;           // clamped length of batch b
+        int len;           // keys batch b attends to (clamped, windowed)
+        int kst;           // cache row of its first key (window start)
         long long base;    // global index of batch b's first tile
         int lens64, chunk; // lengths of batches 64 chunk + lane (one per lane)
     };
@@ -395,6 +404,10 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
         return (long long)(((unsigned long long)hi32 << 32) | lo32);
     };
     auto clamp_len = [&](int len) { return len < 0 ? 0 : (len > p.Tmax ? p.Tmax : len); };
+    auto set_len = [&](Cur &c, int clamped) {  // window: the last `window` keys
+        c.len = (p.window > 0 && clamped > p.window) ? p.window : clamped;
+        c.kst = uni(clamped - c.len);
+    };
     auto locate = [&](long long t) {
         Cur c;
         long long base = 0;
@@ -419,7 +432,7 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
                 c.u = uni((int)(rel % c.n));
                 c.chunk = uni(b0 >> 6);
                 c.lens64 = b < p.B ? clamp_len(p.lens[b]) : 0;
-                c.len = __builtin_amdgcn_readlane(c.lens64, L);
+                set_len(c, __builtin_amdgcn_readlane(c.lens64, L));
                 return c;
             }
             base += __shfl(incl, 63);
@@ -435,13 +448,14 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
             c.b = uni(c.b + 1);
             if (c.b >= p.B) {  // past the last batch (only the copy cursor gets here)
                 c.len = kTK;
+                c.kst = 0;
             } else {
                 if ((c.b >> 6) != c.chunk) {  // next 64 batches: one vector load
                     c.chunk = c.b >> 6;
                     const int bb = 64 * c.chunk + lane;
                     c.lens64 = bb < p.B ? clamp_len(p.lens[bb]) : 0;
                 }
-                c.len = __builtin_amdgcn_readlane(c.lens64, c.b & 63);
+                set_len(c, __builtin_amdgcn_readlane(c.lens64, c.b & 63));
             }
             c.n = (c.len + kTK - 1) / kTK;
         } while (c.n == 0);
@@ -493,8 +507,8 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
         const int kvh = c.s / p.n_hblk;
         const int len = c.len;
         const int k0 = c.u * kTK;
-        const Elem *kb = (const Elem *)p.k + (size_t)c.b * p.k_sb + (size_t)kvh * p.k_sh;
-        const Elem *vb = (const Elem *)p.v + (size_t)c.b * p.v_sb + (size_t)kvh * p.v_sh;
+        const Elem *kb = (const Elem *)p.k + (size_t)c.b * p.k_sb + (size_t)kvh * p.k_sh + (size_t)c.kst * p.k_st;
+        const Elem *vb = (const Elem *)p.v + (size_t)c.b * p.v_sb + (size_t)kvh * p.v_sh + (size_t)c.kst * p.v_st;
         if (k0 + kTK <= len) {
             const Elem *k0p = kb + (size_t)k0 * p.k_st;
             const Elem *v0p = vb + (size_t)k0 * p.v_st;
@@ -521,7 +535,7 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
         if constexpr (F8) {
             // row scales: lanes 0-31 the keys', 32-63 the values' (rows past
             // the sequence end re-read its last row)
-            const int r = min(k0 + (lane & 31), len - 1);
+            const int r = c.kst + min(k0 + (lane & 31), len - 1);
             const float *sp = lane < 32
                 ? p.k_scale + (size_t)c.b * p.ks_sb + (size_t)kvh * p.ks_sh + (size_t)r * p.ks_st
                 : p.v_scale + (size_t)c.b * p.vs_sb + (size_t)kvh * p.vs_sh + (size_t)r * p.vs_st;

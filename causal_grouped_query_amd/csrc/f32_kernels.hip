@@ -106,11 +106,16 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs p)
     const int lane = threadIdx.x;
     int len = p.lens[b];
     len = len < 0 ? 0 : (len > p.Tmax ? p.Tmax : len);
+    int kst = 0;  // sliding window: the last `window` keys only, rows kst ..
+    if (p.window > 0 && len > p.window) {
+        kst = len - p.window;
+        len = p.window;
+    }
     const int kbeg = split * p.chunk;
     const int kend = min(len, kbeg + p.chunk);
     const float *qrow = (const float *)p.q + ((size_t)b * p.Hq + a) * D;
-    const float *kb = (const float *)p.k + (size_t)b * p.k_sb + (size_t)g * p.k_sh;
-    const float *vb = (const float *)p.v + (size_t)b * p.v_sb + (size_t)g * p.v_sh;
+    const float *kb = (const float *)p.k + (size_t)b * p.k_sb + (size_t)g * p.k_sh + (size_t)kst * p.k_st;
+    const float *vb = (const float *)p.v + (size_t)b * p.v_sb + (size_t)g * p.v_sh + (size_t)kst * p.v_st;
     // p.c carries the plain scale for the fp32 path
     float acc[2], m, l;
     attend_f32<D>(qrow, kb, p.k_st, vb, p.v_st, kbeg, kend, p.c, acc, m, l, sq, sk);

@@ -73,6 +73,9 @@ struct DecodeArgs {
     int fp8;
     const float *k_scale, *v_scale;
     long long ks_sb, ks_sh, ks_st, vs_sb, vs_sh, vs_st;
+    // sliding window (> 0): the query at position len - 1 sees only the
+    // last min(len, window) keys, rows len - that .. len - 1 of the cache
+    int window;
 };
 
 int launch_decode_bf16(const DecodeArgs &a, int Dk, int Dv, hipStream_t stream);

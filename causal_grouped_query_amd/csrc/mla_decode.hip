@@ -81,12 +81,17 @@ __global__ __launch_bounds__(kNT, 1) void mla_decode_kernel(DecodeArgs p)
 
     int len = p.lens[b];
     len = len < 0 ? 0 : (len > p.Tmax ? p.Tmax : len);
+    int kst = 0;  // dense with a sliding window: the last `window` keys, rows kst ..
+    if (!SPARSE && p.window > 0 && len > p.window) {
+        kst = len - p.window;
+        len = p.window;
+    }
     const int kbeg = split * p.chunk;
     // dense: cache positions [kbeg, kend); sparse: index-list entries
     const int kend = min(SPARSE ? p.topk : len, kbeg + p.chunk);
     int ntiles = kend > kbeg ? (kend - kbeg + kTK - 1) / kTK : 0;
 
-    const uint16_t *kb = (const uint16_t *)p.k + (size_t)b * p.k_sb + (size_t)kvh * p.k_sh;
+    const uint16_t *kb = (const uint16_t *)p.k + (size_t)b * p.k_sb + (size_t)kvh * p.k_sh + (size_t)kst * p.k_st;
 
     // sparse: copy entries [kbeg, kbeg + 32 ntiles) of the list to LDS
     // (addresses clamped into the list; what lies past kend is never used

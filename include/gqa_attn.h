@@ -247,6 +247,8 @@ int gqa_attn_decode(const void *q, const void *k, const void *v, void *out, cons
  *   out      [B, Hq, 1, Dv] bf16, contiguous
  *   seq_lens, workspace: as for gqa_attn_decode (workspace of
  *            gqa_attn_decode_workspace_size(B, Hq, Dv, splits) bytes)
+ *   window   0, or w >= 1: a sliding window as for gqa_attn_decode_window
+ *            (the last min(seq_lens[b], w) rows only)
  *   num_splits  0 (the value of gqa_attn_decode_splits(..., GQA_BF16)) or
  *            3 .. 1024: the bound on the pieces one sequence's keys are cut
  *            into by the balanced schedule; 1 and 2 return
@@ -261,7 +263,7 @@ int gqa_attn_decode_fp8(const void *q, const void *k, const void *v, const float
                         int Tmax, int Dk, int Dv, long long k_sb, long long k_sh, long long k_st,
                         long long v_sb, long long v_sh, long long v_st, long long ks_sb,
                         long long ks_sh, long long ks_st, long long vs_sb, long long vs_sh,
-                        long long vs_st, float scale, int num_splits, void *workspace,
+                        long long vs_st, float scale, int window, int num_splits, void *workspace,
                         size_t workspace_bytes, void *stream);
 
 /*
@@ -306,6 +308,24 @@ int gqa_attn_decode_topk(const void *q, const void *kv, void *out, const int *se
                          const int *indices, int B, int Hq, int Tmax, int topk, int Dk, int Dv,
                          long long kv_sb, long long kv_st, float scale, int num_splits,
                          void *workspace, size_t workspace_bytes, int dtype, void *stream);
+
+/*
+ * gqa_attn_decode with a sliding window ("A Visual Guide to Attention",
+ * section on which positions are visible: sliding-window attention keeps
+ * direct access to the most recent w positions; the "Attention variants"
+ * page lists sliding-window masks among those an implementation handles).
+ * window = w >= 1: the query of sequence b (position seq_lens[b] - 1) sees
+ * keys max(0, seq_lens[b] - w) .. seq_lens[b] - 1 of the cache (rows before
+ * them are never read); window = 0: no window (exactly gqa_attn_decode);
+ * window < 0: GQA_ERR_INVALID_ARG.  Every other argument, rule and
+ * supported shape as for gqa_attn_decode.  (A rolling cache that keeps only
+ * the last w rows needs no window: pass its fill level as seq_lens.)
+ */
+int gqa_attn_decode_window(const void *q, const void *k, const void *v, void *out,
+                           const int *seq_lens, int B, int Hq, int Hkv, int Tmax, int Dk, int Dv,
+                           long long k_sb, long long k_sh, long long k_st, long long v_sb,
+                           long long v_sh, long long v_st, float scale, int window, int num_splits,
+                           void *workspace, size_t workspace_bytes, int dtype, void *stream);
 
 /* Static, thread-safe description of a GQA_* return code. */
 const char *gqa_attn_strerror(int code);

@@ -181,12 +181,13 @@ def _f8(**kw):
     D, H, T = 128, 8, 64
     a = dict(q=FAKE, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE, out=FAKE, lens=FAKE, B=2, Hq=32, Hkv=H, Tmax=T, Dk=D, Dv=D,
              ksb=H * T * D, ksh=T * D, kst=D, vsb=H * T * D, vsh=T * D, vst=D, ssb=H * T, ssh=T, sst=1,
-             tsb=H * T, tsh=T, tst=1, scale=0.1, S=0, ws=FAKE, wsb=1 << 30)
+             tsb=H * T, tsh=T, tst=1, scale=0.1, win=0, S=0, ws=FAKE, wsb=1 << 30)
     a.update(kw)
     return gqa.lib().gqa_attn_decode_fp8(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["out"], a["lens"], a["B"],
                                          a["Hq"], a["Hkv"], a["Tmax"], a["Dk"], a["Dv"], a["ksb"], a["ksh"], a["kst"],
                                          a["vsb"], a["vsh"], a["vst"], a["ssb"], a["ssh"], a["sst"], a["tsb"],
-                                         a["tsh"], a["tst"], a["scale"], a["S"], a["ws"], a["wsb"], None)
+                                         a["tsh"], a["tst"], a["scale"], a["win"], a["S"], a["ws"], a["wsb"],
+                                         None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -194,7 +195,7 @@ def _f8(**kw):
     (dict(lens=0), INVALID), (dict(Hq=30), INVALID), (dict(Tmax=0), INVALID), (dict(kst=120), INVALID),
     (dict(kst=64), INVALID), (dict(vsh=8), INVALID), (dict(sst=0), INVALID), (dict(tsh=-1), INVALID),
     (dict(S=1), INVALID), (dict(S=2), INVALID), (dict(S=1025), INVALID), (dict(ks=FAKE + 2), INVALID),
-    (dict(k=FAKE + 8), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(k=FAKE + 8), INVALID), (dict(scale=float("nan")), INVALID), (dict(win=-1), INVALID),
     (dict(Dk=96, Dv=96), UNSUP), (dict(Dk=128, Dv=64), UNSUP), (dict(kst=1 << 26), UNSUP),
     (dict(ws=0), WS), (dict(wsb=4096), WS),
 ])
@@ -229,3 +230,12 @@ def test_fwd_shard_rejects_on_host(kw, code):
 ])
 def test_merge_rejects_on_host(args, code):
     assert gqa.lib().gqa_attn_merge(*args, None) == code
+
+
+def test_decode_window_rejects_on_host():
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 64, 128, 128, 2 * 64 * 128, 64 * 128, 128, 2 * 64 * 128,
+            64 * 128, 128, 0.1]
+    L = gqa.lib()
+    assert L.gqa_attn_decode_window(*args, -1, 0, FAKE, 1 << 30, BF16, None) == INVALID
+    assert L.gqa_attn_decode_window(*args, 4, 0, 0, 1 << 30, BF16, None) == WS
+    assert L.gqa_attn_decode_window(*(args[:9] + [96, 96] + args[11:]), 4, 0, FAKE, 1 << 30, BF16, None) == UNSUP
