@@ -300,6 +300,12 @@ GQA_API int gqa_attn_merge(const float *o_parts, const float *lse_parts, void *o
     m.S = num_parts;
     m.Dv = Dv;
     m.out_bf16 = out_dtype == GQA_BF16;
+    // gathered partials, part-major: o [S, rows, Dv], lse [S, rows], natural log
+    m.o_rs = Dv;
+    m.o_ss = rows * Dv;
+    m.l_rs = 1;
+    m.l_ss = rows;
+    m.lse_mul = 1.4426950408889634f;  // log2(e)
     (void)hipGetLastError();
     return launch_status(gqa::launch_merge(m, (hipStream_t)stream));
 }

@@ -80,9 +80,10 @@ __global__ __launch_bounds__(kMT) void merge_kernel(MergeArgs p)
     if (t >= p.rows * per_row) return;
     const long long row = t / per_row;
     const int d0 = (int)(t - row * per_row) * 4;
-    constexpr float kLog2e = 1.4426950408889634f;
+    const float *lr = p.lse + row * p.l_rs;
+    const float *orow = p.o + row * p.o_rs + d0;
     float L = -INFINITY;
-    for (int s = 0; s < p.S; ++s) L = fmaxf(L, p.lse[(size_t)s * p.rows + row] * kLog2e);
+    for (int s = 0; s < p.S; ++s) L = fmaxf(L, lr[(size_t)s * p.l_ss] * p.lse_mul);
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     if (L != -INFINITY) {
@@ -91,8 +92,8 @@ __global__ __launch_bounds__(kMT) void merge_kernel(MergeArgs p)
         // (its slot is in bounds) but selected away, whatever it holds
 #pragma unroll 8
         for (int s = 0; s < p.S; ++s) {
-            const float w = __builtin_amdgcn_exp2f(p.lse[(size_t)s * p.rows + row] * kLog2e - L);
-            const float4 v = *(const float4 *)(p.o + ((size_t)s * p.rows + row) * p.Dv + d0);
+            const float w = __builtin_amdgcn_exp2f(lr[(size_t)s * p.l_ss] * p.lse_mul - L);
+            const float4 v = *(const float4 *)(orow + (size_t)s * p.o_ss);
             const bool use = w != 0.f;
             wsum += w;
             acc[0] = use ? fmaf(w, v.x, acc[0]) : acc[0];

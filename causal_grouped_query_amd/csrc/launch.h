@@ -112,14 +112,19 @@ struct CombineArgs {
 };
 int launch_combine(const CombineArgs &a, hipStream_t stream);
 
-// Exact LSE merge of S gathered partial results (part-major, natural-log LSE).
+// Exact LSE merge of S partial results of `rows` rows: part s of row r has
+// its output at o + r*o_rs + s*o_ss (Dv fp32) and its lse at
+// lse + r*l_rs + s*l_ss, natural log times lse_mul = log2(e), or base 2
+// with lse_mul = 1.
 struct MergeArgs {
-    const float *o;    // [S, rows, Dv]
-    const float *lse;  // [S, rows]
+    const float *o;
+    const float *lse;
     void *out;         // [rows, Dv], bf16 or fp32
     long long rows;
     int S, Dv;
     int out_bf16;
+    long long o_rs, o_ss, l_rs, l_ss;
+    float lse_mul;
 };
 int launch_merge(const MergeArgs &a, hipStream_t stream);
 
