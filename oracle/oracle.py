@@ -9,7 +9,14 @@ The oracle computes the dense softmax attention of the unified formula
 o_a = softmax(Q_a K_{g(a)}^T * scale + M) V_{g(a)} ("Attention variants"
 page, unified-notation section), row by row in fp64, with the query position
 offset Tk - Tq of that page's minimal semantic implementation.  See the header
-of gqa_oracle.c for the step list.
+of gqa_oracle.c for the step list.  Around that one definition:
+
+  attention / probs       dense, causal or not, decode lengths, sliding window
+  attention_varlen        packed sequences (cu_seqlens), padding (seqused)
+  attention_e4m3kv        an FP8 E4M3 cache with one scale per row
+  attention_shard         one key shard at absolute positions (partial + lse)
+  decode_topk             DSA top-k selection on the absorbed MLA cache
+  lse_merge               exact merge of partial results
 """
 from __future__ import annotations
 
