@@ -104,3 +104,16 @@ def test_context_parallel_shards_merge_to_full_attention(nshard):
     ref = O.attention(q, k, v, 1.0 / np.sqrt(D), True, rows=rows)
     got = merged.reshape(B * Hq * T, D)[rows]
     _check(got, ref, f"context parallel, {nshard} shards")
+
+
+@pytest.mark.parametrize("Dv,S", [(512, 3), (64, 9), (128, 1)])
+def test_merge_other_widths(Dv, S):
+    rows = 257
+    g = torch.Generator("cpu").manual_seed(540 + Dv)
+    o = torch.randn(S, rows, Dv, generator=g)
+    lse = torch.randn(S, rows, generator=g) * 3
+    if S > 1:
+        lse[0, 5:9] = -float("inf")
+    ref, _ = O.lse_merge(o.numpy().astype(np.float64), lse.numpy().astype(np.float64))
+    out = gqa.merge(o.cuda(), lse.cuda(), out_dtype=torch.float32)
+    _check(out, ref, f"merge Dv={Dv} S={S}", tmax=1e-5, tmean=1e-6)

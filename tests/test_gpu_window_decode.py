@@ -54,17 +54,17 @@ def test_window_decode_bf16(window, splits):
     _check(out, ref, f"window decode bf16 w={window} S={splits}", 2e-2, 2e-3)
 
 
-@pytest.mark.parametrize("window", [3, 50, 1000])
-def test_window_decode_f32_d64(window):
-    B, Hq, Hkv, T, D = len(LENS), 8, 2, 700, 64
+@pytest.mark.parametrize("window,D", [(3, 64), (50, 64), (1000, 64), (40, 128)])
+def test_window_decode_f32(window, D):
+    B, Hq, Hkv, T = len(LENS), 8, 2, 700
     q = _rand((B, Hq, 1, D), 610, torch.float32)
     k = _rand((B, Hkv, T, D), 611, torch.float32)
     v = _rand((B, Hkv, T, D), 612, torch.float32)
-    ref = O.attention(q, k, v, 0.125, True, kv_lens=LENS, window=window)
+    ref = O.attention(q, k, v, 1.0 / np.sqrt(D), True, kv_lens=LENS, window=window)
     _nan_outside_window(k, LENS, window)
     _nan_outside_window(v, LENS, window)
-    out = gqa.decode(q.cuda(), k.cuda(), v.cuda(), torch.tensor(LENS, dtype=torch.int32).cuda(), scale=0.125,
-                     window=window)
+    out = gqa.decode(q.cuda(), k.cuda(), v.cuda(), torch.tensor(LENS, dtype=torch.int32).cuda(),
+                     scale=1.0 / np.sqrt(D), window=window)
     _check(out, ref, f"window decode fp32 w={window}", 1e-5, 1e-5)
 
 
