@@ -225,3 +225,29 @@ def test_varlen_padding_equals_packed():
     cp = torch.tensor([0] + np.cumsum(lens).tolist(), dtype=torch.int32, device="cuda")
     packed = gqa.attention_varlen(q[idx], k[idx], v[idx], cp, cp, causal=True, window=33)
     assert torch.equal(pad[idx], packed)
+
+
+def test_multi_token_decode_over_padded_cache():
+    """Incremental decode with several new tokens per sequence (the query
+    count differs from the cache length, as the masks section of the
+    "Attention variants" page calls out): a [B, Tmax, Hkv, D] cache with
+    per-sequence fill levels, 4 queries per sequence at its last positions,
+    expressed as packed slots (cu_seqlens = multiples of Tmax) with used
+    lengths."""
+    B, Tmax, Hq, Hkv, D, nq = 5, 600, 32, 8, 128, 4
+    lens = [600, 4, 257, 31, 100]
+    q = _rand((B * nq, Hq, D), 700)
+    kc = _rand((B, Tmax, Hkv, D), 701)
+    vc = _rand((B, Tmax, Hkv, D), 702)
+    for b, n in enumerate(lens):
+        kc[b, n:] = float("nan")
+        vc[b, n:] = float("nan")
+    cu_q = torch.arange(0, (B + 1) * nq, nq, dtype=torch.int32)
+    cu_k = torch.arange(0, (B + 1) * Tmax, Tmax, dtype=torch.int32)
+    used_k = torch.tensor(lens, dtype=torch.int32)
+    out = gqa.attention_varlen(q.cuda(), kc.reshape(B * Tmax, Hkv, D).cuda(), vc.reshape(B * Tmax, Hkv, D).cuda(),
+                               cu_q.cuda(), cu_k.cuda(), causal=True, seqused_k=used_k.cuda())
+    kflat, vflat = kc.reshape(B * Tmax, Hkv, D), vc.reshape(B * Tmax, Hkv, D)
+    ref = O.attention_varlen(q, kflat, vflat, cu_q.tolist(), cu_k.tolist(), 1.0 / np.sqrt(D), True,
+                             seqused_k=lens)
+    _check(out, ref, "multi-token decode, padded cache")
