@@ -197,6 +197,27 @@ __device__ __forceinline__ void g2lds16(const void *uniform_base, unsigned byte_
                  : "memory");
 }
 
+// Same copy with the LDS destination given as a workgroup-uniform LDS byte
+// address (no generic-pointer round trip, whose null check costs scalar
+// instructions per copy).
+__device__ __forceinline__ void g2lds16_at(const void *uniform_base, unsigned byte_off, unsigned lds_addr)
+{
+    const unsigned long long a = (unsigned long long)uniform_base;
+    const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+    const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+    const unsigned long long base = ((unsigned long long)hi << 32) | lo;
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(byte_off), "s"(base),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "memory");
+}
+
+__device__ __forceinline__ void g2lds16_at(const void *gptr, unsigned lds_addr)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+                 "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                 : "memory");
+}
+
 // Complete a register's pending global load here: the compiler waits for it
 // before an asm statement that reads the register.  Without this, a value
 // loaded before a loop whose copies are issued as inline assembly can leave a

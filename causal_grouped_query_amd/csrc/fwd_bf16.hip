@@ -108,6 +108,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
     constexpr int NINS = kBN * CPR / kThreads;     // async copies per thread per tensor
     constexpr int ROWS = 32 * kNC;                 // query rows per wave
     static_assert(kBN * CPR % kThreads == 0, "tile must split evenly over the workgroup");
+    static_assert(offsetof(FwdSmem<D>, v) == kStages * FwdSmem<D>::TILE * 2, "V ring follows the K ring");
     using Tile = PlaneTile<kBN>;
 
     __shared__ __attribute__((aligned(1024))) FwdSmem<D> sm;
@@ -225,23 +226,27 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
         goff_[j] = (unsigned)(row * krs + chunk * 8) * 2u;
         gvoff_[j] = VAR ? (unsigned)(row * vrs + chunk * 8) * 2u : goff_[j];
     }
-    auto issue = [&](const uint16_t *src, uint16_t *dst, int k0, const unsigned (&offs)[NINS], long long rs) {
+    // LDS byte address of this wave's first slot in K ring slot 0 (V slots
+    // follow the K slots)
+    const unsigned ring_lds = lds_u32(&sm) + (unsigned)(w * 64 * 16);
+    constexpr unsigned kTileBytes = FwdSmem<D>::TILE * 2u;
+    auto issue = [&](const uint16_t *src, unsigned dst, int k0, const unsigned (&offs)[NINS], long long rs) {
         if (k0 + kBN <= Tk) {
             const uint16_t *s0 = src + (size_t)k0 * rs;
 #pragma unroll
-            for (int j = 0; j < NINS; ++j) g2lds16(s0, offs[j], dst + (j * kNW + w) * 64 * 8);
+            for (int j = 0; j < NINS; ++j) g2lds16_at(s0, offs[j], dst + (unsigned)(j * kNW * 64 * 16));
         } else {
 #pragma unroll
             for (int j = 0; j < NINS; ++j) {
                 const int row = min(k0 + grow_[j], Tk - 1);
-                g2lds16((const char *)(src + (size_t)row * rs) + (offs[j] - (unsigned)(grow_[j] * rs) * 2u),
-                        dst + (j * kNW + w) * 64 * 8);
+                g2lds16_at((const char *)(src + (size_t)row * rs) + (offs[j] - (unsigned)(grow_[j] * rs) * 2u),
+                           dst + (unsigned)(j * kNW * 64 * 16));
             }
         }
     };
     auto issue_kv = [&](int j, int slot) {  // tile t0 + j of the workgroup into ring slot `slot`
-        issue(kbase, sm.k[slot], (t0 + j) * kBN, goff_, krs);
-        issue(vbase, sm.v[slot], (t0 + j) * kBN, gvoff_, vrs);
+        issue(kbase, ring_lds + (unsigned)slot * kTileBytes, (t0 + j) * kBN, goff_, krs);
+        issue(vbase, ring_lds + (unsigned)(kStages + slot) * kTileBytes, (t0 + j) * kBN, gvoff_, vrs);
     };
 
     // ---- Q^T in registers (B operands), zero for rows past Tq ----
