@@ -410,6 +410,7 @@ GQA_API int gqa_attn_decode_topk(const void *q, const void *kv, void *out, const
     c.S = S;
     c.Dv = Dv;
     c.out_bf16 = 1;
+    c.part_bf16 = 1;
     return launch_status(gqa::launch_combine(c, st));
 }
 
@@ -493,6 +494,7 @@ GQA_API int gqa_attn_decode_fp8(const void *q, const void *k, const void *v, con
     c.S = S;
     c.Dv = Dv;
     c.out_bf16 = 1;
+    c.part_bf16 = 1;
     return launch_status(gqa::launch_combine(c, st));
 }
 
@@ -595,6 +597,7 @@ static int decode_impl(const void *q, const void *k, const void *v, void *out, c
     c.S = S;
     c.Dv = Dv;
     c.out_bf16 = dtype == GQA_BF16;
+    c.part_bf16 = dtype == GQA_BF16;  // the bf16 and fp8 kernels store bf16 partials, the fp32 kernel fp32
     return launch_status(gqa::launch_combine(c, st));
 }
 

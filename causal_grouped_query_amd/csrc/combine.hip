@@ -7,56 +7,75 @@
 //     L = log2 sum_s 2^{lse_s},   o = sum_s 2^{lse_s - L} o_s,
 // the same merge online softmax applies tile by tile ("A Visual Guide to
 // Attention", section on sources and execution).  Empty chunks carry
-// lse = -inf and weigh nothing (their partial outputs are not even read);
-// a row with no keys at all yields zeros.
+// lse = -inf and weigh nothing (their partial outputs are loaded but
+// selected away, whatever they hold); a row with no keys at all yields
+// zeros.  Partial outputs are bf16 (from the bf16 and fp8 kernels) or fp32
+// (from the fp32 kernel); the merge accumulates in fp32.
 #include "launch.h"
 
 namespace gqa {
 
 namespace {
 
-constexpr int kCT = 128;  // threads per row; each owns 4 output dims
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <bool OUT_BF16>
+constexpr int kCT = 128;  // threads per row at most; each owns 4 output dims
+constexpr int kCB = 16;   // partial outputs loaded together before any is used
+
+// Latency, not bandwidth, bounds this pass (a few MB in total), so every
+// load is issued before its value is needed: one round trip for the row's
+// lse values (lane s holds split s), one per batch of kCB partial outputs
+// (unconditional loads of in-bounds slots; slots past the split count and
+// empty slots get weight 0 and are selected away, whatever they hold).
+template <bool OUT_BF16, bool PART_BF16>
 __global__ __launch_bounds__(kCT) void combine_kernel(CombineArgs p)
 {
+    using PT = typename std::conditional<PART_BF16, __bf16, float>::type;
+    using PT4 = typename std::conditional<PART_BF16, bf16x4, f32x4>::type;
     const size_t row = blockIdx.x;  // b * Hq + head
     const float *lse = p.part_lse + row * p.S;
-    const float *po = p.part_o + row * (size_t)p.S * p.Dv;
+    const PT *po = (const PT *)p.part_o + row * (size_t)p.S * p.Dv;
     const int ns = p.S;
-
-    // lane s of each wave holds split s (chunks of 64): max, then weights
     const int lane = threadIdx.x & 63;
-    float L = -INFINITY;
-    for (int s0 = 0; s0 < ns; s0 += 64) L = fmaxf(L, s0 + lane < ns ? lse[s0 + lane] : -INFINITY);
+    const int dim = threadIdx.x * 4;
+    const int d0 = min(dim, p.Dv - 4);  // lanes past Dv mirror the last dims and store nothing
+
+    float ll = lane < ns ? lse[lane] : -INFINITY;
+    float L = ll;
+    for (int s0 = 64; s0 < ns; s0 += 64) L = fmaxf(L, s0 + lane < ns ? lse[s0 + lane] : -INFINITY);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) L = fmaxf(L, __shfl_xor(L, o));
-    const int d0 = threadIdx.x * 4;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     if (L != -INFINITY) {
         for (int s0 = 0; s0 < ns; s0 += 64) {
-            const float wl = s0 + lane < ns ? __builtin_amdgcn_exp2f(lse[s0 + lane] - L) : 0.f;
+            if (s0 > 0) ll = s0 + lane < ns ? lse[s0 + lane] : -INFINITY;
+            const float wl = __builtin_amdgcn_exp2f(ll - L);  // 0 for lse = -inf
             const int n = min(64, ns - s0);
-#pragma unroll 4
-            for (int s = 0; s < n; ++s) {
-                const float w = __shfl(wl, s);
-                wsum += w;
-                if (w != 0.f && d0 < p.Dv) {  // empty slots (lse = -inf) are never read
-                    const float4 v = *(const float4 *)(po + (size_t)(s0 + s) * p.Dv + d0);
-                    acc[0] = fmaf(w, v.x, acc[0]);
-                    acc[1] = fmaf(w, v.y, acc[1]);
-                    acc[2] = fmaf(w, v.z, acc[2]);
-                    acc[3] = fmaf(w, v.w, acc[3]);
+            for (int sb = 0; sb < n; sb += kCB) {
+                PT4 v[kCB];
+#pragma unroll
+                for (int i = 0; i < kCB; ++i)
+                    v[i] = *(const PT4 *)(po + (size_t)(s0 + min(sb + i, n - 1)) * p.Dv + d0);
+#pragma unroll
+                for (int i = 0; i < kCB; ++i) {
+                    const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), min(sb + i, 63)));
+                    const float w = sb + i < n ? wi : 0.f;
+                    const bool use = w != 0.f;
+                    wsum += w;
+                    acc[0] = use ? fmaf(w, (float)v[i][0], acc[0]) : acc[0];
+                    acc[1] = use ? fmaf(w, (float)v[i][1], acc[1]) : acc[1];
+                    acc[2] = use ? fmaf(w, (float)v[i][2], acc[2]) : acc[2];
+                    acc[3] = use ? fmaf(w, (float)v[i][3], acc[3]) : acc[3];
                 }
             }
         }
     }
-    if (d0 >= p.Dv) return;
+    if (dim >= p.Dv) return;
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     if (OUT_BF16) {
         uint16_t *out = (uint16_t *)p.out + row * p.Dv + d0;
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         bf16x4 r = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv), (__bf16)(acc[2] * inv),
                     (__bf16)(acc[3] * inv)};
         *(bf16x4 *)out = r;
@@ -104,7 +123,6 @@ __global__ __launch_bounds__(kMT) void merge_kernel(MergeArgs p)
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
     if (OUT_BF16) {
-        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
         bf16x4 r = {(__bf16)(acc[0] * inv), (__bf16)(acc[1] * inv), (__bf16)(acc[2] * inv),
                     (__bf16)(acc[3] * inv)};
         *(bf16x4 *)((uint16_t *)p.out + row * p.Dv + d0) = r;
@@ -132,12 +150,16 @@ int launch_merge(const MergeArgs &a, hipStream_t stream)
 
 int launch_combine(const CombineArgs &a, hipStream_t stream)
 {
-    if (a.Dv % 4 != 0 || a.Dv > 4 * kCT) return -1;
-    dim3 grid((unsigned)((size_t)a.B * a.Hq)), block(kCT);
-    if (a.out_bf16)
-        hipLaunchKernelGGL(combine_kernel<true>, grid, block, 0, stream, a);
+    if (a.Dv % 4 != 0 || a.Dv <= 0 || a.Dv > 4 * kCT || a.S <= 0) return -1;
+    dim3 grid((unsigned)((size_t)a.B * a.Hq)), block((a.Dv / 4 + 63) / 64 * 64);  // whole waves
+    if (a.part_bf16 && a.out_bf16)
+        hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, stream, a);
+    else if (a.part_bf16)
+        hipLaunchKernelGGL((combine_kernel<false, true>), grid, block, 0, stream, a);
+    else if (a.out_bf16)
+        hipLaunchKernelGGL((combine_kernel<true, false>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL(combine_kernel<false>, grid, block, 0, stream, a);
+        hipLaunchKernelGGL((combine_kernel<false, false>), grid, block, 0, stream, a);
     return 0;
 }
 

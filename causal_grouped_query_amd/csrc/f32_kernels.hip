@@ -120,7 +120,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs p)
     float acc[2], m, l;
     attend_f32<D>(qrow, kb, p.k_st, vb, p.v_st, kbeg, kend, p.c, acc, m, l, sq, sk);
     const size_t prow = ((size_t)b * p.Hq + a) * p.S + split;
-    float *po = p.part_o + prow * D;
+    float *po = (float *)p.part_o + prow * D;
     const float inv = l > 0.f ? 1.f / l : 0.f;
     po[lane] = acc[0] * inv;
     if (D > 64) po[lane + 64] = acc[1] * inv;

@@ -53,7 +53,8 @@ struct DecodeArgs {
     const void *k;       // cache, element strides below
     const void *v;
     const int *lens;     // device int32 [B]
-    float *part_o;       // [B, Hq, S, Dv] fp32, normalised partial outputs
+    void *part_o;        // [B, Hq, S, Dv] normalised partial outputs: bf16 from the
+                         // bf16 / fp8 kernels, fp32 from the fp32 kernel
     float *part_lse;     // [B, Hq, S] fp32, base-2 log-sum-exp of scaled scores
     int B, Hq, Hkv, Tmax, G;
     long long k_sb, k_sh, k_st;
@@ -104,11 +105,12 @@ int launch_decode_f32(const DecodeArgs &a, int D, hipStream_t stream);
 
 // Log-sum-exp combine of the decode partials into the output.
 struct CombineArgs {
-    const float *part_o;
+    const void *part_o;  // bf16 when part_bf16, else fp32
     const float *part_lse;
     void *out;           // [B, Hq, 1, Dv], bf16 or fp32
     int B, Hq, S, Dv;
     int out_bf16;
+    int part_bf16;
 };
 int launch_combine(const CombineArgs &a, hipStream_t stream);
 

@@ -268,11 +268,14 @@ __global__ __launch_bounds__(kNT, 1) void mla_decode_kernel(DecodeArgs p)
     if (!head_ok) return;
     const float l_tot = quarters_sum(l_run);
     const size_t prow = ((size_t)b * p.Hq + head) * p.S + split;
-    float *po = p.part_o + prow * kDV + 4 * g;
+    __bf16 *po = (__bf16 *)p.part_o + prow * kDV + 4 * g;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     // element i of o[db]: output dim 16 db + 4 g + i, head r16
 #pragma unroll
-    for (int db = 0; db < kDB; ++db) *(f32x4 *)(po + 16 * db) = o[db] * inv;
+    for (int db = 0; db < kDB; ++db) {
+        const f32x4 r = o[db] * inv;
+        *(bf16x4 *)(po + 16 * db) = bf16x4{(__bf16)r[0], (__bf16)r[1], (__bf16)r[2], (__bf16)r[3]};
+    }
     if (g == 0) p.part_lse[prow] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
 }
 

@@ -183,8 +183,10 @@ int gqa_attn_decode_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int Dv, int
 
 /*
  * Bytes of device workspace gqa_attn_decode needs for num_splits splits
- * (num_splits >= 1): fp32 partial outputs [B, Hq, S, Dv] and fp32 partial
- * log-sum-exp values [B, Hq, S].  Returns 0 for invalid arguments.
+ * (num_splits >= 1): room for fp32 partial outputs [B, Hq, S, Dv] followed
+ * by fp32 partial log-sum-exp values [B, Hq, S].  The bf16 and fp8 paths
+ * store their partial outputs as bf16 in the first half of the output area;
+ * the fp32 path uses all of it.  Returns 0 for invalid arguments.
  */
 size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_splits);
 
