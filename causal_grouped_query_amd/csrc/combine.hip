@@ -94,6 +94,7 @@ constexpr int kMT = 256;  // threads per merge workgroup
 template <bool OUT_BF16>
 __global__ __launch_bounds__(kMT) void merge_kernel(MergeArgs p)
 {
+    constexpr int kB = 8;  // parts whose loads are in flight together
     const int per_row = p.Dv / 4;
     const long long t = (long long)blockIdx.x * kMT + threadIdx.x;
     if (t >= p.rows * per_row) return;
@@ -101,24 +102,41 @@ __global__ __launch_bounds__(kMT) void merge_kernel(MergeArgs p)
     const int d0 = (int)(t - row * per_row) * 4;
     const float *lr = p.lse + row * p.l_rs;
     const float *orow = p.o + row * p.o_rs + d0;
+    // Batches of kB parts with the part index clamped to the last one, so
+    // every load is unconditional and in bounds (a repeated part does not
+    // change the max, and gets weight 0 below); each batch is one round trip.
     float L = -INFINITY;
-    for (int s = 0; s < p.S; ++s) L = fmaxf(L, lr[(size_t)s * p.l_ss] * p.lse_mul);
+    for (int s0 = 0; s0 < p.S; s0 += kB) {
+        float l[kB];
+#pragma unroll
+        for (int i = 0; i < kB; ++i) l[i] = lr[(size_t)min(s0 + i, p.S - 1) * p.l_ss];
+#pragma unroll
+        for (int i = 0; i < kB; ++i) L = fmaxf(L, l[i] * p.lse_mul);
+    }
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     float wsum = 0.f;
     if (L != -INFINITY) {
-        // no data-dependent branch, so the loads of consecutive parts are in
-        // flight together; an empty part (weight 0: lse = -inf) is loaded
-        // (its slot is in bounds) but selected away, whatever it holds
-#pragma unroll 8
-        for (int s = 0; s < p.S; ++s) {
-            const float w = __builtin_amdgcn_exp2f(lr[(size_t)s * p.l_ss] * p.lse_mul - L);
-            const float4 v = *(const float4 *)(orow + (size_t)s * p.o_ss);
-            const bool use = w != 0.f;
-            wsum += w;
-            acc[0] = use ? fmaf(w, v.x, acc[0]) : acc[0];
-            acc[1] = use ? fmaf(w, v.y, acc[1]) : acc[1];
-            acc[2] = use ? fmaf(w, v.z, acc[2]) : acc[2];
-            acc[3] = use ? fmaf(w, v.w, acc[3]) : acc[3];
+        for (int s0 = 0; s0 < p.S; s0 += kB) {
+            float l[kB];
+            f32x4 v[kB];
+#pragma unroll
+            for (int i = 0; i < kB; ++i) {
+                const size_t s = (size_t)min(s0 + i, p.S - 1);
+                l[i] = lr[s * p.l_ss];
+                v[i] = *(const f32x4 *)(orow + s * p.o_ss);
+            }
+            // an empty part (weight 0: lse = -inf) is selected away, whatever
+            // its output holds
+#pragma unroll
+            for (int i = 0; i < kB; ++i) {
+                const float w = s0 + i < p.S ? __builtin_amdgcn_exp2f(l[i] * p.lse_mul - L) : 0.f;
+                const bool use = w != 0.f;
+                wsum += w;
+                acc[0] = use ? fmaf(w, v[i][0], acc[0]) : acc[0];
+                acc[1] = use ? fmaf(w, v[i][1], acc[1]) : acc[1];
+                acc[2] = use ? fmaf(w, v[i][2], acc[2]) : acc[2];
+                acc[3] = use ? fmaf(w, v[i][3], acc[3]) : acc[3];
+            }
         }
     }
     const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
