@@ -91,7 +91,9 @@ int default_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int dtype)
     return (int)s;
 }
 
-// workspace: fp32 partial outputs [B, Hq, S, Dv], fp32 partial log2-sum-exp [B, Hq, S]
+// workspace: room for fp32 partial outputs [B, Hq, S, Dv] (the bf16 and fp8
+// paths store bf16 partials in its first half), then fp32 partial
+// log2-sum-exp [B, Hq, S]
 size_t ws_bytes(int B, int Hq, int Dv, int S)
 {
     const size_t rows = (size_t)B * Hq * S;
