@@ -2,7 +2,9 @@
 weight 0) and must select empty slots away whatever they hold.  Each decode
 entry point runs with a workspace pre-filled with 0xFF bytes (NaN in fp32 and
 in bf16) against the fp64 oracle; ragged lengths leave many slots empty.
-Tolerance as for every bf16 path: max |err| <= 2e-2, mean |err| <= 2e-3.
+Split counts above 64 take the combine's second pass over slots (one lane
+per slot, 64 at a time).  Tolerance as for every bf16 path: max |err| <=
+2e-2, mean |err| <= 2e-3; fp32: max |err| <= 1e-5.
 """
 import numpy as np
 import pytest
@@ -34,7 +36,7 @@ def _nan_ws(nbytes):
     return torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
 
 
-@pytest.mark.parametrize("splits", [0, 2, 9, 40])
+@pytest.mark.parametrize("splits", [0, 2, 9, 40, 100, 300])
 def test_gqa_decode_nan_workspace(splits):
     B, Hq, Hkv, T, D = len(LENS), 32, 8, 700, 128
     q, k, v = _rand((B, Hq, 1, D), 800), _rand((B, Hkv, T, D), 801), _rand((B, Hkv, T, D), 802)
@@ -82,3 +84,18 @@ def test_fp8_decode_nan_workspace():
                          scale=w.scale, num_splits=S, workspace=_nan_ws(gqa.decode_workspace_size(w.B, w.Hq, w.Dv, S)))
     ref = O.attention_e4m3kv(q, kc, ks, vc, vs, w.scale, True, kv_lens=LENS)
     _check(out, ref, "fp8 decode, NaN workspace")
+
+
+@pytest.mark.parametrize("splits", [3, 130])
+def test_f32_decode_nan_workspace(splits):
+    B, Hq, Hkv, T, D = len(LENS), 8, 2, 700, 64
+    g = torch.Generator("cpu").manual_seed(830)
+    q = torch.randn(B, Hq, 1, D, generator=g)
+    k = torch.randn(B, Hkv, T, D, generator=g)
+    v = torch.randn(B, Hkv, T, D, generator=g)
+    out = gqa.decode(q.cuda(), k.cuda(), v.cuda(), torch.tensor(LENS, dtype=torch.int32).cuda(), scale=0.125,
+                     num_splits=splits, workspace=_nan_ws(gqa.decode_workspace_size(B, Hq, D, splits)))
+    ref = O.attention(q, k, v, 0.125, True, kv_lens=LENS)
+    d = np.abs(out.double().cpu().numpy() - ref)
+    print(f"fp32 decode, NaN workspace, S={splits} max_abs={d.max():.3e}", flush=True)
+    assert np.isfinite(out.cpu().numpy()).all() and d.max() <= 1e-5
