@@ -24,8 +24,9 @@ constexpr int kCT = 128;  // threads per row at most; each owns 4 output dims
 constexpr int kCB = 16;   // partial outputs loaded together before any is used
 
 // Latency, not bandwidth, bounds this pass (a few MB in total), so every
-// load is issued before its value is needed: one round trip for the row's
-// lse values (lane s holds split s), one per batch of kCB partial outputs
+// load is issued before its value is needed: the row's lse values (lane s
+// holds split s) and the first kCB partial outputs in one round trip, one
+// more per further batch of kCB partial outputs
 // (unconditional loads of in-bounds slots; slots past the split count and
 // empty slots get weight 0 and are selected away, whatever they hold).
 template <bool OUT_BF16, bool PART_BF16>
@@ -41,34 +42,41 @@ __global__ __launch_bounds__(kCT) void combine_kernel(CombineArgs p)
     const int dim = threadIdx.x * 4;
     const int d0 = min(dim, p.Dv - 4);  // lanes past Dv mirror the last dims and store nothing
 
+    auto load_batch = [&](PT4 (&v)[kCB], int s0, int sb, int n) {
+#pragma unroll
+        for (int i = 0; i < kCB; ++i) v[i] = *(const PT4 *)(po + (size_t)(s0 + min(sb + i, n - 1)) * p.Dv + d0);
+    };
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.f;
+    auto add_batch = [&](const PT4 (&v)[kCB], int sb, int n, float wl) {
+#pragma unroll
+        for (int i = 0; i < kCB; ++i) {
+            const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), min(sb + i, 63)));
+            const float w = sb + i < n ? wi : 0.f;
+            const bool use = w != 0.f;
+            wsum += w;
+            acc[0] = use ? fmaf(w, (float)v[i][0], acc[0]) : acc[0];
+            acc[1] = use ? fmaf(w, (float)v[i][1], acc[1]) : acc[1];
+            acc[2] = use ? fmaf(w, (float)v[i][2], acc[2]) : acc[2];
+            acc[3] = use ? fmaf(w, (float)v[i][3], acc[3]) : acc[3];
+        }
+    };
+
     float ll = lane < ns ? lse[lane] : -INFINITY;
+    PT4 v[kCB];
+    load_batch(v, 0, 0, min(64, ns));  // in flight together with the lse load
     float L = ll;
     for (int s0 = 64; s0 < ns; s0 += 64) L = fmaxf(L, s0 + lane < ns ? lse[s0 + lane] : -INFINITY);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) L = fmaxf(L, __shfl_xor(L, o));
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.f;
     if (L != -INFINITY) {
         for (int s0 = 0; s0 < ns; s0 += 64) {
             if (s0 > 0) ll = s0 + lane < ns ? lse[s0 + lane] : -INFINITY;
             const float wl = __builtin_amdgcn_exp2f(ll - L);  // 0 for lse = -inf
             const int n = min(64, ns - s0);
             for (int sb = 0; sb < n; sb += kCB) {
-                PT4 v[kCB];
-#pragma unroll
-                for (int i = 0; i < kCB; ++i)
-                    v[i] = *(const PT4 *)(po + (size_t)(s0 + min(sb + i, n - 1)) * p.Dv + d0);
-#pragma unroll
-                for (int i = 0; i < kCB; ++i) {
-                    const float wi = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), min(sb + i, 63)));
-                    const float w = sb + i < n ? wi : 0.f;
-                    const bool use = w != 0.f;
-                    wsum += w;
-                    acc[0] = use ? fmaf(w, (float)v[i][0], acc[0]) : acc[0];
-                    acc[1] = use ? fmaf(w, (float)v[i][1], acc[1]) : acc[1];
-                    acc[2] = use ? fmaf(w, (float)v[i][2], acc[2]) : acc[2];
-                    acc[3] = use ? fmaf(w, (float)v[i][3], acc[3]) : acc[3];
-                }
+                if (s0 > 0 || sb > 0) load_batch(v, s0, sb, n);
+                add_batch(v, sb, n, wl);
             }
         }
     }
