@@ -164,6 +164,14 @@ struct PlaneTile {
 // is explicit (wait_vmem / wait_vmem_le before lds_barrier).  The
 // instructions have no register results; they only read their address
 // operands at issue.  M0 carries the LDS base (1 wait state before the copy).
+//
+// Every one of these statements writes M0 and names it in its clobber list.
+// M0 is a reserved register of the AMDGPU backend (the compiler sets it
+// right before each of its own uses and never keeps a value in it); clang
+// warns that a reserved register is not preserved across the statement,
+// which is exactly what the clobber says, so that warning is silenced here.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ unsigned lds_u32(const void *lds_ptr)
 {
     return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(GQA_LDS const void *)lds_ptr);
@@ -173,7 +181,7 @@ __device__ __forceinline__ void g2lds16(const void *gptr, void *lds_wave_base)
 {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
                  "s"(lds_u32(lds_wave_base))
-                 : "memory");
+                 : "memory", "m0");
 }
 
 // 4 bytes per lane (global_load_lds_dword): lane l's word lands at
@@ -182,7 +190,7 @@ __device__ __forceinline__ void g2lds4(const void *gptr, void *lds_wave_base)
 {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr),
                  "s"(lds_u32(lds_wave_base))
-                 : "memory");
+                 : "memory", "m0");
 }
 
 // Same copy from a workgroup-uniform base plus a per-lane unsigned byte
@@ -195,7 +203,7 @@ __device__ __forceinline__ void g2lds16(const void *uniform_base, unsigned byte_
     const unsigned long long base = ((unsigned long long)hi << 32) | lo;
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(byte_off), "s"(base),
                  "s"(lds_u32(lds_wave_base))
-                 : "memory");
+                 : "memory", "m0");
 }
 
 // Same copy with the LDS destination given as a workgroup-uniform LDS byte
@@ -209,15 +217,17 @@ __device__ __forceinline__ void g2lds16_at(const void *uniform_base, unsigned by
     const unsigned long long base = ((unsigned long long)hi << 32) | lo;
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(byte_off), "s"(base),
                  "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-                 : "memory");
+                 : "memory", "m0");
 }
 
 __device__ __forceinline__ void g2lds16_at(const void *gptr, unsigned lds_addr)
 {
     asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
                  "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-                 : "memory");
+                 : "memory", "m0");
 }
+
+#pragma clang diagnostic pop
 
 // Complete a register's pending global load here: the compiler waits for it
 // before an asm statement that reads the register.  Without this, a value
@@ -276,6 +286,29 @@ __device__ __forceinline__ float halves_sum(float x)
 {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Max of finite or -inf values with one VALU instruction each.  fmaxf
+// follows IEEE maxNum, for which the compiler first quiets every input it
+// cannot prove canonical (one extra v_max_f32 x, x per input); the softmax
+// max runs on MFMA results and -inf, where that is never needed.
+__device__ __forceinline__ float vmax3(float a, float b, float c)
+{
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+__device__ __forceinline__ float vmax(float a, float b)
+{
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+// max over lanes l and l ^ 32 of finite or -inf values (see halves_max)
+__device__ __forceinline__ float halves_vmax(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // Max / sum over the four lanes l, l^16, l^32, l^48 (one 16x16 accumulator

@@ -32,10 +32,11 @@
 //    half the L2 -> LDS traffic per FLOP of two 4-wave workgroups per CU.
 //  * Online softmax in base 2: scale*log2(e) is folded into one FMA per
 //    score, exp via v_exp_f32, the row sum via v_dot2 over the bf16-rounded
-//    weights.  The running max is only moved (and O rescaled) when a tile's
-//    max exceeds it by more than 2^8; weights then stay <= 256, which fp32
-//    and bf16 carry with the same relative precision as weights <= 1, and
-//    the normalised result is the same softmax.
+//    weights.  The reference max is set from a lane's first visible tile
+//    and moved (O rescaled) only when that lane's tile weights sum past
+//    2^16, so the common tile computes no max at all; weights stay below
+//    2^16, which fp32 and bf16 carry with the same relative precision as
+//    weights <= 1, and the normalised result is the same softmax.
 //  * Grid order: tiles of one (batch, KV head, head block) are consecutive
 //    on one XCD (the dispatcher deals workgroups round-robin over 8 XCDs, so
 //    the remap keeps a KV head's K/V in one L2), heaviest causal tiles first.
@@ -45,6 +46,8 @@
 //    and a lower mask bound per lane.  Optional used lengths per sequence
 //    turn the tail of each slot into padding (a right-padded batch): padded
 //    keys are never read, padded query rows never written.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -64,6 +67,8 @@ namespace {
 #ifndef GQA_FWD_PREFETCH
 #define GQA_FWD_PREFETCH 6  // LDS operand reads kept in flight ahead of the MFMAs (0: compiler's choice)
 #endif
+// sum of one lane's weights in a tile past which its reference max moves
+constexpr float kSumCap = 65536.0f;
 constexpr int kNC = GQA_FWD_NC;
 constexpr int kNW = GQA_FWD_NW;
 #ifndef GQA_FWD_BN
@@ -296,10 +301,10 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
 
     const float c = p.c;
 
-    // One tile: S^T = K Q^T (each K operand feeds NC MFMAs), mask on
-    // diagonal / ragged tiles, online softmax, O^T += V^T P^T (each V^T
-    // operand feeds NC MFMAs).
-    auto scores = [&](int it, f32x16 (&sc)[kNC][kNT]) {
+    // Tile building blocks: S^T = K Q^T (each K operand feeds NC MFMAs);
+    // mask on diagonal / ragged tiles and online softmax (VALU only); O^T +=
+    // V^T P^T (each V^T operand feeds NC MFMAs).
+    auto qk_body = [&](int it, f32x16 (&sc)[kNC][kNT]) {
         const char *ks_ = (const char *)sm.k[it % kStages];
 #pragma unroll
         for (int cb = 0; cb < kNC; ++cb)
@@ -317,23 +322,47 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
                 for (int cb = 0; cb < kNC; ++cb) sc[cb][t] = mfma32x32x16(a, qreg[cb][ks], sc[cb][t]);
             }
         }
-#if GQA_FWD_PREFETCH
-        {
-            // schedule: PREFETCH operand reads first, then one MFMA group per
-            // further read, so the LDS latency overlaps earlier MFMAs
-            constexpr int NR = kNT * KS, PF = GQA_FWD_PREFETCH < NR ? GQA_FWD_PREFETCH : NR;
-            __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
-#pragma unroll
-            for (int i = 0; i < NR - PF; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, kNC, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, kNC * PF, 0);
-        }
-#endif
-
     };
-    auto finish = [&](int it, f32x16 (&sc)[kNC][kNT]) {
+    auto pv_body = [&](int it, const u32x4 (&pb)[kNC][2 * kNT]) {
+        const char *vs_ = (const char *)sm.v[it % kStages];
+#pragma unroll
+        for (int st = 0; st < 2 * kNT; ++st) {
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) {
+                const int o_ = dt * Tile::PLANE_BYTES + 16 * st * 64;
+                const u32x2 lo = lds_read_tr16(vs_ + vb_h0 + o_);
+                const u32x2 hv = lds_read_tr16(vs_ + vb_h1 + o_);
+                const u32x4 va = {lo.x, lo.y, hv.x, hv.y};
+#pragma unroll
+                for (int cb = 0; cb < kNC; ++cb) o[cb][dt] = mfma32x32x16(va, pb[cb][st], o[cb][dt]);
+            }
+        }
+    };
+    // Operand-read schedule of NG MFMA groups (NC MFMAs each) fed by R LDS
+    // reads per group: the reads of the next GQA_FWD_PREFETCH groups are
+    // issued ahead of the MFMAs, so the LDS latency overlaps earlier MFMAs.
+    auto read_schedule = [&](auto ng_, auto r_) {
+#if GQA_FWD_PREFETCH
+        constexpr int NG = decltype(ng_)::value, R = decltype(r_)::value;
+        constexpr int PF = GQA_FWD_PREFETCH < NG ? GQA_FWD_PREFETCH : NG;
+        __builtin_amdgcn_sched_group_barrier(0x100, R * PF, 0);
+#pragma unroll
+        for (int i = 0; i < NG - PF; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, kNC, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, kNC * PF, 0);
+#endif
+    };
+    auto qk = [&](int it, f32x16 (&sc)[kNC][kNT]) {
+        qk_body(it, sc);
+        read_schedule(std::integral_constant<int, kNT * KS>{}, std::integral_constant<int, 1>{});
+    };
+    auto pv = [&](int it, const u32x4 (&pb)[kNC][2 * kNT]) {
+        pv_body(it, pb);
+        read_schedule(std::integral_constant<int, 2 * kNT * DT>{}, std::integral_constant<int, 2>{});
+    };
+    auto softmax = [&](int it, f32x16 (&sc)[kNC][kNT], u32x4 (&pb)[kNC][2 * kNT]) {
         const int k0 = (t0 + it) * kBN;
         const bool need_mask = (p.causal && k0 + kBN - 1 > off + q0) || (k0 + kBN > Tk) || (win > 0 && k0 < wlo_hi);
         if (need_mask) {
@@ -348,36 +377,25 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
                     }
         }
 
-        // online softmax (base 2); the reference max of a lane's query only
-        // moves (and its O column is rescaled) when a tile max exceeds it by
-        // more than 2^8 -- and only for that lane, so a row never depends on
-        // keys it cannot see
-        auto move_ref = [&]() {
-#pragma unroll
-            for (int cb = 0; cb < kNC; ++cb) {
-                float mx = sc[cb][0][0];
-#pragma unroll
-                for (int t = 0; t < kNT; ++t)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[cb][t][e]);
-                const float mt = halves_max(mx) * c;
-                const float m_new = (mt > m_run[cb] + 8.0f) ? mt : m_run[cb];
-                const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[cb] - m_new);
-                m_run[cb] = m_new;
-                l_run[cb] *= alpha;
-#pragma unroll
-                for (int i = 0; i < DT; ++i)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e) o[cb][i][e] *= alpha;
-            }
-        };
-        u32x4 pb[kNC][2 * kNT];
+        // online softmax (base 2).  The weights are formed against a
+        // reference that moves rarely: it is set from the tile max on a
+        // lane's first tile with a visible key, and afterwards it moves (and
+        // the lane's O column is rescaled) only when the lane's tile weights
+        // sum past kSumCap -- an overflow to inf shows up there too -- in
+        // which case the weights are formed again against the moved
+        // reference.  Weights then stay below 2^16, which fp32 and bf16 carry
+        // with the same relative precision as weights <= 1, and the
+        // normalised result is the same softmax.  A lane moves only on its
+        // own scores, so a row never depends on keys it cannot see.  In the
+        // common case the block is the weights alone, written for
+        // instruction-level parallelism (its latency is exposed beside
+        // another wave's MFMAs): four independent row-sum chains, one check.
         float ts[kNC];  // this lane's sum of the tile's weights
         auto weights = [&]() {
 #pragma unroll
             for (int cb = 0; cb < kNC; ++cb) {
                 const float m_use = (m_run[cb] == -INFINITY) ? 0.f : m_run[cb];
-                ts[cb] = 0.f;
+                float part[2 * kNT];
 #pragma unroll
                 for (int t = 0; t < kNT; ++t) {
 #pragma unroll
@@ -391,57 +409,68 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
                         pk.y = pack_bf16x2(pv[2], pv[3]);
                         pk.z = pack_bf16x2(pv[4], pv[5]);
                         pk.w = pack_bf16x2(pv[6], pv[7]);
-                        ts[cb] = sum_bf16x8(pk, ts[cb]);
+                        part[2 * t + h] = sum_bf16x8(pk, 0.f);
                         pb[cb][2 * t + h] = pk;
                     }
                 }
+                float acc = part[0];
+#pragma unroll
+                for (int i = 1; i < 2 * kNT; ++i) acc += part[i];
+                ts[cb] = acc;
             }
         };
-        {
-            bool any_move = false;
+        // move the reference of every lane whose tile max exceeds it by more
+        // than 2^8 (the tile max as a tree of v_max3, log2 units)
+        auto move_ref = [&]() {
 #pragma unroll
             for (int cb = 0; cb < kNC; ++cb) {
-                float mx = sc[cb][0][0];
+                constexpr int NV = 16 * kNT;
+                float m1[NV];
 #pragma unroll
                 for (int t = 0; t < kNT; ++t)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) mx = fmaxf(mx, sc[cb][t][e]);
-                any_move |= halves_max(mx) * c > m_run[cb] + 8.0f;
+                    for (int e = 0; e < 16; ++e) m1[16 * t + e] = sc[cb][t][e];
+                int n_ = NV;
+#pragma unroll
+                for (int r = 0; r < 6; ++r) {
+                    if (n_ == 1) break;
+                    const int out = (n_ + 2) / 3;
+#pragma unroll
+                    for (int e = 0; e < out; ++e) {
+                        const int a = 3 * e;
+                        m1[e] = a + 2 < n_ ? vmax3(m1[a], m1[a + 1], m1[a + 2])
+                                           : (a + 1 < n_ ? vmax(m1[a], m1[a + 1]) : m1[a]);
+                    }
+                    n_ = out;
+                }
+                const float mt = halves_vmax(m1[0]) * c;
+                const float m_new = (mt > m_run[cb] + 8.0f) ? mt : m_run[cb];
+                const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run[cb] - m_new);
+                m_run[cb] = m_new;
+                l_run[cb] *= alpha;
+#pragma unroll
+                for (int i = 0; i < DT; ++i)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) o[cb][i][e] *= alpha;
             }
-            if (__any(any_move)) move_ref();
+        };
+        bool fresh = false;
+#pragma unroll
+        for (int cb = 0; cb < kNC; ++cb) fresh |= m_run[cb] == -INFINITY;
+        if (__any(fresh)) move_ref();
+        weights();
+        bool big = false;
+#pragma unroll
+        for (int cb = 0; cb < kNC; ++cb) big |= !(ts[cb] <= kSumCap);
+        if (__any(big)) {
+            move_ref();
             weights();
         }
 #pragma unroll
         for (int cb = 0; cb < kNC; ++cb) l_run[cb] += ts[cb];
-
-        const char *vs_ = (const char *)sm.v[it % kStages];
-#pragma unroll
-        for (int st = 0; st < 2 * kNT; ++st) {
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) {
-                const int o_ = dt * Tile::PLANE_BYTES + 16 * st * 64;
-                const u32x2 lo = lds_read_tr16(vs_ + vb_h0 + o_);
-                const u32x2 hv = lds_read_tr16(vs_ + vb_h1 + o_);
-                const u32x4 va = {lo.x, lo.y, hv.x, hv.y};
-#pragma unroll
-                for (int cb = 0; cb < kNC; ++cb) o[cb][dt] = mfma32x32x16(va, pb[cb][st], o[cb][dt]);
-            }
-        }
-#if GQA_FWD_PREFETCH
-        {
-            constexpr int NM = 2 * kNT * DT, PF = GQA_FWD_PREFETCH < NM ? GQA_FWD_PREFETCH : NM;
-            __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
-#pragma unroll
-            for (int i = 0; i < NM - PF; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, kNC, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-            }
-            __builtin_amdgcn_sched_group_barrier(0x008, kNC * PF, 0);
-        }
-#endif
     };
 
-    // ring of kStages K/V slots: kStages - 1 tiles in flight while one is computed
+    // ring of kStages K/V slots, filled kStages - 1 tiles ahead
 #pragma unroll
     for (int s_ = 0; s_ < kStages - 1; ++s_)
         if (s_ < ntiles) issue_kv(s_, s_);
@@ -450,6 +479,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
         return wave_active && k0 <= wlast && (win <= 0 || k0 + kBN - 1 >= wfirst);
     };
     f32x16 sc[kNC][kNT];
+    u32x4 pb[kNC][2 * kNT];
     for (int it = 0; it < ntiles; ++it) {
         if (it + kStages - 2 < ntiles)
             wait_vmem_le<(kStages - 2) * 2 * NINS>();  // tile it landed; later ones may fly
@@ -459,8 +489,9 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
         const int nx = it + kStages - 1;
         if (nx < ntiles) issue_kv(nx, nx % kStages);
         if (live(it)) {
-            scores(it, sc);
-            finish(it, sc);
+            qk(it, sc);
+            softmax(it, sc, pb);
+            pv(it, pb);
         }
     }
 

@@ -109,6 +109,24 @@ def test_fwd_scale_variants():
         _check(out, O.attention(q, k, v, scale, True), "bf16", f"scale {scale}")
 
 
+@pytest.mark.parametrize("slope", [60.0, -60.0, 200.0])
+def test_fwd_growing_and_falling_logits(slope):
+    """Scores that rise (or fall) along the key axis by tens to hundreds of
+    log2 units: a rising row makes the kernel move its reference max many
+    times mid-row (each move rescales O), a falling row never moves it after
+    the first tile.  Both must still match the oracle."""
+    B, Hq, Hkv, T, D = 1, 4, 1, 700, 128
+    g = torch.Generator("cpu").manual_seed(17)
+    q = (torch.ones(B, Hq, T, D) + 0.1 * torch.randn(B, Hq, T, D, generator=g)).to(torch.bfloat16)
+    ramp = torch.linspace(0.0, 1.0, T).view(1, 1, T, 1)
+    # q.k_j * scale * log2(e) grows by about `slope` over the row
+    k = (ramp * slope / (D * 0.0884 * 1.4427) + 0.05 * torch.randn(B, Hkv, T, D, generator=g)).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, T, D, generator=g).to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(D)
+    out = gqa.attention(q.cuda(), k.cuda(), v.cuda(), scale=scale, causal=True)
+    _check(out, O.attention(q, k, v, scale, True), "bf16", f"logit slope {slope}")
+
+
 # ------------------------------------------------------------------ stated invariants on the GPU
 
 def test_future_perturbation_is_bit_identical():
