@@ -104,6 +104,97 @@ def traffic_for(kernel: str, launches_per_unit: int = 1):
     return t["bytes_per_launch"]
 
 
+PROFILE_WORKLOADS = ("prefill", "decode", "mqa", "mla", "topk", "swa", "fp8", "probes")
+
+
+def _profile_call(torch, gqa, W, dev, name):
+    """Inputs in HBM and a zero-argument launch of one workload (for counter
+    passes: one call per step, nothing else on the GPU)."""
+    if name in ("prefill", "mqa"):
+        w = W.GQA_PREFILL if name == "prefill" else W.MQA_SUFFIX
+        sets = []
+        for wv in (w, dataclasses.replace(w, seed=w.seed + 100)):
+            q, k, v = (t.to(dev) for t in W.fwd_inputs(wv))
+            sets.append((q, k, v, torch.empty((w.B, w.Hq, w.Tq, w.Dv), dtype=torch.bfloat16, device=dev)))
+        turn = [0]
+
+        def fn():
+            q, k, v, out = sets[turn[0] % 2]
+            turn[0] += 1
+            gqa.attention(q, k, v, scale=w.scale, causal=True, out=out)
+        return fn, {"workload": w.name, "flop_per_call": fwd_flops(w)}
+    if name == "swa":
+        w = W.SWA_VARLEN
+        q, k, v, cu = (t.to(dev) for t in W.varlen_inputs(w))
+        out = torch.empty((q.shape[0], w.Hq, w.Dv), dtype=torch.bfloat16, device=dev)
+        return (lambda: gqa.attention_varlen(q, k, v, cu, cu, scale=w.scale, causal=True, window=w.extra["window"],
+                                             out=out)), {"workload": w.name, "flop_per_call": varlen_flops(w)}
+    if name in ("decode", "mla"):
+        w = W.GQA_DECODE if name == "decode" else W.MLA_DECODE
+        q, kc, vc, lens = W.decode_inputs(w, nan_tail=False)
+        q, kc, lens_d = q.to(dev), kc.to(dev), lens.to(dev)
+        vc = kc[..., : w.Dv] if name == "mla" else vc.to(dev)
+        out = torch.empty((w.B, w.Hq, 1, w.Dv), dtype=torch.bfloat16, device=dev)
+        S = gqa.decode_splits(w.B, w.Hq, w.Hkv, w.Tk, w.Dk, w.Dv, gqa.GQA_BF16)
+        ws = torch.empty(gqa.decode_workspace_size(w.B, w.Hq, w.Dv, S), dtype=torch.uint8, device=dev)
+        return (lambda: gqa.decode(q, kc, vc, lens_d, scale=w.scale, num_splits=S, out=out, workspace=ws)), {
+            "workload": w.name, "kv_bytes_per_call": decode_bytes(w, lens.tolist()), "splits": S}
+    if name == "fp8":
+        w = W.GQA_DECODE_FP8
+        q, kc, vc, ks, vs, lens = W.fp8_decode_inputs(w, nan_tail=False)
+        lens_l = lens.tolist()
+        q, kc, vc, ks, vs, lens = (t.to(dev) for t in (q, kc, vc, ks, vs, lens))
+        out = torch.empty((w.B, w.Hq, 1, w.Dv), dtype=torch.bfloat16, device=dev)
+        S = gqa.decode_splits(w.B, w.Hq, w.Hkv, w.Tk, w.Dk, w.Dv, gqa.GQA_BF16)
+        ws = torch.empty(gqa.decode_workspace_size(w.B, w.Hq, w.Dv, S), dtype=torch.uint8, device=dev)
+        return (lambda: gqa.decode_fp8(q, kc, vc, ks, vs, lens, scale=w.scale, num_splits=S, out=out,
+                                       workspace=ws)), {"workload": w.name,
+                                                        "kv_bytes_per_call": fp8_decode_bytes(w, lens_l)}
+    if name == "topk":
+        w = W.MLA_TOPK
+        q, kc, _, lens = W.decode_inputs(w, nan_tail=False)
+        sels = [W.topk_indices(dataclasses.replace(w, seed=w.seed + 10 * i), lens).to(dev) for i in range(8)]
+        sel_rows = [min(w.extra["topk"], n) for n in lens.tolist()]
+        q, kc, lens_d = q.to(dev), kc.to(dev), lens.to(dev)
+        out = torch.empty((w.B, w.Hq, 1, w.Dv), dtype=torch.bfloat16, device=dev)
+        S = gqa.decode_topk_splits(w.B, w.Hq, w.extra["topk"], w.Dk, w.Dv, gqa.GQA_BF16)
+        ws = torch.empty(gqa.decode_workspace_size(w.B, w.Hq, w.Dv, S), dtype=torch.uint8, device=dev)
+        turn = [0]
+
+        def fn():
+            idx = sels[turn[0] % len(sels)]
+            turn[0] += 1
+            gqa.decode_topk(q, kc, lens_d, idx, scale=w.scale, num_splits=S, out=out, workspace=ws)
+        return fn, {"workload": w.name, "kv_bytes_per_call": topk_bytes(w, sel_rows), "splits": S}
+    raise ValueError(name)
+
+
+def profile_one(torch, gqa, W, dev, name, steps, warmup) -> int:
+    """Launch one workload warmup + steps times (nothing else), time the
+    timed calls with HIP events on the launch stream, print one JSON line."""
+    fn, info = _profile_call(torch, gqa, W, dev, name)
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    med = statistics.median(us)
+    info.update({"profile": name, "calls": steps, "median_us": round(med, 2), "mean_us": round(sum(us) / len(us), 2)})
+    if "flop_per_call" in info:
+        info["TFLOP/s"] = round(info["flop_per_call"] / med / 1e6, 1)
+        info["frac_mfma_peak"] = round(info["TFLOP/s"] / PEAK_BF16_TFLOPS, 4)
+    if "kv_bytes_per_call" in info:
+        info["GB/s"] = round(info["kv_bytes_per_call"] / med / 1e3, 1)
+        info["frac_hbm_peak"] = round(info["GB/s"] / PEAK_HBM_GBPS, 4)
+    print(json.dumps(info), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +206,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--profile", choices=sorted(PROFILE_WORKLOADS), default=None,
+                    help="only launch this workload's kernels (warmup + steps calls, for rocprofv3 passes)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -142,6 +235,12 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
         return 0
+
+    if args.profile == "probes":
+        print(json.dumps(probe_context(torch, dev)), flush=True)
+        return 0
+    if args.profile:
+        return profile_one(torch, gqa, W, dev, args.profile, args.steps, args.warmup)
 
     # ---------------- inputs (seeded, synthetic, resident in HBM) ----------------
     # The prefill alternates between two input sets (seeds s and s + 100) so
@@ -249,6 +348,7 @@ def main() -> int:
     torch.cuda.empty_cache()
     result["context"] = {"hbm_copy_GBps": copy_bandwidth(torch, dev),
                          "bf16_gemm_TFLOPs": gemm_rate(torch, dev),
+                         "probes": probe_context(torch, dev),
                          "note": "plain 1 GiB device-to-device copy (reads + writes), the practical HBM rate; "
                                  "8192^3 bf16 GEMM through torch (hipBLASLt), a practical dense-MFMA rate "
                                  "under the board power limit"}
@@ -283,6 +383,81 @@ def copy_bandwidth(torch, dev) -> float:
     sec = _time(torch, lambda: dst.copy_(src), reps=5, warm=2)
     del src, dst
     return round(2 * n / sec / 1e9, 1)
+
+
+def probe_context(torch, dev) -> dict:
+    """Ceilings measured on this GPU by the probe kernels (libgqa_probes.so):
+    a pure v_mfma_f32_32x32x16_bf16 loop (8 independent chains per wave, every
+    CU) on seeded N(0,1) bf16 operands and on zeros, and a global_load_lds
+    stream of 2 GiB through LDS with no arithmetic.  Each reports the shader
+    clock it ran at (s_memtime cycles per 100 MHz s_memrealtime tick,
+    median over workgroups)."""
+    import ctypes
+    path = os.path.join(ROOT, "causal_grouped_query_amd", "libgqa_probes.so")
+    L = ctypes.CDLL(path)
+    P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.gqa_probe_mfma_bf16.restype = I
+    L.gqa_probe_mfma_bf16.argtypes = [P, I, P, P, I, I, I, P]
+    L.gqa_probe_stream_lds.restype = I
+    L.gqa_probe_stream_lds.argtypes = [P, SZ, I, I, P, P]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def clock_ghz(clk):
+        c = clk.view(-1, 4).cpu().double()
+        ghz = (c[:, 1] - c[:, 0]) / ((c[:, 3] - c[:, 2]) * 10.0)  # cycles per ns (realtime is 100 MHz)
+        return round(float(ghz.median()), 3)
+
+    res = {}
+    n_ops = 4096
+    g = torch.Generator("cpu").manual_seed(11)
+    ops_rand = torch.randn(n_ops * 64 * 8, generator=g).to(torch.bfloat16).to(dev)
+    ops_zero = torch.zeros_like(ops_rand)
+    grid, waves, iters = 256, 8, 40000  # one resident round: 2 waves per SIMD
+    out = torch.empty(grid * waves * 64, dtype=torch.float32, device=dev)
+    clk = torch.zeros(grid * 4, dtype=torch.int64, device=dev)
+    flop = 32768.0 * 8 * iters * grid * waves
+    for name, ops in (("n01", ops_rand), ("zeros", ops_zero)):
+        best = None
+        for _ in range(3):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            rc = L.gqa_probe_mfma_bf16(ops.data_ptr(), n_ops, out.data_ptr(), clk.data_ptr(), grid, waves, iters,
+                                       stream)
+            e.record()
+            torch.cuda.synchronize()
+            if rc != 0:
+                raise RuntimeError("MFMA probe launch failed")
+            sec = s.elapsed_time(e) * 1e-3
+            if best is None or sec < best[0]:
+                best = (sec, clock_ghz(clk))
+        sec, ghz = best
+        tf = flop / sec / 1e12
+        res[f"mfma_bf16_{name}"] = {"TFLOP/s": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                                    "shader_clock_GHz": ghz,
+                                    "frac_peak_at_clock": round(tf / (PEAK_BF16_TFLOPS * ghz / 2.4), 4)}
+    del ops_rand, ops_zero, out
+    nbytes, grid_s = 2 << 30, 2048
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    clk = torch.zeros(grid_s * 4, dtype=torch.int64, device=dev)
+    best = None
+    for _ in range(4):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        rc = L.gqa_probe_stream_lds(src.data_ptr(), nbytes // grid_s, grid_s, 1, clk.data_ptr(), stream)
+        e.record()
+        torch.cuda.synchronize()
+        if rc != 0:
+            raise RuntimeError("stream probe launch failed")
+        sec = s.elapsed_time(e) * 1e-3
+        if best is None or sec < best[0]:
+            best = (sec, clock_ghz(clk))
+    res["stream_global_load_lds"] = {"GB/s": round(nbytes / best[0] / 1e9, 1),
+                                     "frac_peak": round(nbytes / best[0] / 1e9 / PEAK_HBM_GBPS, 4),
+                                     "shader_clock_GHz": best[1], "bytes": nbytes}
+    del src
+    res["note"] = ("probe kernels: dense 32x32x16 bf16 MFMA loop on every CU (2 waves per SIMD, 8 independent "
+                   "chains each) and a read-only HBM -> LDS stream; shader clock from s_memtime / s_memrealtime")
+    return res
 
 
 def gemm_rate(torch, dev) -> float:

@@ -1,7 +1,9 @@
 """Build libgqa_attn.so in-tree with hipcc for gfx950.
 
 Every .hip file under csrc/ is compiled to an object in parallel and linked
-into causal_grouped_query_amd/libgqa_attn.so.  Device code is built with the
+into causal_grouped_query_amd/libgqa_attn.so; the measurement probes under
+probes/ (peak MFMA and streaming-copy rates for the benchmark's roofline
+context) go into libgqa_probes.so.  Device code is built with the
 packed-fp32 instructions disabled.
 """
 from __future__ import annotations
@@ -17,6 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgqa_attn.so")
+PROBE_LIB = os.path.join(PKG, "libgqa_probes.so")  # measurement aids for bench.py (not the attention ABI)
 OBJDIR = os.path.join(PKG, "_build")
 ARCH = os.environ.get("GQA_OFFLOAD_ARCH", "gfx950")
 
@@ -29,7 +32,8 @@ FLAGS = [
 
 
 def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.basename(src).replace(".hip", ".o"))
+    sub = "probe_" if os.path.basename(os.path.dirname(src)) == "probes" else ""
+    obj = os.path.join(OBJDIR, sub + os.path.basename(src).replace(".hip", ".o"))
     cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -37,19 +41,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    probe_srcs = sorted(glob.glob(os.path.join(PKG, "probes", "*.hip")))
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probe_srcs))) as ex:
+        objs = list(ex.map(_compile, srcs + probe_srcs))
+    _link(objs[: len(srcs)], LIB)
+    _link(objs[len(srcs):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 
