@@ -143,7 +143,7 @@ GQA_API const char *gqa_attn_strerror(int code)
 
 GQA_API int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out, int B, int Hq,
                          int Hkv, int Tq, int Tk, int Dk, int Dv, float scale, int causal,
-                         int dtype, void *stream)
+                         gqa_dtype dtype, void *stream)
 {
     if (!q || !k || !v || !out) return GQA_ERR_INVALID_ARG;
     int rc = check_common(B, Hq, Hkv, Dk, Dv, scale, dtype);
@@ -197,7 +197,7 @@ GQA_API int gqa_attn_fwd_varlen(const void *q, const void *k, const void *v, voi
                                 int Hkv, int total_q, int Dk, int Dv, long long q_sh, long long q_st,
                                 long long k_sh, long long k_st, long long v_sh, long long v_st,
                                 long long o_sh, long long o_st, float scale, int causal, int window,
-                                int dtype, void *stream)
+                                gqa_dtype dtype, void *stream)
 {
     if (!q || !k || !v || !out || !cu_seqlens_q || !cu_seqlens_k) return GQA_ERR_INVALID_ARG;
     int rc = check_common(num_seqs, Hq, Hkv, Dk, Dv, scale, dtype);
@@ -253,7 +253,7 @@ GQA_API int gqa_attn_fwd_varlen(const void *q, const void *k, const void *v, voi
 
 GQA_API int gqa_attn_fwd_shard(const void *q, const void *k, const void *v, float *out, float *lse, int B,
                                int Hq, int Hkv, int Tq, int Tk, int Dk, int Dv, long long q_pos0,
-                               long long k_pos0, float scale, int causal, int dtype, void *stream)
+                               long long k_pos0, float scale, int causal, gqa_dtype dtype, void *stream)
 {
     if (!q || !k || !v || !out || !lse) return GQA_ERR_INVALID_ARG;
     int rc = check_common(B, Hq, Hkv, Dk, Dv, scale, dtype);
@@ -285,7 +285,7 @@ GQA_API int gqa_attn_fwd_shard(const void *q, const void *k, const void *v, floa
 }
 
 GQA_API int gqa_attn_merge(const float *o_parts, const float *lse_parts, void *out, int num_parts,
-                           long long rows, int Dv, int out_dtype, void *stream)
+                           long long rows, int Dv, gqa_dtype out_dtype, void *stream)
 {
     if (!o_parts || !lse_parts || !out) return GQA_ERR_INVALID_ARG;
     if (num_parts <= 0 || rows <= 0 || Dv <= 0) return GQA_ERR_INVALID_ARG;
@@ -312,7 +312,7 @@ GQA_API int gqa_attn_merge(const float *o_parts, const float *lse_parts, void *o
     return launch_status(gqa::launch_merge(m, (hipStream_t)stream));
 }
 
-GQA_API int gqa_attn_decode_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int Dv, int dtype)
+GQA_API int gqa_attn_decode_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int Dv, gqa_dtype dtype)
 {
     int rc = check_common(B, Hq, Hkv, Dk, Dv, 1.f, dtype);
     if (rc != GQA_OK) return rc;
@@ -337,7 +337,7 @@ static int topk_default_splits(int B, int Hq, int topk)
     return (int)s;
 }
 
-static int topk_shape_check(int B, int Hq, int topk, int Dk, int Dv, int dtype)
+static int topk_shape_check(int B, int Hq, int topk, int Dk, int Dv, gqa_dtype dtype)
 {
     int rc = check_common(B, Hq, 1, Dk, Dv, 1.f, dtype);
     if (rc != GQA_OK) return rc;
@@ -347,7 +347,7 @@ static int topk_shape_check(int B, int Hq, int topk, int Dk, int Dv, int dtype)
     return GQA_OK;
 }
 
-GQA_API int gqa_attn_decode_topk_splits(int B, int Hq, int topk, int Dk, int Dv, int dtype)
+GQA_API int gqa_attn_decode_topk_splits(int B, int Hq, int topk, int Dk, int Dv, gqa_dtype dtype)
 {
     int rc = topk_shape_check(B, Hq, topk, Dk, Dv, dtype);
     if (rc != GQA_OK) return rc;
@@ -357,7 +357,7 @@ GQA_API int gqa_attn_decode_topk_splits(int B, int Hq, int topk, int Dk, int Dv,
 GQA_API int gqa_attn_decode_topk(const void *q, const void *kv, void *out, const int *seq_lens,
                                  const int *indices, int B, int Hq, int Tmax, int topk, int Dk, int Dv,
                                  long long kv_sb, long long kv_st, float scale, int num_splits,
-                                 void *workspace, size_t workspace_bytes, int dtype, void *stream)
+                                 void *workspace, size_t workspace_bytes, gqa_dtype dtype, void *stream)
 {
     if (!q || !kv || !out || !seq_lens || !indices) return GQA_ERR_INVALID_ARG;
     int rc = check_common(B, Hq, 1, Dk, Dv, scale, dtype);
@@ -607,7 +607,7 @@ GQA_API int gqa_attn_decode(const void *q, const void *k, const void *v, void *o
                             const int *seq_lens, int B, int Hq, int Hkv, int Tmax, int Dk, int Dv,
                             long long k_sb, long long k_sh, long long k_st, long long v_sb,
                             long long v_sh, long long v_st, float scale, int num_splits,
-                            void *workspace, size_t workspace_bytes, int dtype, void *stream)
+                            void *workspace, size_t workspace_bytes, gqa_dtype dtype, void *stream)
 {
     return decode_impl(q, k, v, out, seq_lens, B, Hq, Hkv, Tmax, Dk, Dv, k_sb, k_sh, k_st, v_sb, v_sh, v_st,
                        scale, 0, num_splits, workspace, workspace_bytes, dtype, stream);
@@ -618,7 +618,7 @@ GQA_API int gqa_attn_decode_window(const void *q, const void *k, const void *v, 
                                    int Dv, long long k_sb, long long k_sh, long long k_st,
                                    long long v_sb, long long v_sh, long long v_st, float scale,
                                    int window, int num_splits, void *workspace,
-                                   size_t workspace_bytes, int dtype, void *stream)
+                                   size_t workspace_bytes, gqa_dtype dtype, void *stream)
 {
     return decode_impl(q, k, v, out, seq_lens, B, Hq, Hkv, Tmax, Dk, Dv, k_sb, k_sh, k_st, v_sb, v_sh, v_st,
                        scale, window, num_splits, workspace, workspace_bytes, dtype, stream);

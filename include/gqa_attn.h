@@ -77,7 +77,7 @@ enum {
  * Returns GQA_OK or a negative GQA_ERR_* code.
  */
 int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out, int B, int Hq, int Hkv,
-                 int Tq, int Tk, int Dk, int Dv, float scale, int causal, int dtype, void *stream);
+                 int Tq, int Tk, int Dk, int Dv, float scale, int causal, gqa_dtype dtype, void *stream);
 
 /*
  * Forward over packed variable-length sequences, with an optional sliding
@@ -129,7 +129,7 @@ int gqa_attn_fwd_varlen(const void *q, const void *k, const void *v, void *out, 
                         int num_seqs, int Hq, int Hkv, int total_q, int Dk,
                         int Dv, long long q_sh, long long q_st, long long k_sh, long long k_st, long long v_sh,
                         long long v_st, long long o_sh, long long o_st, float scale, int causal, int window,
-                        int dtype, void *stream);
+                        gqa_dtype dtype, void *stream);
 
 /*
  * Forward over one shard of the key axis, for sequence (context) parallelism:
@@ -158,7 +158,7 @@ int gqa_attn_fwd_varlen(const void *q, const void *k, const void *v, void *out, 
  */
 int gqa_attn_fwd_shard(const void *q, const void *k, const void *v, float *out, float *lse, int B,
                        int Hq, int Hkv, int Tq, int Tk, int Dk, int Dv, long long q_pos0,
-                       long long k_pos0, float scale, int causal, int dtype, void *stream);
+                       long long k_pos0, float scale, int causal, gqa_dtype dtype, void *stream);
 
 /*
  * Exact log-sum-exp merge of num_parts partial results of the same rows
@@ -171,7 +171,7 @@ int gqa_attn_fwd_shard(const void *q, const void *k, const void *v, float *out, 
  * 512; num_parts 1 .. 1024.
  */
 int gqa_attn_merge(const float *o_parts, const float *lse_parts, void *out, int num_parts,
-                   long long rows, int Dv, int out_dtype, void *stream);
+                   long long rows, int Dv, gqa_dtype out_dtype, void *stream);
 
 /*
  * Split count the decode entry point uses when called with num_splits = 0.
@@ -179,7 +179,7 @@ int gqa_attn_merge(const float *o_parts, const float *lse_parts, void *out, int 
  * workspace can be sized before any device call.  Host-only; returns >= 1,
  * or a negative GQA_ERR_* code for invalid or unsupported arguments.
  */
-int gqa_attn_decode_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int Dv, int dtype);
+int gqa_attn_decode_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int Dv, gqa_dtype dtype);
 
 /*
  * Bytes of device workspace gqa_attn_decode needs for num_splits splits
@@ -192,9 +192,13 @@ size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_splits);
 
 /*
  * Single-token decode over a KV cache, split over the key axis with a
- * log-sum-exp combine (flash-decoding style; the pages describe decode as
- * bound by reading the KV stream, and the online-softmax merge of partial
- * blocks as exact up to rounding).
+ * log-sum-exp combine.  A decode step reads the whole cached history and is
+ * bound by that KV stream ("Linear Attention 与 Sparse Attention 梳理",
+ * section 6.2 on decode; "Attention variants", KV Cache 成本 section, whose
+ * cache-size formula is the read per step); partial results over key blocks
+ * merge exactly by the online-softmax rescaling ("A Visual Guide to
+ * Attention", section on sources and execution), which is what the combine
+ * pass applies to the per-split (output, log-sum-exp) pairs.
  *
  *   q        [B, Hq, 1, Dk]  contiguous
  *   k, v     KV cache: element (b, h, t, d) at k[b*k_sb + h*k_sh + t*k_st + d]
@@ -226,7 +230,7 @@ size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_splits);
 int gqa_attn_decode(const void *q, const void *k, const void *v, void *out, const int *seq_lens,
                     int B, int Hq, int Hkv, int Tmax, int Dk, int Dv, long long k_sb, long long k_sh,
                     long long k_st, long long v_sb, long long v_sh, long long v_st, float scale,
-                    int num_splits, void *workspace, size_t workspace_bytes, int dtype,
+                    int num_splits, void *workspace, size_t workspace_bytes, gqa_dtype dtype,
                     void *stream);
 
 /*
@@ -272,7 +276,7 @@ int gqa_attn_decode_fp8(const void *q, const void *k, const void *v, const float
  * Split count gqa_attn_decode_topk uses when called with num_splits = 0
  * (shape only, host-only): >= 1, or a negative GQA_ERR_* code.
  */
-int gqa_attn_decode_topk_splits(int B, int Hq, int topk, int Dk, int Dv, int dtype);
+int gqa_attn_decode_topk_splits(int B, int Hq, int topk, int Dk, int Dv, gqa_dtype dtype);
 
 /*
  * Top-k sparse single-token decode on the absorbed-MLA cache: DeepSeek Sparse
@@ -309,7 +313,7 @@ int gqa_attn_decode_topk_splits(int B, int Hq, int topk, int Dk, int Dv, int dty
 int gqa_attn_decode_topk(const void *q, const void *kv, void *out, const int *seq_lens,
                          const int *indices, int B, int Hq, int Tmax, int topk, int Dk, int Dv,
                          long long kv_sb, long long kv_st, float scale, int num_splits,
-                         void *workspace, size_t workspace_bytes, int dtype, void *stream);
+                         void *workspace, size_t workspace_bytes, gqa_dtype dtype, void *stream);
 
 /*
  * gqa_attn_decode with a sliding window ("A Visual Guide to Attention",
@@ -327,7 +331,7 @@ int gqa_attn_decode_window(const void *q, const void *k, const void *v, void *ou
                            const int *seq_lens, int B, int Hq, int Hkv, int Tmax, int Dk, int Dv,
                            long long k_sb, long long k_sh, long long k_st, long long v_sb,
                            long long v_sh, long long v_st, float scale, int window, int num_splits,
-                           void *workspace, size_t workspace_bytes, int dtype, void *stream);
+                           void *workspace, size_t workspace_bytes, gqa_dtype dtype, void *stream);
 
 /* Static, thread-safe description of a GQA_* return code. */
 const char *gqa_attn_strerror(int code);
