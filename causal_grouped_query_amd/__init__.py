@@ -8,6 +8,7 @@ stream.  There is no fallback: if the library is missing, every call raises.
     attention_varlen(q, k, v, cu_q, cu_k, scale=None, causal=True, window=0)
                                                       packed variable-length forward, sliding window
     decode(q, k_cache, v_cache, seq_lens, scale=None) split-KV single-token decode
+    decode_noalloc(q, k_cache, v_cache, seq_lens, out) the same decode with no device allocation
     decode_topk(q, kv_cache, seq_lens, indices)       top-k sparse (DSA) decode, absorbed MLA
     decode_fp8(q, k_codes, v_codes, k_scale, v_scale, seq_lens)
                                                       decode over an FP8 E4M3 cache with row scales
@@ -26,7 +27,7 @@ import os
 
 __all__ = [
     "LIB_PATH", "GQA_BF16", "GQA_F32", "GQAError", "lib", "attention", "attention_varlen", "decode",
-    "decode_splits", "decode_workspace_size", "decode_topk", "decode_topk_splits", "decode_fp8", "attention_shard", "merge", "strerror",
+    "decode_splits", "decode_workspace_size", "decode_noalloc", "decode_noalloc_scratch_bytes", "decode_topk", "decode_topk_splits", "decode_fp8", "attention_shard", "merge", "strerror",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_attn.so")
@@ -36,7 +37,7 @@ GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP
 EXPORTS = ("gqa_attn_fwd", "gqa_attn_fwd_varlen", "gqa_attn_decode", "gqa_attn_decode_splits",
            "gqa_attn_decode_workspace_size", "gqa_attn_decode_topk", "gqa_attn_decode_topk_splits",
            "gqa_attn_decode_fp8", "gqa_attn_fwd_shard", "gqa_attn_merge", "gqa_attn_decode_window",
-           "gqa_attn_strerror")
+           "gqa_attn_decode_noalloc", "gqa_attn_decode_noalloc_scratch_bytes", "gqa_attn_strerror")
 
 _lib = None
 
@@ -82,6 +83,10 @@ def lib() -> ctypes.CDLL:
         L.gqa_attn_fwd_shard.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, LL, LL, F, I, I, P]
         L.gqa_attn_merge.restype = I
         L.gqa_attn_merge.argtypes = [P, P, P, I, LL, I, I, P]
+        L.gqa_attn_decode_noalloc.restype = I
+        L.gqa_attn_decode_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, I, LL, LL, LL, LL, LL, LL, F, I, I, P]
+        L.gqa_attn_decode_noalloc_scratch_bytes.restype = SZ
+        L.gqa_attn_decode_noalloc_scratch_bytes.argtypes = [I, I, I, I, I]
         L.gqa_attn_strerror.restype = ctypes.c_char_p
         L.gqa_attn_strerror.argtypes = [I]
         _lib = L
@@ -219,14 +224,8 @@ def decode_workspace_size(B: int, Hq: int, Dv: int, num_splits: int) -> int:
     return int(lib().gqa_attn_decode_workspace_size(B, Hq, Dv, num_splits))
 
 
-def decode(q, k_cache, v_cache, seq_lens, scale: float | None = None, num_splits: int = 0, out=None,
-           workspace=None, window: int = 0):
-    """Single-token decode: q [B,Hq,1,Dk] over caches [B,Hkv,Tmax,D] holding seq_lens[b] keys.
-
-    seq_lens: int32 device tensor [B].  Cache slots at or past seq_lens[b] are
-    never read into the result.  num_splits = 0 lets the library choose.
-    window = w > 0: only the last min(seq_lens[b], w) keys (sliding window).
-    """
+def _decode_shapes(q, k_cache, v_cache, seq_lens):
+    """Checks shared by the decode wrappers; returns B, Hq, Hkv, Tmax, Dk, Dv."""
     import torch
     _check_cuda(q, k_cache, v_cache, seq_lens)
     if q.dim() != 4 or q.shape[2] != 1 or not q.is_contiguous():
@@ -244,6 +243,19 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float | None = None, num_splits
     Bv, Hkv2, Tmax2, Dv = v_cache.shape
     if not (B == Bk == Bv == seq_lens.shape[0] and Hkv == Hkv2 and Tmax == Tmax2 and Dk == Dk2):
         raise ValueError("inconsistent q / cache / seq_lens shapes")
+    return B, Hq, Hkv, Tmax, Dk, Dv
+
+
+def decode(q, k_cache, v_cache, seq_lens, scale: float | None = None, num_splits: int = 0, out=None,
+           workspace=None, window: int = 0):
+    """Single-token decode: q [B,Hq,1,Dk] over caches [B,Hkv,Tmax,D] holding seq_lens[b] keys.
+
+    seq_lens: int32 device tensor [B].  Cache slots at or past seq_lens[b] are
+    never read into the result.  num_splits = 0 lets the library choose.
+    window = w > 0: only the last min(seq_lens[b], w) keys (sliding window).
+    """
+    import torch
+    B, Hq, Hkv, Tmax, Dk, Dv = _decode_shapes(q, k_cache, v_cache, seq_lens)
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(Dk)
@@ -274,6 +286,33 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float | None = None, num_splits
     if rc != GQA_OK:
         raise GQAError(rc, where)
     return out
+
+
+def decode_noalloc(q, k_cache, v_cache, seq_lens, out, scale: float | None = None, num_splits: int = 0):
+    """decode() through gqa_attn_decode_noalloc: the split partials live in
+    the library's per-GPU scratch array, so the call allocates nothing (out
+    is the caller's [B,Hq,1,Dv] tensor).  Calls that overlap on one GPU race
+    on that array; a shape whose partials exceed it raises GQAError
+    (GQA_ERR_WORKSPACE)."""
+    B, Hq, Hkv, Tmax, Dk, Dv = _decode_shapes(q, k_cache, v_cache, seq_lens)
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(Dk)
+    _check_cuda(out)
+    if out.shape != (B, Hq, 1, Dv) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B,Hq,1,Dv] tensor of q's dtype")
+    ks, vs = k_cache.stride(), v_cache.stride()
+    rc = lib().gqa_attn_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), out.data_ptr(),
+                                       seq_lens.data_ptr(), B, Hq, Hkv, Tmax, Dk, Dv, ks[0], ks[1], ks[2], vs[0],
+                                       vs[1], vs[2], float(scale), int(num_splits), code, _stream())
+    if rc != GQA_OK:
+        raise GQAError(rc, "gqa_attn_decode_noalloc")
+    return out
+
+
+def decode_noalloc_scratch_bytes(B: int, Hq: int, Dv: int, num_splits: int, dtype_code: int) -> int:
+    """Bytes of the per-GPU scratch a decode_noalloc shape needs (0: invalid)."""
+    return int(lib().gqa_attn_decode_noalloc_scratch_bytes(B, Hq, Dv, num_splits, dtype_code))
 
 
 def decode_topk_splits(B: int, Hq: int, topk: int, Dk: int, Dv: int, dtype_code: int) -> int:

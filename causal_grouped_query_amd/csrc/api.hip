@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gqa_attn.h"
 #include "launch.h"
 
@@ -506,11 +508,27 @@ GQA_API size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_spl
     return ws_bytes(B, Hq, Dv, num_splits);
 }
 
+// Workspace layouts of the decode: the caller-sized one (room for fp32
+// partial outputs [B, Hq, S, Dv], then the fp32 partial LSE [B, Hq, S]) and
+// the compact one of the allocation-free entry point (partial outputs in the
+// element type the kernels store -- bf16 on the bf16 path, fp32 on the fp32
+// path -- then the LSE at the next 256-byte boundary).
+static size_t compact_ws_lse_offset(int B, int Hq, int Dv, int S, int dtype)
+{
+    const size_t rows = (size_t)B * Hq * S;
+    const size_t o_bytes = rows * Dv * (dtype == GQA_BF16 ? 2 : 4);
+    return (o_bytes + 255) & ~(size_t)255;
+}
+static size_t compact_ws_bytes(int B, int Hq, int Dv, int S, int dtype)
+{
+    return compact_ws_lse_offset(B, Hq, Dv, S, dtype) + (size_t)B * Hq * S * sizeof(float);
+}
+
 static int decode_impl(const void *q, const void *k, const void *v, void *out, const int *seq_lens, int B,
                        int Hq, int Hkv, int Tmax, int Dk, int Dv, long long k_sb, long long k_sh,
                        long long k_st, long long v_sb, long long v_sh, long long v_st, float scale,
                        int window, int num_splits, void *workspace, size_t workspace_bytes, int dtype,
-                       void *stream)
+                       void *stream, bool compact = false, bool dry_run = false)
 {
     if (!q || !k || !v || !out || !seq_lens) return GQA_ERR_INVALID_ARG;
     if (window < 0) return GQA_ERR_INVALID_ARG;
@@ -538,7 +556,7 @@ static int decode_impl(const void *q, const void *k, const void *v, void *out, c
     if (!aligned(seq_lens, 4)) return GQA_ERR_INVALID_ARG;
 
     const int S = num_splits ? num_splits : default_splits(B, Hq, Hkv, Tmax, Dk, dtype);
-    const size_t need = ws_bytes(B, Hq, Dv, S);
+    const size_t need = compact ? compact_ws_bytes(B, Hq, Dv, S, dtype) : ws_bytes(B, Hq, Dv, S);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return GQA_ERR_WORKSPACE;
 
     const int G = Hq / Hkv;
@@ -553,7 +571,8 @@ static int decode_impl(const void *q, const void *k, const void *v, void *out, c
     a.v = v;
     a.lens = seq_lens;
     a.part_o = (float *)workspace;
-    a.part_lse = (float *)workspace + (size_t)B * Hq * S * Dv;
+    a.part_lse = compact ? (float *)((char *)workspace + compact_ws_lse_offset(B, Hq, Dv, S, dtype))
+                         : (float *)workspace + (size_t)B * Hq * S * Dv;
     a.B = B;
     a.Hq = Hq;
     a.Hkv = Hkv;
@@ -580,12 +599,14 @@ static int decode_impl(const void *q, const void *k, const void *v, void *out, c
             a.n_wg = gqa::decode_bf16_flat_workgroups(Dk);
         }
         a.c = folded_scale(scale);
+        if (dry_run) return GQA_OK;
         (void)hipGetLastError();
         rc = gqa::launch_decode_bf16(a, Dk, Dv, st);
     } else {
         if (Hq > 65535 || B > 65535) return GQA_ERR_UNSUPPORTED;
         a.n_hblk = 1;
         a.c = scale;  // the fp32 path works in natural-log units
+        if (dry_run) return GQA_OK;
         (void)hipGetLastError();
         rc = gqa::launch_decode_f32(a, Dk, st);
     }
@@ -622,4 +643,62 @@ GQA_API int gqa_attn_decode_window(const void *q, const void *k, const void *v, 
 {
     return decode_impl(q, k, v, out, seq_lens, B, Hq, Hkv, Tmax, Dk, Dv, k_sb, k_sh, k_st, v_sb, v_sh, v_st,
                        scale, window, num_splits, workspace, workspace_bytes, dtype, stream);
+}
+
+// ---- allocation-free decode ----
+//
+// The scratch of gqa_attn_decode_noalloc: one array per GPU for the life of
+// the process.  In host code `scratch` names a host-side stand-in, not the
+// device array, so it is never passed to a kernel or a copy: its device
+// address is looked up once per device (hipGetSymbolAddress, with that device
+// current) and kept in scratch_dev[].  Every call on a device uses the same
+// array, so calls that overlap on one GPU race on it.  Nothing in it has to
+// start at zero: the partial kernels write every slot the combine reads.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)GQA_DECODE_NOALLOC_MAX_SCRATCH;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+void *scratch_dev[kMaxDevices];
+std::mutex scratch_mu;
+
+// device address of this device's scratch array, or null on a HIP error
+void *scratch_for_current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        scratch_dev[dev] = ptr;
+    }
+    return scratch_dev[dev];
+}
+
+} // namespace
+
+GQA_API size_t gqa_attn_decode_noalloc_scratch_bytes(int B, int Hq, int Dv, int num_splits, gqa_dtype dtype)
+{
+    if (B <= 0 || Hq <= 0 || Dv <= 0 || num_splits <= 0 || num_splits > kMaxSplits) return 0;
+    if (dtype != GQA_BF16 && dtype != GQA_F32) return 0;
+    return compact_ws_bytes(B, Hq, Dv, num_splits, dtype);
+}
+
+GQA_API int gqa_attn_decode_noalloc(const void *q, const void *k, const void *v, void *out,
+                                    const int *seq_lens, int B, int Hq, int Hkv, int Tmax, int Dk, int Dv,
+                                    long long k_sb, long long k_sh, long long k_st, long long v_sb,
+                                    long long v_sh, long long v_st, float scale, int num_splits,
+                                    gqa_dtype dtype, void *stream)
+{
+    // every argument is checked before the first HIP call (a dry run with a
+    // stand-in workspace address that is never used); a shape whose partials
+    // do not fit the scratch returns GQA_ERR_WORKSPACE
+    int rc = decode_impl(q, k, v, out, seq_lens, B, Hq, Hkv, Tmax, Dk, Dv, k_sb, k_sh, k_st, v_sb, v_sh, v_st,
+                         scale, 0, num_splits, (void *)(uintptr_t)256, kScratchBytes, dtype, stream, true, true);
+    if (rc != GQA_OK) return rc;
+    void *ws = scratch_for_current_device();
+    if (!ws) return GQA_ERR_HIP;
+    return decode_impl(q, k, v, out, seq_lens, B, Hq, Hkv, Tmax, Dk, Dv, k_sb, k_sh, k_st, v_sb, v_sh, v_st,
+                       scale, 0, num_splits, ws, kScratchBytes, dtype, stream, true);
 }

@@ -333,6 +333,36 @@ int gqa_attn_decode_window(const void *q, const void *k, const void *v, void *ou
                            long long v_sh, long long v_st, float scale, int window, int num_splits,
                            void *workspace, size_t workspace_bytes, gqa_dtype dtype, void *stream);
 
+/*
+ * gqa_attn_decode for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, rules, shapes and result as gqa_attn_decode, without the
+ * workspace: the split partials live in a device array the library holds
+ * for the life of the process, one per GPU, of GQA_DECODE_NOALLOC_MAX_SCRATCH
+ * bytes.  The call allocates nothing; its first call on a device looks up
+ * that device's array (hipGetSymbolAddress) with the device current.
+ *
+ * A shape needs gqa_attn_decode_noalloc_scratch_bytes(B, Hq, Dv, S, dtype)
+ * bytes of it for S splits (num_splits, or gqa_attn_decode_splits() when 0):
+ * B*Hq*S partial outputs of Dv elements (bf16 for GQA_BF16, fp32 for GQA_F32)
+ * plus B*Hq*S fp32 log-sum-exp values.  A shape that needs more returns
+ * GQA_ERR_WORKSPACE with nothing enqueued (e.g. B = 64, Hq = 32, Dv = 128,
+ * S = 10 needs 5.3 MB; the absorbed-MLA B = 16, Hq = 128, Dv = 512, S = 16
+ * needs 33.7 MB).
+ *
+ * Calls on one GPU share its array: calls that overlap in time on that GPU
+ * (different streams, or other processes' threads sharing this library
+ * instance) race and corrupt each other's partials; order them on one
+ * stream.  The array keeps the last call's contents; nothing in it needs to
+ * start zeroed (every slot a call's combine reads is written by that call).
+ */
+#define GQA_DECODE_NOALLOC_MAX_SCRATCH (64u << 20)
+size_t gqa_attn_decode_noalloc_scratch_bytes(int B, int Hq, int Dv, int num_splits, gqa_dtype dtype);
+int gqa_attn_decode_noalloc(const void *q, const void *k, const void *v, void *out, const int *seq_lens,
+                            int B, int Hq, int Hkv, int Tmax, int Dk, int Dv, long long k_sb,
+                            long long k_sh, long long k_st, long long v_sb, long long v_sh,
+                            long long v_st, float scale, int num_splits, gqa_dtype dtype, void *stream);
+
 /* Static, thread-safe description of a GQA_* return code. */
 const char *gqa_attn_strerror(int code);
 

@@ -239,3 +239,36 @@ def test_decode_window_rejects_on_host():
     assert L.gqa_attn_decode_window(*args, -1, 0, FAKE, 1 << 30, BF16, None) == INVALID
     assert L.gqa_attn_decode_window(*args, 4, 0, 0, 1 << 30, BF16, None) == WS
     assert L.gqa_attn_decode_window(*(args[:9] + [96, 96] + args[11:]), 4, 0, FAKE, 1 << 30, BF16, None) == UNSUP
+
+
+def test_decode_noalloc_rejects_on_host():
+    """gqa_attn_decode_noalloc checks every argument before its first HIP
+    call: rejected calls here never reach the device (there is none)."""
+    D, H, T, B, Hq = 128, 2, 64, 2, 8
+    L = gqa.lib()
+
+    def call(q=FAKE, Hq_=Hq, Hkv=H, Dk=D, Dv=D, S=0, dtype=BF16, B_=B, k=FAKE, v=FAKE, kst=D):
+        return L.gqa_attn_decode_noalloc(q, k, v, FAKE, FAKE, B_, Hq_, Hkv, T, Dk, Dv, Hkv * T * kst, T * kst, kst,
+                                         Hkv * T * kst, T * kst, kst, 0.1, S, dtype, None)
+    assert call(q=0) == INVALID
+    assert call(Hq_=6, Hkv=4) == INVALID
+    assert call(S=-1) == INVALID
+    assert call(S=1025) == INVALID
+    assert call(dtype=7) == INVALID
+    assert call(Dk=96, Dv=96) == UNSUP
+    # absorbed-MLA shape whose partials exceed the scratch: B = 1024 sequences
+    # of 128 heads, 16 splits of 512 bf16 values
+    assert call(B_=1024, Hq_=128, Hkv=1, Dk=576, Dv=512, S=16, kst=576) == WS
+    # the fp32 path stores fp32 partials: 4 bytes per value
+    assert call(B_=4096, Hq_=32, Hkv=8, S=64, dtype=F32) == WS
+
+
+def test_decode_noalloc_scratch_sizes():
+    # bf16 partials (2 bytes) then the fp32 lse at the next 256-byte boundary
+    rows = 64 * 32 * 10
+    assert gqa.decode_noalloc_scratch_bytes(64, 32, 128, 10, BF16) == rows * 128 * 2 + rows * 4
+    rows = 16 * 128 * 16
+    assert gqa.decode_noalloc_scratch_bytes(16, 128, 512, 16, BF16) == rows * 512 * 2 + rows * 4
+    assert gqa.decode_noalloc_scratch_bytes(1, 1, 3, 1, F32) == 256 + 4
+    assert gqa.decode_noalloc_scratch_bytes(0, 32, 128, 10, BF16) == 0
+    assert gqa.decode_noalloc_scratch_bytes(1, 32, 128, 10, 9) == 0
