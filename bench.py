@@ -8,7 +8,8 @@ synthetic N(0,1) tensors already resident in HBM.  `value` is the prefill
 throughput in TFLOP/s (algorithmic FLOPs: 2*(Dk+Dv) per visible causal
 (query, key) pair per query head); the decode KV read rate is reported next
 to it.  Per-kernel times come from HIP events recorded on the stream the
-library launches on (torch's current stream).
+library launches on (torch's current stream); `value` and the roofline
+figures use the median launch, the mean is reported beside it.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-extra]
 
@@ -295,15 +296,17 @@ def main() -> int:
     F = fwd_flops(wp)
     lens_list = lens_cpu.tolist()
     DB = decode_bytes(wd, lens_list)
-    pre_tflops = F / t_pre / 1e12
-    dec_gbps = DB / t_dec / 1e9
+    # rates at the median launch (the mean is reported beside it)
+    pre_tflops = F / t_pre_med / 1e12
+    dec_gbps = DB / t_dec_med / 1e9
 
     tr = traffic_for("fwd_bf16_kernel")
     roofline = {
         "kernel": "fwd_bf16_kernel<128> (gqa_attn_fwd, one launch per step)",
         "bound": "mfma", "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4), "traffic": tr,
-        "avg_launch_us": round(t_pre * 1e6, 2), "median_launch_us": round(t_pre_med * 1e6, 2),
+        "median_launch_us": round(t_pre_med * 1e6, 2), "avg_launch_us": round(t_pre * 1e6, 2),
+        "frac_at_avg": round(F / t_pre / 1e12 / PEAK_BF16_TFLOPS, 4),
         "flop_per_launch": F,
     }
     trd = traffic_for("decode_bf16_flat_kernel")
@@ -311,7 +314,8 @@ def main() -> int:
         "kernel": f"decode_bf16_flat_kernel<128,128> + combine_kernel (gqa_attn_decode, balanced, {S} slots)",
         "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
         "frac": round(dec_gbps / PEAK_HBM_GBPS, 4), "traffic": trd,
-        "avg_launch_us": round(t_dec * 1e6, 2), "median_launch_us": round(t_dec_med * 1e6, 2),
+        "median_launch_us": round(t_dec_med * 1e6, 2), "avg_launch_us": round(t_dec * 1e6, 2),
+        "frac_at_avg": round(DB / t_dec / 1e9 / PEAK_HBM_GBPS, 4),
         "kv_bytes_per_launch": DB, "sum_len": int(sum(lens_list)),
     }
 
@@ -622,39 +626,84 @@ def _cpu_model() -> str:
 
 
 def cpu_baseline(target_s: float):
-    """The fp64 oracle as it stands, on this host's cores, over a bounded random
-    sample of the prefill workload's rows; rate scaled to TFLOP/s of the same
-    algorithmic FLOP count."""
+    """The fp64 oracle as it stands, on this host's cores, on all five headline
+    workloads with the same seeded inputs: the tiny fp32 one and the GQA decode
+    in full, the GQA prefill, MQA suffix and absorbed-MLA decode on a random
+    row sample of about target_s / 3 seconds each.  Rates are the workload's
+    algorithmic FLOPs of the rows done per second; `value` is the GQA
+    prefill's, in the unit of the metric."""
     import numpy as np
     import workloads as W
     from oracle import oracle as O
 
-    w = W.GQA_PREFILL
-    q, k, v = W.fwd_inputs(w)
     threads = O.max_threads()
     rng = np.random.default_rng(12345)
-    n_rows_total = w.B * w.Hq * w.Tq
-    done_rows, done_flops, elapsed = 0, 0.0, 0.0
-    batch = 2048
-    while elapsed < target_s and done_rows < n_rows_total:
-        rows = rng.integers(0, n_rows_total, size=batch)
-        i = rows % w.Tq
-        flops = float(np.sum(2.0 * (w.Dk + w.Dv) * (i + 1)))  # square causal: row i sees i+1 keys
-        t0 = time.perf_counter()
-        O.attention(q, k, v, w.scale, True, rows=rows, threads=threads)
-        elapsed += time.perf_counter() - t0
-        done_rows += batch
-        done_flops += flops
-        if elapsed < 1.0:
-            batch *= 2
+    per = {}
+
+    def run(name, q, k, v, scale, flops_of_row, n_rows, lens=None, budget=None):
+        """Rows of one workload, all of them or a sampled stream of batches
+        until the budget is spent; returns the per-workload record."""
+        done_rows, done_flops, elapsed, batch = 0, 0.0, 0.0, 4 * threads
+        while done_rows < n_rows and (budget is None or elapsed < budget):
+            if budget is None:
+                rows = np.arange(n_rows, dtype=np.int64)
+            else:
+                rows = rng.integers(0, n_rows, size=min(batch, n_rows))
+            t0 = time.perf_counter()
+            O.attention(q, k, v, scale, True, kv_lens=lens, rows=rows, threads=threads)
+            elapsed += time.perf_counter() - t0
+            done_rows += rows.size
+            done_flops += float(sum(flops_of_row(int(r)) for r in rows))
+            if budget is not None:
+                # next batch: twice this one, but no more than the rest of the budget at the rate so far
+                rate = done_rows / elapsed
+                batch = max(threads, min(2 * batch, int(rate * (budget - elapsed))))
+        per[name] = {"GFLOP/s": round(done_flops / elapsed / 1e9, 3), "seconds": round(elapsed, 2),
+                     "rows": int(done_rows), "rows_total": int(n_rows),
+                     "sample": "all rows" if budget is None else "uniform random rows"}
+        return per[name]
+
+    def fwd_row_flops(w):
+        off = w.Tk - w.Tq
+        return lambda r: 2.0 * (w.Dk + w.Dv) * min(w.Tk, off + r % w.Tq + 1)
+
+    each = target_s / 3.0
+    # tiny fp32: prefill rows, then its decode step (the last query over all keys)
+    w = W.TINY_F32
+    q, k, v = W.fwd_inputs(w)
+    run(w.name, q, k, v, w.scale, fwd_row_flops(w), w.B * w.Hq * w.Tq)
+    # GQA prefill (the metric's workload): sampled rows
+    w = W.GQA_PREFILL
+    q, k, v = W.fwd_inputs(w)
+    head = run(w.name, q, k, v, w.scale, fwd_row_flops(w), w.B * w.Hq * w.Tq, budget=each)
+    del q, k, v
+    # GQA decode: every (sequence, head) row over its cached length
+    w = W.GQA_DECODE
+    q, k, v, lens = W.decode_inputs(w, nan_tail=False)
+    ll = lens.tolist()
+    run(w.name, q, k, v, w.scale, lambda r: 2.0 * (w.Dk + w.Dv) * ll[r // w.Hq], w.B * w.Hq, lens=ll)
+    del q, k, v
+    # MQA suffix: sampled rows
+    w = W.MQA_SUFFIX
+    q, k, v = W.fwd_inputs(w)
+    run(w.name, q, k, v, w.scale, fwd_row_flops(w), w.B * w.Hq * w.Tq, budget=each)
+    del q, k, v
+    # absorbed MLA decode (V is the latent prefix of K): sampled rows
+    w = W.MLA_DECODE
+    q, k, v, lens = W.decode_inputs(w, nan_tail=False)
+    ll = lens.tolist()
+    run(w.name, q, k, v, w.scale, lambda r: 2.0 * (w.Dk + w.Dv) * ll[r // w.Hq], w.B * w.Hq, lens=ll,
+        budget=each)
+    del q, k, v
     return {
-        "value": done_flops / elapsed / 1e12,
+        "value": head["GFLOP/s"] / 1e3,
         "unit": "TFLOP/s",
         "cores": threads,
         "cpu_model": _cpu_model(),
         "kind": "oracle",
-        "sample": f"{done_rows} uniformly drawn query rows (of {n_rows_total}) of {w.name}, fp64, "
-                  f"{elapsed:.1f} s",
+        "sample": (f"{head['rows']} uniformly drawn query rows (of {head['rows_total']}) of {W.GQA_PREFILL.name}, "
+                   f"fp64, {head['seconds']} s; all five workloads under 'configs'"),
+        "configs": per,
     }
 
 
