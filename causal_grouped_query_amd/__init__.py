@@ -26,8 +26,9 @@ import math
 import os
 
 __all__ = [
-    "LIB_PATH", "GQA_BF16", "GQA_F32", "GQAError", "lib", "attention", "attention_varlen", "decode",
-    "decode_splits", "decode_workspace_size", "decode_noalloc", "decode_noalloc_scratch_bytes", "decode_topk", "decode_topk_splits", "decode_fp8", "attention_shard", "merge", "strerror",
+    "LIB_PATH", "GQA_BF16", "GQA_F32", "GQAError", "lib", "attention", "attention_varlen", "check_cu_seqlens",
+    "decode",
+    "decode_splits", "decode_workspace_size", "decode_noalloc", "decode_noalloc_scratch_bytes", "decode_topk", "decode_topk_splits", "check_topk_distinct", "decode_fp8", "attention_shard", "merge", "strerror",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_attn.so")
@@ -61,8 +62,8 @@ def lib() -> ctypes.CDLL:
         L.gqa_attn_fwd.restype = I
         L.gqa_attn_fwd.argtypes = [P, P, P, P, I, I, I, I, I, I, I, F, I, I, P]
         L.gqa_attn_fwd_varlen.restype = I
-        L.gqa_attn_fwd_varlen.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, LL, LL, LL, LL, LL, LL, LL, LL, F,
-                                          I, I, I, P]
+        L.gqa_attn_fwd_varlen.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, LL, LL, LL, LL, LL, LL, LL, LL,
+                                          F, I, I, I, P]
         L.gqa_attn_decode_splits.restype = I
         L.gqa_attn_decode_splits.argtypes = [I, I, I, I, I, I, I]
         L.gqa_attn_decode_workspace_size.restype = SZ
@@ -156,8 +157,24 @@ def _token_strides(t, name):
     return t.stride(1), t.stride(0)
 
 
+def check_cu_seqlens(cu, total: int, name: str = "cu_seqlens") -> None:
+    """Host-side check of packed-sequence offsets (a list, array or CPU
+    tensor): non-decreasing, starting at or above 0, ending at or below
+    `total` token slots.  Raises ValueError otherwise."""
+    vals = [int(x) for x in (cu.tolist() if hasattr(cu, "tolist") else cu)]
+    if len(vals) < 2:
+        raise ValueError(f"{name} needs num_seqs + 1 >= 2 offsets")
+    if vals[0] < 0:
+        raise ValueError(f"{name}[0] = {vals[0]} is negative")
+    for i in range(len(vals) - 1):
+        if vals[i + 1] < vals[i]:
+            raise ValueError(f"{name} decreases at {i}: {vals[i]} -> {vals[i + 1]}")
+    if vals[-1] > total:
+        raise ValueError(f"{name}[-1] = {vals[-1]} exceeds the {total} token slots of the tensor")
+
+
 def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float | None = None, causal: bool = True,
-                     window: int = 0, out=None, seqused_q=None, seqused_k=None):
+                     window: int = 0, out=None, seqused_q=None, seqused_k=None, validate: bool = False):
     """Packed variable-length forward.  q [total_q, Hq, Dk], k [total_k, Hkv, Dk],
     v [total_k, Hkv, Dv] (any strides with unit-stride D), bfloat16; sequence i
     owns tokens cu_seqlens[i] .. cu_seqlens[i+1]-1 (int32 device tensors of
@@ -166,6 +183,9 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float | None = 
     seqused_q / seqused_k (int32 device tensors of num_seqs entries, optional):
     only the first seqused[i] tokens of slot i are used, the rest is padding;
     padded query rows of out are not written.  Returns out [total_q, Hq, Dv].
+    The kernel clamps every sequence to the tensors' token extents; with
+    validate=True the offsets are also copied to the host and checked
+    (check_cu_seqlens), which synchronises with the device.
     """
     import torch
     _check_cuda(q, k, v, cu_seqlens_q, cu_seqlens_k)
@@ -195,6 +215,9 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float | None = 
     if Dk != Dk2 or v.shape[1] != Hkv or v.shape[0] != k.shape[0]:
         raise ValueError("inconsistent q/k/v shapes")
     n = cu_seqlens_q.numel() - 1
+    if validate:
+        check_cu_seqlens(cu_seqlens_q.cpu(), total_q, "cu_seqlens_q")
+        check_cu_seqlens(cu_seqlens_k.cpu(), k.shape[0], "cu_seqlens_k")
     if scale is None:
         scale = 1.0 / math.sqrt(Dk)
     if out is None:
@@ -206,7 +229,7 @@ def attention_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, scale: float | None = 
     o_sh, o_st = _token_strides(out, "out")
     rc = lib().gqa_attn_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                    cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), used[0], used[1], n, Hq, Hkv,
-                                   total_q, Dk, Dv, q_sh, q_st, k_sh, k_st, v_sh, v_st, o_sh, o_st,
+                                   total_q, k.shape[0], Dk, Dv, q_sh, q_st, k_sh, k_st, v_sh, v_st, o_sh, o_st,
                                    float(scale), int(bool(causal)), int(window), _dtype_code(q), _stream())
     if rc != GQA_OK:
         raise GQAError(rc, "gqa_attn_fwd_varlen")
@@ -322,12 +345,27 @@ def decode_topk_splits(B: int, Hq: int, topk: int, Dk: int, Dv: int, dtype_code:
     return s
 
 
+def check_topk_distinct(indices, seq_lens) -> None:
+    """Host-side check that no row of a top-k list (CPU tensor or array
+    [B, topk]) names a valid position twice; raises ValueError otherwise."""
+    import numpy as np
+    idx = np.asarray(indices.cpu() if hasattr(indices, "cpu") else indices)
+    lens = np.asarray(seq_lens.cpu() if hasattr(seq_lens, "cpu") else seq_lens)
+    for b in range(idx.shape[0]):
+        row = idx[b][(idx[b] >= 0) & (idx[b] < lens[b])]
+        if np.unique(row).size != row.size:
+            raise ValueError(f"indices row {b} lists a position more than once")
+
+
 def decode_topk(q, kv_cache, seq_lens, indices, Dv: int = 512, scale: float | None = None,
-                num_splits: int = 0, out=None, workspace=None):
+                num_splits: int = 0, out=None, workspace=None, validate: bool = False):
     """Top-k sparse decode on the absorbed-MLA cache: q [B,Hq,1,Dk] attends
     only to the cache positions listed in indices [B, topk] (int32; entries
     outside [0, seq_lens[b]) select nothing).  kv_cache [B,1,Tmax,Dk] (or
-    [B,Tmax,Dk]); the value is its first Dv columns.  Returns [B,Hq,1,Dv]."""
+    [B,Tmax,Dk]); the value is its first Dv columns.  Returns [B,Hq,1,Dv].
+    A position repeated inside one slice of the list counts once; repeats
+    across slices count once per slice (see the C header).  validate=True
+    checks on the host that no row repeats a position (synchronises)."""
     import torch
     _check_cuda(q, kv_cache, seq_lens, indices)
     if q.dim() != 4 or q.shape[2] != 1 or not q.is_contiguous():
@@ -345,6 +383,8 @@ def decode_topk(q, kv_cache, seq_lens, indices, Dv: int = 512, scale: float | No
     if kv.shape[0] != B or kv.shape[2] != Dk or seq_lens.shape[0] != B or indices.shape[0] != B:
         raise ValueError("inconsistent q / cache / seq_lens / indices shapes")
     Tmax, topk = kv.shape[1], indices.shape[1]
+    if validate:
+        check_topk_distinct(indices, seq_lens)
     code = _dtype_code(q)
     if scale is None:
         scale = 1.0 / math.sqrt(Dk)

@@ -196,7 +196,7 @@ GQA_API int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out,
 GQA_API int gqa_attn_fwd_varlen(const void *q, const void *k, const void *v, void *out,
                                 const int *cu_seqlens_q, const int *cu_seqlens_k,
                                 const int *seqused_q, const int *seqused_k, int num_seqs, int Hq,
-                                int Hkv, int total_q, int Dk, int Dv, long long q_sh, long long q_st,
+                                int Hkv, int total_q, int total_k, int Dk, int Dv, long long q_sh, long long q_st,
                                 long long k_sh, long long k_st, long long v_sh, long long v_st,
                                 long long o_sh, long long o_st, float scale, int causal, int window,
                                 gqa_dtype dtype, void *stream)
@@ -204,7 +204,7 @@ GQA_API int gqa_attn_fwd_varlen(const void *q, const void *k, const void *v, voi
     if (!q || !k || !v || !out || !cu_seqlens_q || !cu_seqlens_k) return GQA_ERR_INVALID_ARG;
     int rc = check_common(num_seqs, Hq, Hkv, Dk, Dv, scale, dtype);
     if (rc != GQA_OK) return rc;
-    if (total_q < 0) return GQA_ERR_INVALID_ARG;
+    if (total_q < 0 || total_k < 0) return GQA_ERR_INVALID_ARG;
     if (causal != 0 && causal != 1) return GQA_ERR_INVALID_ARG;
     if (window < 0 || (window > 0 && !causal)) return GQA_ERR_INVALID_ARG;
     const long long in_strides[6] = {q_sh, q_st, k_sh, k_st, v_sh, v_st};
@@ -236,6 +236,8 @@ GQA_API int gqa_attn_fwd_varlen(const void *q, const void *k, const void *v, voi
     a.causal = causal;
     a.c = folded_scale(scale);
     a.varlen = 1;
+    a.total_q = total_q;
+    a.total_k = total_k;
     a.cu_q = cu_seqlens_q;
     a.cu_k = cu_seqlens_k;
     a.used_q = seqused_q;  // null: the whole slot
@@ -414,7 +416,6 @@ GQA_API int gqa_attn_decode_topk(const void *q, const void *kv, void *out, const
     c.S = S;
     c.Dv = Dv;
     c.out_bf16 = 1;
-    c.part_bf16 = 1;
     return launch_status(gqa::launch_combine(c, st));
 }
 
@@ -498,7 +499,6 @@ GQA_API int gqa_attn_decode_fp8(const void *q, const void *k, const void *v, con
     c.S = S;
     c.Dv = Dv;
     c.out_bf16 = 1;
-    c.part_bf16 = 1;
     return launch_status(gqa::launch_combine(c, st));
 }
 
@@ -508,15 +508,14 @@ GQA_API size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_spl
     return ws_bytes(B, Hq, Dv, num_splits);
 }
 
-// Workspace layouts of the decode: the caller-sized one (room for fp32
-// partial outputs [B, Hq, S, Dv], then the fp32 partial LSE [B, Hq, S]) and
-// the compact one of the allocation-free entry point (partial outputs in the
-// element type the kernels store -- bf16 on the bf16 path, fp32 on the fp32
-// path -- then the LSE at the next 256-byte boundary).
+// Workspace layouts of the decode: the caller-sized one (fp32 partial
+// outputs [B, Hq, S, Dv], then the fp32 partial LSE [B, Hq, S]) and the
+// compact one of the allocation-free entry point (the same partials, then
+// the LSE at the next 256-byte boundary).
 static size_t compact_ws_lse_offset(int B, int Hq, int Dv, int S, int dtype)
 {
     const size_t rows = (size_t)B * Hq * S;
-    const size_t o_bytes = rows * Dv * (dtype == GQA_BF16 ? 2 : 4);
+    const size_t o_bytes = rows * Dv * sizeof(float);
     return (o_bytes + 255) & ~(size_t)255;
 }
 static size_t compact_ws_bytes(int B, int Hq, int Dv, int S, int dtype)
@@ -620,7 +619,6 @@ static int decode_impl(const void *q, const void *k, const void *v, void *out, c
     c.S = S;
     c.Dv = Dv;
     c.out_bf16 = dtype == GQA_BF16;
-    c.part_bf16 = dtype == GQA_BF16;  // the bf16 and fp8 kernels store bf16 partials, the fp32 kernel fp32
     return launch_status(gqa::launch_combine(c, st));
 }
 

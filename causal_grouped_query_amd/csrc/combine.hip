@@ -9,8 +9,7 @@
 // Attention", section on sources and execution).  Empty chunks carry
 // lse = -inf and weigh nothing (their partial outputs are loaded but
 // selected away, whatever they hold); a row with no keys at all yields
-// zeros.  Partial outputs are bf16 (from the bf16 and fp8 kernels) or fp32
-// (from the fp32 kernel); the merge accumulates in fp32.
+// zeros.  Partial outputs are fp32 and the merge accumulates in fp32.
 #include "launch.h"
 
 namespace gqa {
@@ -29,11 +28,11 @@ constexpr int kCB = 16;   // partial outputs loaded together before any is used
 // more per further batch of kCB partial outputs
 // (unconditional loads of in-bounds slots; slots past the split count and
 // empty slots get weight 0 and are selected away, whatever they hold).
-template <bool OUT_BF16, bool PART_BF16>
+template <bool OUT_BF16>
 __global__ __launch_bounds__(kCT) void combine_kernel(CombineArgs p)
 {
-    using PT = typename std::conditional<PART_BF16, __bf16, float>::type;
-    using PT4 = typename std::conditional<PART_BF16, bf16x4, f32x4>::type;
+    using PT = float;
+    using PT4 = f32x4;
     const size_t row = blockIdx.x;  // b * Hq + head
     const float *lse = p.part_lse + row * p.S;
     const PT *po = (const PT *)p.part_o + row * (size_t)p.S * p.Dv;
@@ -178,14 +177,10 @@ int launch_combine(const CombineArgs &a, hipStream_t stream)
 {
     if (a.Dv % 4 != 0 || a.Dv <= 0 || a.Dv > 4 * kCT || a.S <= 0) return -1;
     dim3 grid((unsigned)((size_t)a.B * a.Hq)), block((a.Dv / 4 + 63) / 64 * 64);  // whole waves
-    if (a.part_bf16 && a.out_bf16)
-        hipLaunchKernelGGL((combine_kernel<true, true>), grid, block, 0, stream, a);
-    else if (a.part_bf16)
-        hipLaunchKernelGGL((combine_kernel<false, true>), grid, block, 0, stream, a);
-    else if (a.out_bf16)
-        hipLaunchKernelGGL((combine_kernel<true, false>), grid, block, 0, stream, a);
+    if (a.out_bf16)
+        hipLaunchKernelGGL((combine_kernel<true>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((combine_kernel<false, false>), grid, block, 0, stream, a);
+        hipLaunchKernelGGL((combine_kernel<false>), grid, block, 0, stream, a);
     return 0;
 }
 

@@ -288,16 +288,13 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kern
     if (!head_ok) return;
     const float l_tot = halves_sum(l_run);
     const size_t prow = ((size_t)b * p.Hq + head) * p.S + split;
-    __bf16 *po = (__bf16 *)p.part_o + prow * DV;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            bf16x4 v4 = {(__bf16)(o[dt][4 * j] * inv), (__bf16)(o[dt][4 * j + 1] * inv),
-                         (__bf16)(o[dt][4 * j + 2] * inv), (__bf16)(o[dt][4 * j + 3] * inv)};
-            *(bf16x4 *)(po + 32 * dt + 8 * j + 4 * hi) = v4;
-        }
+        for (int j = 0; j < 4; ++j)
+            store_partial4(p.part_o, prow * DV + 32 * dt + 8 * j + 4 * hi, o[dt][4 * j] * inv,
+                           o[dt][4 * j + 1] * inv, o[dt][4 * j + 2] * inv, o[dt][4 * j + 3] * inv);
     // empty chunk: o = 0 and lse = -inf, so it weighs nothing in the merge
     if (hi == 0) p.part_lse[prow] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
 }
@@ -730,16 +727,13 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
             if (head_ok) {
                 const float l_tot = halves_sum(l_run);
                 const size_t prow = ((size_t)cc.b * p.Hq + head) * p.S + j;
-                __bf16 *po = (__bf16 *)p.part_o + prow * DV;
                 const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
                 for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) {
-                        bf16x4 v4 = {(__bf16)(o[dt][4 * jj] * inv), (__bf16)(o[dt][4 * jj + 1] * inv),
-                                     (__bf16)(o[dt][4 * jj + 2] * inv), (__bf16)(o[dt][4 * jj + 3] * inv)};
-                        *(bf16x4 *)(po + 32 * dt + 8 * jj + 4 * hi) = v4;
-                    }
+                    for (int jj = 0; jj < 4; ++jj)
+                        store_partial4(p.part_o, prow * DV + 32 * dt + 8 * jj + 4 * hi, o[dt][4 * jj] * inv,
+                                       o[dt][4 * jj + 1] * inv, o[dt][4 * jj + 2] * inv, o[dt][4 * jj + 3] * inv);
                 if (hi == 0) p.part_lse[prow] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
             }
             if (j == 0 && head_ok && hi == 0) {

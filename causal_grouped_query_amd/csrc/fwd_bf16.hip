@@ -92,11 +92,16 @@ struct FwdSmem {
 // VAR: packed variable-length sequences (cu_seqlens), strided tensors and an
 // optional sliding window; false: the dense [B,H,T,D] problem (every VAR term
 // below folds away).
+// first token slot of packed sequence b, clamped to [0, total]
+__device__ __forceinline__ int seq_start(const int *cu, int b, int total) { return min(max(cu[b], 0), total); }
 // tokens of packed sequence b: its slot length, or the used length when
-// given (clamped to the slot; the rest of the slot is padding)
-__device__ __forceinline__ int used_len(const int *cu, const int *used, int b)
+// given (clamped to the slot; the rest of the slot is padding).  The slot is
+// clamped to [0, total), so offsets that disagree with the buffers never
+// address a token outside them.
+__device__ __forceinline__ int used_len(const int *cu, const int *used, int b, int total)
 {
-    const int n = max(cu[b + 1] - cu[b], 0);
+    const int s = seq_start(cu, b, total);
+    const int n = min(max(cu[b + 1], s), total) - s;
     return used ? min(max(used[b], 0), n) : n;
 }
 
@@ -140,7 +145,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
         int base = 0, bsel = -1, fb1 = 0;
         for (int b0 = 0; b0 < p.B; b0 += 64) {
             const int bb = b0 + lane0;
-            const int nt = bb < p.B ? (used_len(p.cu_q, p.used_q, bb) + p.Pt - 1) / p.Pt : 0;
+            const int nt = bb < p.B ? (used_len(p.cu_q, p.used_q, bb, p.total_q) + p.Pt - 1) / p.Pt : 0;
             int incl = nt;
 #pragma unroll
             for (int o = 1; o < 64; o <<= 1) {
@@ -175,10 +180,10 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
     // sequence bounds: the whole problem, or sequence b of the packed batch
     int Tq = p.Tq, Tk = p.Tk, sq0 = 0, sk0 = 0;
     if (VAR) {
-        sq0 = p.cu_q[b];
-        sk0 = p.cu_k[b];
-        Tq = used_len(p.cu_q, p.used_q, b);
-        Tk = used_len(p.cu_k, p.used_k, b);
+        sq0 = seq_start(p.cu_q, b, p.total_q);
+        sk0 = seq_start(p.cu_k, b, p.total_k);
+        Tq = used_len(p.cu_q, p.used_q, b, p.total_q);
+        Tk = used_len(p.cu_k, p.used_k, b, p.total_k);
         if (qt * p.Pt >= Tq) return;  // the whole workgroup (no barrier passed yet)
     }
     const int win = VAR ? p.window : 0;  // > 0: keys p-w+1 .. p only

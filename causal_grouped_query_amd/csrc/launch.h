@@ -7,6 +7,16 @@
 
 namespace gqa {
 
+// Store 4 consecutive normalised partial values (fp32) at element e of a
+// split-partial row.  The partials stay in fp32 until the combine: a second
+// bf16 rounding before the output's own would double the rounding error of
+// large outputs.
+__device__ __forceinline__ void store_partial4(void *po, size_t e, float a, float b, float c, float d)
+{
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    *(f4 *)((float *)po + e) = f4{a, b, c, d};
+}
+
 // Prefill / suffix forward (contiguous [B,H,T,D] tensors).
 struct FwdArgs {
     const uint16_t *q;  // bf16 bits
@@ -30,6 +40,7 @@ struct FwdArgs {
     // (likewise k, v, out); n_qt = bound on the query tiles of all sequences;
     // window > 0: keys p-w+1 .. p only
     int varlen;
+    int total_q, total_k;  // token slots of q / out and of k / v: every range is clamped to them
     const int *cu_q, *cu_k;
     const int *used_q, *used_k;
     long long q_sh, q_st, k_sh, k_st, v_sh, v_st, o_sh, o_st;
@@ -53,8 +64,7 @@ struct DecodeArgs {
     const void *k;       // cache, element strides below
     const void *v;
     const int *lens;     // device int32 [B]
-    void *part_o;        // [B, Hq, S, Dv] normalised partial outputs: bf16 from the
-                         // bf16 / fp8 kernels, fp32 from the fp32 kernel
+    float *part_o;       // [B, Hq, S, Dv] normalised partial outputs (fp32)
     float *part_lse;     // [B, Hq, S] fp32, base-2 log-sum-exp of scaled scores
     int B, Hq, Hkv, Tmax, G;
     long long k_sb, k_sh, k_st;
@@ -105,12 +115,11 @@ int launch_decode_f32(const DecodeArgs &a, int D, hipStream_t stream);
 
 // Log-sum-exp combine of the decode partials into the output.
 struct CombineArgs {
-    const void *part_o;  // bf16 when part_bf16, else fp32
+    const float *part_o;  // [B, Hq, S, Dv] fp32
     const float *part_lse;
     void *out;           // [B, Hq, 1, Dv], bf16 or fp32
     int B, Hq, S, Dv;
     int out_bf16;
-    int part_bf16;
 };
 int launch_combine(const CombineArgs &a, hipStream_t stream);
 

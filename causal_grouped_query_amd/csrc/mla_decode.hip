@@ -58,12 +58,65 @@ struct MlaSmem {
     uint16_t k[kStages][kTK * kDK];
 };
 
+// The index mask of the DSA page is a scatter: a position listed twice is
+// selected once.  Within a staged slice of n entries, every entry that
+// repeats the position of an earlier entry of the slice is replaced by -1
+// (selects nothing).  An open-addressing table of 2 * kMaxChunk slots maps
+// each valid position to the smallest slice index listing it: an entry
+// claims an empty slot, or lowers the index held by the slot of its
+// position; afterwards an entry is kept iff its position's slot holds its
+// own index.  Slots only ever hold entries of one position, so the result
+// is deterministic.  All threads of the workgroup take part; ends with a
+// barrier.
+__device__ __forceinline__ void dedup_slice(int *sidx, unsigned *htab, int n, int len, int tid)
+{
+    constexpr unsigned kEmpty = 0xffffffffu, kMask = 2 * kMaxChunk - 1;
+    auto home = [](int pos) { return ((unsigned)pos * 2654435761u) >> 19; };  // 13 bits: 2 * kMaxChunk slots
+    for (int e = tid; e < n; e += kNT) {
+        const int pos = sidx[e];
+        if ((unsigned)pos >= (unsigned)len) continue;
+        for (unsigned h = home(pos) & kMask;; h = (h + 1) & kMask) {
+            const unsigned old = atomicCAS(&htab[h], kEmpty, (unsigned)e);
+            if (old == kEmpty) break;  // claimed
+            if (sidx[old] == pos) {    // this position's slot: keep the smaller index
+                atomicMin(&htab[h], (unsigned)e);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    bool drop[(kMaxChunk + kNT - 1) / kNT];
+#pragma unroll
+    for (int r = 0; r < (kMaxChunk + kNT - 1) / kNT; ++r) {
+        const int e = tid + r * kNT;
+        drop[r] = false;
+        if (e >= n) continue;
+        const int pos = sidx[e];
+        if ((unsigned)pos >= (unsigned)len) continue;
+        for (unsigned h = home(pos) & kMask;; h = (h + 1) & kMask) {
+            const unsigned v = htab[h];
+            if (v == kEmpty) break;  // (not reached: the position was inserted along this probe path)
+            if (sidx[v] == pos) {
+                drop[r] = v != (unsigned)e;
+                break;
+            }
+        }
+    }
+    __syncthreads();  // every lookup done before any entry is overwritten
+#pragma unroll
+    for (int r = 0; r < (kMaxChunk + kNT - 1) / kNT; ++r)
+        if (drop[r]) sidx[tid + r * kNT] = -1;
+    __syncthreads();
+}
+
 template <bool SPARSE>
 __global__ __launch_bounds__(kNT, 1) void mla_decode_kernel(DecodeArgs p)
 {
     constexpr int NCOPY = kTK * kCPR / 64;  // 36 wave-copies per tile, spread over 8 waves
     __shared__ __attribute__((aligned(1024))) MlaSmem sm;
     __shared__ __attribute__((aligned(16))) int sidx[SPARSE ? kMaxChunk : 4];  // staged index slice
+    // sparse: open-addressing set of the slice's positions (entry indices)
+    __shared__ unsigned htab[SPARSE ? 2 * kMaxChunk : 1];
 
     // chunk-major order, as in the other decode kernel
     const int nbk = p.B * p.Hkv;
@@ -101,8 +154,10 @@ __global__ __launch_bounds__(kNT, 1) void mla_decode_kernel(DecodeArgs p)
         const int *il = p.idx + (size_t)b * p.topk;
         for (int e0 = w * 64; e0 < ntiles * kTK; e0 += kNT)
             g2lds4(il + min(kbeg + e0 + lane, p.topk - 1), &sidx[e0]);
+        for (int i = tid; i < 2 * kMaxChunk; i += kNT) htab[i] = 0xffffffffu;
         wait_vmem();
-        lds_barrier();  // the slice is visible to every wave
+        lds_barrier();  // the slice and the empty table are visible to every wave
+        dedup_slice(sidx, htab, kend - kbeg, len, tid);
     }
 
     // wave copy j covers LDS chunks [64 j, 64 j + 64); waves take j = w, w + 8, ...
@@ -268,14 +323,12 @@ __global__ __launch_bounds__(kNT, 1) void mla_decode_kernel(DecodeArgs p)
     if (!head_ok) return;
     const float l_tot = quarters_sum(l_run);
     const size_t prow = ((size_t)b * p.Hq + head) * p.S + split;
-    __bf16 *po = (__bf16 *)p.part_o + prow * kDV + 4 * g;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     // element i of o[db]: output dim 16 db + 4 g + i, head r16
 #pragma unroll
-    for (int db = 0; db < kDB; ++db) {
-        const f32x4 r = o[db] * inv;
-        *(bf16x4 *)(po + 16 * db) = bf16x4{(__bf16)r[0], (__bf16)r[1], (__bf16)r[2], (__bf16)r[3]};
-    }
+    for (int db = 0; db < kDB; ++db)
+        store_partial4(p.part_o, prow * kDV + 4 * g + 16 * db, o[db][0] * inv, o[db][1] * inv, o[db][2] * inv,
+                       o[db][3] * inv);
     if (g == 0) p.part_lse[prow] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
 }
 

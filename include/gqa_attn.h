@@ -111,22 +111,26 @@ int gqa_attn_fwd(const void *q, const void *k, const void *v, void *out, int B, 
  * lengths.  A right-padded batch [B, Tpad, H, D] is cu_seqlens = 0, Tpad,
  * 2*Tpad, ... with seqused = the true lengths.  NULL: every slot is used.
  *
- * total_q is the number of packed query slots, cu_seqlens_q[num_seqs]; it
- * sizes the grid (sum_i ceil(Tq_i / tile) <= total_q / tile + num_seqs), and
- * total_q = 0 returns GQA_OK with nothing enqueued.  The offsets are device
- * data and cannot be checked on the host: they must lie inside the buffers
- * and agree with total_q.  Used query rows of out are written in
- * full; out must not overlap itself or the inputs.
+ * total_q / total_k are the token slots of q and out / of k and v (the
+ * buffers' token extents, normally cu_seqlens_q[num_seqs] and
+ * cu_seqlens_k[num_seqs]); total_q sizes the grid (sum_i ceil(Tq_i / tile)
+ * <= total_q / tile + num_seqs), and total_q = 0 returns GQA_OK with nothing
+ * enqueued.  The offsets are device data and cannot be checked on the host;
+ * the kernel clamps every sequence's slot to [0, total_q) / [0, total_k),
+ * so offsets that disagree with the buffers never address a token outside
+ * them (such a sequence is cut short, and with overlapping or decreasing
+ * offsets some query rows may be left unwritten).  Used query rows of out
+ * are written in full; out must not overlap itself or the inputs.
  * Requirements (else GQA_ERR_INVALID_ARG): q, k, v 16-byte aligned, out 8,
  * cu and seqused arrays 4; q/k/v head and token strides positive multiples of 8
  * elements, out strides positive multiples of 4; window >= 0 and only with
- * causal = 1; total_q >= 0.  bf16 only, (Dk, Dv) = (64, 64) or (128, 128); fp32 and other
+ * causal = 1; total_q, total_k >= 0.  bf16 only, (Dk, Dv) = (64, 64) or (128, 128); fp32 and other
  * dims return GQA_ERR_UNSUPPORTED, as do key / value token strides st with
  * 126 * st + 2 * Dk >= 2^31 (tile offsets are 32-bit byte offsets).
  */
 int gqa_attn_fwd_varlen(const void *q, const void *k, const void *v, void *out, const int *cu_seqlens_q,
                         const int *cu_seqlens_k, const int *seqused_q, const int *seqused_k,
-                        int num_seqs, int Hq, int Hkv, int total_q, int Dk,
+                        int num_seqs, int Hq, int Hkv, int total_q, int total_k, int Dk,
                         int Dv, long long q_sh, long long q_st, long long k_sh, long long k_st, long long v_sh,
                         long long v_st, long long o_sh, long long o_st, float scale, int causal, int window,
                         gqa_dtype dtype, void *stream);
@@ -183,10 +187,8 @@ int gqa_attn_decode_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int Dv, gqa
 
 /*
  * Bytes of device workspace gqa_attn_decode needs for num_splits splits
- * (num_splits >= 1): room for fp32 partial outputs [B, Hq, S, Dv] followed
- * by fp32 partial log-sum-exp values [B, Hq, S].  The bf16 and fp8 paths
- * store their partial outputs as bf16 in the first half of the output area;
- * the fp32 path uses all of it.  Returns 0 for invalid arguments.
+ * (num_splits >= 1): fp32 partial outputs [B, Hq, S, Dv] followed by fp32
+ * partial log-sum-exp values [B, Hq, S].  Returns 0 for invalid arguments.
  */
 size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_splits);
 
@@ -297,11 +299,16 @@ int gqa_attn_decode_topk_splits(int B, int Hq, int topk, int Dk, int Dv, gqa_dty
  *   indices  device int32[B, topk], row-major: the selected positions of
  *            sequence b.  Entries outside [0, seq_lens[b]) select nothing
  *            (use -1 to pad a shorter selection); such entries are never
- *            used as addresses.  The listed positions must be distinct (as a
- *            top-k produces them): a repeated position is counted once per
- *            occurrence, where the page's mask counts it once.  The order of
- *            the list does not matter.  A sequence with no valid entry gets
- *            a zero output row.
+ *            used as addresses.  The order of the list does not matter.  A
+ *            sequence with no valid entry gets a zero output row.  The
+ *            page's mask is a scatter, so a position listed twice is
+ *            selected once: the list is cut into num_splits slices of
+ *            ceil(topk / num_splits) entries rounded up to a multiple of 32,
+ *            and inside a slice an entry that repeats an earlier entry's
+ *            position selects nothing.  A top-k lists distinct positions;
+ *            a list whose repeats fall in different slices counts such a
+ *            position once per slice (num_splits = 1, possible for lists of
+ *            up to 4096 entries, applies the mask's rule to any list).
  *   num_splits  slices of the index list, 1 .. 1024, or 0 for
  *            gqa_attn_decode_topk_splits(); each slice may hold at most 4096
  *            entries (else GQA_ERR_UNSUPPORTED).
@@ -344,11 +351,10 @@ int gqa_attn_decode_window(const void *q, const void *k, const void *v, void *ou
  *
  * A shape needs gqa_attn_decode_noalloc_scratch_bytes(B, Hq, Dv, S, dtype)
  * bytes of it for S splits (num_splits, or gqa_attn_decode_splits() when 0):
- * B*Hq*S partial outputs of Dv elements (bf16 for GQA_BF16, fp32 for GQA_F32)
- * plus B*Hq*S fp32 log-sum-exp values.  A shape that needs more returns
- * GQA_ERR_WORKSPACE with nothing enqueued (e.g. B = 64, Hq = 32, Dv = 128,
- * S = 10 needs 5.3 MB; the absorbed-MLA B = 16, Hq = 128, Dv = 512, S = 16
- * needs 33.7 MB).
+ * B*Hq*S fp32 partial outputs of Dv values plus B*Hq*S fp32 log-sum-exp
+ * values.  A shape that needs more returns GQA_ERR_WORKSPACE with nothing
+ * enqueued (e.g. B = 64, Hq = 32, Dv = 128, S = 10 needs 10.6 MB; the
+ * absorbed-MLA B = 16, Hq = 128, Dv = 512, S = 16 needs 67.2 MB).
  *
  * Calls on one GPU share its array: calls that overlap in time on that GPU
  * (different streams, or other processes' threads sharing this library
@@ -356,7 +362,7 @@ int gqa_attn_decode_window(const void *q, const void *k, const void *v, void *ou
  * stream.  The array keeps the last call's contents; nothing in it needs to
  * start zeroed (every slot a call's combine reads is written by that call).
  */
-#define GQA_DECODE_NOALLOC_MAX_SCRATCH (64u << 20)
+#define GQA_DECODE_NOALLOC_MAX_SCRATCH (96u << 20)
 size_t gqa_attn_decode_noalloc_scratch_bytes(int B, int Hq, int Dv, int num_splits, gqa_dtype dtype);
 int gqa_attn_decode_noalloc(const void *q, const void *k, const void *v, void *out, const int *seq_lens,
                             int B, int Hq, int Hkv, int Tmax, int Dk, int Dv, long long k_sb,

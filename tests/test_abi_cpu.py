@@ -70,20 +70,22 @@ def test_fwd_rejects_on_host(kw, code):
 
 def _fwd_varlen(**kw):
     H, D = 4, 128
-    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, cq=FAKE, ck=FAKE, uq=None, uk=None, n=2, Hq=H, Hkv=2, maxq=16, Dk=D, Dv=D,
+    a = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, cq=FAKE, ck=FAKE, uq=None, uk=None, n=2, Hq=H, Hkv=2, maxq=16, maxk=16,
+             Dk=D, Dv=D,
              qsh=D, qst=H * D, ksh=D, kst=2 * D, vsh=D, vst=2 * D, osh=D, ost=H * D, scale=0.1, causal=1,
              window=0, dtype=BF16)
     a.update(kw)
     return gqa.lib().gqa_attn_fwd_varlen(a["q"], a["k"], a["v"], a["out"], a["cq"], a["ck"], a["uq"], a["uk"],
                                          a["n"], a["Hq"],
-                                         a["Hkv"], a["maxq"], a["Dk"], a["Dv"], a["qsh"], a["qst"], a["ksh"],
+                                         a["Hkv"], a["maxq"], a["maxk"], a["Dk"], a["Dv"], a["qsh"], a["qst"],
+                                         a["ksh"],
                                          a["kst"], a["vsh"], a["vst"], a["osh"], a["ost"], a["scale"],
                                          a["causal"], a["window"], a["dtype"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(q=0), INVALID), (dict(cq=0), INVALID), (dict(ck=0), INVALID), (dict(n=0), INVALID),
-    (dict(maxq=-1), INVALID), (dict(Hq=6, Hkv=4), INVALID), (dict(causal=2), INVALID),
+    (dict(maxq=-1), INVALID), (dict(maxk=-1), INVALID), (dict(Hq=6, Hkv=4), INVALID), (dict(causal=2), INVALID),
     (dict(window=-1), INVALID), (dict(window=4, causal=0), INVALID), (dict(qst=100), INVALID),
     (dict(kst=0), INVALID), (dict(vsh=-8), INVALID), (dict(ost=6), INVALID), (dict(k=FAKE + 8), INVALID),
     (dict(cq=FAKE + 2), INVALID), (dict(uq=FAKE + 2), INVALID), (dict(uk=FAKE + 1), INVALID),
@@ -259,16 +261,38 @@ def test_decode_noalloc_rejects_on_host():
     # absorbed-MLA shape whose partials exceed the scratch: B = 1024 sequences
     # of 128 heads, 16 splits of 512 bf16 values
     assert call(B_=1024, Hq_=128, Hkv=1, Dk=576, Dv=512, S=16, kst=576) == WS
-    # the fp32 path stores fp32 partials: 4 bytes per value
     assert call(B_=4096, Hq_=32, Hkv=8, S=64, dtype=F32) == WS
 
 
 def test_decode_noalloc_scratch_sizes():
-    # bf16 partials (2 bytes) then the fp32 lse at the next 256-byte boundary
+    # fp32 partials, then the fp32 lse at the next 256-byte boundary
     rows = 64 * 32 * 10
-    assert gqa.decode_noalloc_scratch_bytes(64, 32, 128, 10, BF16) == rows * 128 * 2 + rows * 4
+    assert gqa.decode_noalloc_scratch_bytes(64, 32, 128, 10, BF16) == rows * 128 * 4 + rows * 4
     rows = 16 * 128 * 16
-    assert gqa.decode_noalloc_scratch_bytes(16, 128, 512, 16, BF16) == rows * 512 * 2 + rows * 4
+    assert gqa.decode_noalloc_scratch_bytes(16, 128, 512, 16, BF16) == rows * 512 * 4 + rows * 4
+    assert gqa.decode_noalloc_scratch_bytes(16, 128, 512, 16, BF16) <= 96 << 20  # the absorbed-MLA workload fits
     assert gqa.decode_noalloc_scratch_bytes(1, 1, 3, 1, F32) == 256 + 4
     assert gqa.decode_noalloc_scratch_bytes(0, 32, 128, 10, BF16) == 0
     assert gqa.decode_noalloc_scratch_bytes(1, 32, 128, 10, 9) == 0
+
+
+@pytest.mark.parametrize("cu,total,ok", [
+    ([0, 5, 9], 9, True), ([0, 0, 0], 0, True), ([2, 5, 9], 9, True), ([0, 5, 9], 12, True),
+    ([0, 5, 10], 9, False), ([-1, 5, 9], 9, False), ([0, 6, 5], 9, False), ([0], 9, False),
+])
+def test_check_cu_seqlens(cu, total, ok):
+    """The binding's optional host check of packed offsets: non-decreasing,
+    at or above 0, ending inside the tensor."""
+    if ok:
+        gqa.check_cu_seqlens(cu, total)
+    else:
+        with pytest.raises(ValueError):
+            gqa.check_cu_seqlens(cu, total)
+
+
+def test_check_topk_distinct():
+    import numpy as np
+    lens = np.array([10, 5])
+    gqa.check_topk_distinct(np.array([[1, 2, 3, -1], [0, 4, 7, 7]]), lens)  # 7 >= 5 selects nothing
+    with pytest.raises(ValueError):
+        gqa.check_topk_distinct(np.array([[1, 2, 1, -1], [0, 1, 2, 3]]), lens)

@@ -179,7 +179,7 @@ DEC_CASES = [
 
 @pytest.mark.parametrize("case", DEC_CASES, ids=lambda c: "B{}_Hq{}_Hkv{}_Tmax{}_D{}".format(*c[:5]))
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-@pytest.mark.parametrize("splits", [1, 2, 0, 9])
+@pytest.mark.parametrize("splits", [1, 2, 0, 9, 1024])
 def test_decode_matches_oracle(case, dtype, splits):
     B, Hq, Hkv, Tmax, D, lens = case
     seed = zlib.crc32(repr(case).encode()) % 10000
@@ -211,7 +211,7 @@ FLAT_CASES = [
 
 
 @pytest.mark.parametrize("case", FLAT_CASES, ids=lambda c: "B{}_Hq{}_Hkv{}_Tmax{}_D{}".format(*c[:5]))
-@pytest.mark.parametrize("splits", [3, 0, 64])
+@pytest.mark.parametrize("splits", [3, 0, 64, 1024])
 def test_flat_decode_matches_oracle(case, splits):
     B, Hq, Hkv, Tmax, D, lens = case
     seed = zlib.crc32(repr(case).encode()) % 10000
@@ -351,3 +351,44 @@ def test_workload_decode_full_size_sampled(w):
     rows = _sample_rows(w.B, w.Hq, 1, 48 if w.kind == "mla_decode" else 128, w.seed)
     ref = O.attention(q, k, v, w.scale, True, kv_lens=lens.tolist(), rows=rows)
     _check_rows(out, rows, ref, w.dtype, w.name)
+
+
+@pytest.mark.parametrize("kind", ["gqa", "mla"])
+def test_decode_large_values(kind):
+    """Values eight times larger than N(0,1).  Every bf16 path's rounding
+    (the weights of the P V product, the output) grows with |o|, so the bar
+    here is eight times the N(0,1) one; and the split decode must add no
+    error of its own through its partials: on the GQA shape its error is
+    held to that of the forward kernel on the same query rows (one pass, no
+    partials)."""
+    if kind == "gqa":
+        B, Hq, Hkv, T, D, Dv = 8, 32, 8, 3000, 128, 128
+        q, k = _rand((B, Hq, 1, D), 91, "bf16"), _rand((B, Hkv, T, D), 92, "bf16")
+        v = (_rand((B, Hkv, T, Dv), 93, "bf16").float() * 8).to(torch.bfloat16)
+        lens = [3000, 1, 17, 2048, 999, 64, 2500, 1500]
+        scale = 1.0 / math.sqrt(D)
+    else:
+        B, Hq, T = 4, 128, 3000
+        q = _rand((B, Hq, 1, 576), 94, "bf16")
+        k = (_rand((B, 1, T, 576), 95, "bf16").float() * 8).to(torch.bfloat16)  # the value is K's latent prefix
+        v = k[..., :512]
+        lens = [3000, 2999, 100, 1]
+        scale = 0.02
+    kd = k.cuda()
+    vd = kd[..., :512] if kind == "mla" else v.cuda()
+    lt = torch.tensor(lens, dtype=torch.int32)
+    out = gqa.decode(q.cuda(), kd, vd, lt.cuda(), scale=scale)
+    torch.cuda.synchronize()
+    ref = O.attention(q, k, v, scale, True, kv_lens=lens)
+    mx, mean = _err(out, ref)
+    print(f"{kind} decode, |v| x 8: max_abs={mx:.3e} mean_abs={mean:.3e}", flush=True)
+    assert mx <= 8 * 2e-2 and mean <= 8 * 2e-3
+    if kind == "gqa":
+        fmx, fmean = 0.0, 0.0
+        for b, n in enumerate(lens):  # the same rows through the forward kernel: Tq = 1 over n keys
+            o1 = gqa.attention(q[b:b + 1].cuda(), k[b:b + 1, :, :n].contiguous().cuda(),
+                               v[b:b + 1, :, :n].contiguous().cuda(), scale=scale)
+            e1 = _err(o1, ref[b:b + 1])
+            fmx, fmean = max(fmx, e1[0]), fmean + e1[1] / B
+        print(f"forward on the same rows: max_abs={fmx:.3e} mean_abs={fmean:.3e}", flush=True)
+        assert mx <= 1.25 * fmx + 1e-3 and mean <= 1.25 * fmean + 1e-4

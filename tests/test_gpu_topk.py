@@ -114,3 +114,68 @@ def test_topk_workload_full_size():
     out = gqa.decode_topk(q.cuda(), k.cuda(), lens.cuda(), idx.cuda(), scale=w.scale)
     ref = O.decode_topk(q, k, lens, idx, w.scale, w.Dv)
     _check(out, ref, "topk workload")
+
+
+def _with_repeats(lens, topk, n_distinct, seed):
+    """Index rows of n_distinct positions each, filled up to topk with repeats
+    of positions already listed, shuffled."""
+    rng = np.random.default_rng(seed)
+    idx = np.full((len(lens), topk), -1, dtype=np.int32)
+    for b, n in enumerate(lens):
+        sel = rng.permutation(n)[:min(n, n_distinct)]
+        rep = rng.choice(sel, topk - sel.size)
+        idx[b] = rng.permutation(np.concatenate([sel, rep])).astype(np.int32)
+    return idx
+
+
+@pytest.mark.parametrize("splits", [1, 0])
+def test_topk_repeated_positions_in_one_slice_count_once(splits):
+    """The page's index mask is a scatter: a position listed twice is selected
+    once.  With one slice (splits=1) every repeat is inside it; with the
+    default split the repeats of each slice are drawn from that slice's own
+    positions.  Either way the result is the oracle's set semantics."""
+    lens, topk = [500, 300, 37], 256
+    q, kv, lens_a, _ = _problem(3, 128, 512, lens, topk, 71)
+    if splits == 1:
+        idx = _with_repeats(lens, topk, 100, 72)
+    else:
+        S = gqa.decode_topk_splits(3, 128, topk, 576, 512, gqa.GQA_BF16)
+        chunk = -(-topk // S)
+        chunk = -(-chunk // 32) * 32
+        idx = np.full((3, topk), -1, dtype=np.int32)
+        rng = np.random.default_rng(73)
+        nsl = -(-topk // chunk)
+        for b, n in enumerate(lens):
+            perm = rng.permutation(n)
+            for si, s0 in enumerate(range(0, topk, chunk)):  # each slice: its own disjoint positions, repeated
+                m = min(chunk, topk - s0)
+                own = perm[si * n // nsl:(si + 1) * n // nsl][: max(1, m // 2)]
+                idx[b, s0:s0 + m] = rng.permutation(np.concatenate([own, rng.choice(own, m - own.size)]))
+            used = [set(idx[b, s0:s0 + chunk].tolist()) for s0 in range(0, topk, chunk)]
+            assert all(not (used[i] & used[j]) for i in range(nsl) for j in range(i))  # no cross-slice repeats
+    assert any(np.unique(r[r >= 0]).size < (r >= 0).sum() for r in idx)  # the rows do repeat
+    out = _run(q, kv, lens_a, idx, splits)
+    _check(out, O.decode_topk(q, kv, lens_a, idx, SCALE, 512), f"repeats within slices, splits={splits}")
+    with pytest.raises(ValueError):
+        gqa.decode_topk(q.cuda(), kv.cuda(), torch.from_numpy(lens_a).cuda(), torch.from_numpy(idx).cuda(),
+                        scale=SCALE, num_splits=splits, validate=True)
+
+
+def test_topk_repeats_across_slices_count_once_per_slice():
+    """The documented rule for a list whose repeats fall in different slices
+    (a top-k never produces one): such a position counts once per slice.
+    Checked against the oracle on an expanded cache in which every list
+    entry is a row of its own (set semantics there = per-entry weights)."""
+    lens, topk, splits = [400, 250], 128, 2  # slices of 64 entries
+    q, kv, lens_a, _ = _problem(2, 128, 448, lens, topk, 81)
+    rng = np.random.default_rng(82)
+    idx = np.zeros((2, topk), dtype=np.int32)
+    for b, n in enumerate(lens):
+        sel = rng.permutation(n)[:64]
+        idx[b, :64] = sel
+        idx[b, 64:] = rng.permutation(sel)  # every position once in each slice
+    out = _run(q, kv, lens_a, idx, splits)
+    kv_exp = torch.stack([kv[b, :, torch.from_numpy(idx[b]).long()] for b in range(2)])  # [2, 1, topk, 576]
+    idx_exp = np.tile(np.arange(topk, dtype=np.int32), (2, 1))
+    ref = O.decode_topk(q, kv_exp, np.full(2, topk, dtype=np.int32), idx_exp, SCALE, 512)
+    _check(out, ref, "repeats across slices")

@@ -251,3 +251,30 @@ def test_multi_token_decode_over_padded_cache():
     ref = O.attention_varlen(q, kflat, vflat, cu_q.tolist(), cu_k.tolist(), 1.0 / np.sqrt(D), True,
                              seqused_k=lens)
     _check(out, ref, "multi-token decode, padded cache")
+
+
+@pytest.mark.parametrize("cq_bad,ck_bad,cq_eff,ck_eff", [
+    # last offsets past the tensors' 300 query / 420 key slots
+    ([0, 100, 500], [0, 150, 700], [0, 100, 300], [0, 150, 420]),
+    # a decreasing offset: the second sequence is empty
+    ([0, 200, 100], [0, 300, 250], [0, 200, 200], [0, 300, 300]),
+    # a negative first offset
+    ([-50, 120, 300], [-10, 200, 420], [0, 120, 300], [0, 200, 420]),
+])
+def test_varlen_offsets_clamped_to_the_buffers(cq_bad, ck_bad, cq_eff, ck_eff):
+    """Offsets that disagree with the tensors' token extents are clamped in
+    the kernel: the result is that of the clamped layout, and no token
+    outside q / k / v / out is addressed."""
+    Hq, Hkv, D = 8, 2, 128
+    q, k, v = _rand((300, Hq, D), 41), _rand((420, Hkv, D), 42), _rand((420, Hkv, D), 43)
+    scale = 1.0 / np.sqrt(D)
+    out = torch.zeros((300, Hq, D), dtype=torch.bfloat16, device="cuda")
+    cqd = torch.tensor(cq_bad, dtype=torch.int32, device="cuda")
+    ckd = torch.tensor(ck_bad, dtype=torch.int32, device="cuda")
+    gqa.attention_varlen(q.cuda(), k.cuda(), v.cuda(), cqd, ckd, scale=scale, causal=True, out=out)
+    torch.cuda.synchronize()
+    ref = O.attention_varlen(q, k, v, cq_eff, ck_eff, scale, True)
+    rows = [t for i in range(2) for t in range(cq_eff[i], cq_eff[i + 1])]  # tokens of non-empty sequences
+    _check(out[rows], ref[rows], f"clamped offsets {cq_bad} / {ck_bad}")
+    with pytest.raises(ValueError):
+        gqa.attention_varlen(q.cuda(), k.cuda(), v.cuda(), cqd, ckd, scale=scale, causal=True, validate=True)

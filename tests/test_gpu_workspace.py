@@ -36,7 +36,7 @@ def _nan_ws(nbytes):
     return torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
 
 
-@pytest.mark.parametrize("splits", [0, 2, 9, 40, 100, 300])
+@pytest.mark.parametrize("splits", [0, 2, 9, 40, 100, 300, 1024])
 def test_gqa_decode_nan_workspace(splits):
     B, Hq, Hkv, T, D = len(LENS), 32, 8, 700, 128
     q, k, v = _rand((B, Hq, 1, D), 800), _rand((B, Hkv, T, D), 801), _rand((B, Hkv, T, D), 802)
