@@ -21,6 +21,10 @@ bool finite_nonneg(float x) { return isfinite(x) && x >= 0.f; }
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
+// ceil(a / b) in 64-bit arithmetic (a >= 0, b > 0): sizes near INT_MAX must
+// not overflow before the range checks that reject them
+long long cdiv(long long a, long long b) { return (a + b - 1) / b; }
+
 // scale * log2(e), kept strictly positive so that masked (-inf) scores stay
 // -inf after scaling; a zero scale becomes 1e-30, which leaves every weight
 // exactly equal in fp32 (uniform attention, as scale = 0 means).
@@ -58,15 +62,15 @@ int default_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int dtype)
     if (Dk == 576) {
         // absorbed MLA: a workgroup covers 128 query heads of a sequence and
         // one of S equal key chunks; one workgroup per CU
-        const long long groups = (long long)B * Hkv * ((G + 127) / 128);
+        const long long groups = (long long)B * Hkv * cdiv(G, 128);
         long long s = (256 + groups - 1) / groups;
-        const long long cap = (Tmax + 255) / 256;
+        const long long cap = cdiv(Tmax, 256);
         if (s > cap) s = cap;
         if (s < 1) s = 1;
         if (s > 64) s = 64;
         return (int)s;
     }
-    const long long streams = (long long)B * Hkv * ((G + 31) / 32);
+    const long long streams = (long long)B * Hkv * cdiv(G, 32);
     if (dtype == GQA_BF16) {
         // flat decode: S bounds the pieces any stream may be cut into.  The
         // kernel runs min(resident workgroups, ~T (S-2) / (n_max + S - 4))
@@ -76,7 +80,7 @@ int default_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int dtype)
         // the lengths are ragged.
         const long long wgs = gqa::decode_bf16_flat_workgroups(Dk);
         long long s = 2 + (2 * wgs + streams - 1) / streams;
-        const long long cap = 2 + (Tmax + 31) / 32;
+        const long long cap = 2 + cdiv(Tmax, 32);
         if (s < 8) s = 8;
         if (s > cap) s = cap;
         if (s > 64) s = 64;
@@ -86,7 +90,7 @@ int default_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int dtype)
     // per resident slot if every sequence were full length, chunks of at
     // least 256 keys
     long long s = (3200 + streams - 1) / streams;
-    const long long cap = (Tmax + 255) / 256;
+    const long long cap = cdiv(Tmax, 256);
     if (s > cap) s = cap;
     if (s < 1) s = 1;
     if (s > 64) s = 64;
@@ -122,9 +126,10 @@ bool fwd_geometry(gqa::FwdArgs &a, int B, int Hq, int Hkv, int Tq)
     a.Gt = gt;
     a.Pt = rpw * (waves / gt);
     a.n_hblk = G / gt;
-    a.n_qt = (Tq + a.Pt - 1) / a.Pt;
+    const long long n_qt = cdiv(Tq, a.Pt);
     const long long units = (long long)B * Hkv * a.n_hblk;
-    if (units * a.n_qt > 0x7fffffffLL) return false;
+    if (units * n_qt > 0x7fffffffLL) return false;
+    a.n_qt = (int)n_qt;
     a.n_units = (int)units;
     return true;
 }
@@ -331,11 +336,11 @@ GQA_API int gqa_attn_decode_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int
 // entries, and never a slice longer than the kernel can stage.
 static int topk_default_splits(int B, int Hq, int topk)
 {
-    const long long groups = (long long)B * ((Hq + 127) / 128);
+    const long long groups = (long long)B * cdiv(Hq, 128);
     long long s = (256 + groups - 1) / groups;
-    const long long cap = (topk + 63) / 64;
+    const long long cap = cdiv(topk, 64);
     if (s > cap) s = cap;
-    const long long need = (topk + gqa::mla_topk_max_chunk() - 1) / gqa::mla_topk_max_chunk();
+    const long long need = cdiv(topk, gqa::mla_topk_max_chunk());
     if (s < need) s = need;
     if (s < 1) s = 1;
     return (int)s;
@@ -376,12 +381,11 @@ GQA_API int gqa_attn_decode_topk(const void *q, const void *kv, void *out, const
     if (rc != GQA_OK) return rc;
 
     const int S = num_splits ? num_splits : topk_default_splits(B, Hq, topk);
-    int chunk = (topk + S - 1) / S;
-    chunk = (chunk + 31) / 32 * 32;
+    const int chunk = (int)(cdiv(cdiv(topk, S), 32) * 32);  // topk <= 1024 * 4096 (checked above)
     if (chunk > gqa::mla_topk_max_chunk()) return GQA_ERR_UNSUPPORTED;  // too few splits for topk
     const size_t need = ws_bytes(B, Hq, Dv, S);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return GQA_ERR_WORKSPACE;
-    if ((long long)S * B > 0x7fffffffLL || (Hq + 127) / 128 > 65535) return GQA_ERR_UNSUPPORTED;
+    if ((long long)S * B > 0x7fffffffLL || cdiv(Hq, 128) > 65535) return GQA_ERR_UNSUPPORTED;
 
     gqa::DecodeArgs a = {};
     a.q = q;
@@ -400,7 +404,7 @@ GQA_API int gqa_attn_decode_topk(const void *q, const void *kv, void *out, const
     a.k_st = a.v_st = kv_st;
     a.S = S;
     a.chunk = chunk;
-    a.n_hblk = (Hq + 127) / 128;
+    a.n_hblk = (int)cdiv(Hq, 128);
     a.c = folded_scale(scale);
     a.idx = indices;
     a.topk = topk;
@@ -474,7 +478,7 @@ GQA_API int gqa_attn_decode_fp8(const void *q, const void *k, const void *v, con
     a.S = S;
     a.chunk = 0;
     const int hpb = gqa::decode_bf16_heads_per_block(Dk, G);
-    a.n_hblk = (G + hpb - 1) / hpb;
+    a.n_hblk = (int)cdiv(G, hpb);
     a.n_wg = gqa::decode_fp8_flat_workgroups(Dk);
     a.c = folded_scale(scale);
     a.fp8 = 1;
@@ -561,8 +565,9 @@ static int decode_impl(const void *q, const void *k, const void *v, void *out, c
     const int G = Hq / Hkv;
     const int tile = dtype == GQA_BF16 ? gqa::decode_bf16_key_tile() : 64;
     const int Teff = (window > 0 && window < Tmax) ? window : Tmax;  // keys any query can see
-    int chunk = (Teff + S - 1) / S;
-    chunk = (chunk + tile - 1) / tile * tile;
+    const long long chunk_ll = cdiv(cdiv(Teff, S), tile) * tile;
+    if (chunk_ll > 0x7fffffffLL) return GQA_ERR_UNSUPPORTED;
+    const int chunk = (int)chunk_ll;
 
     gqa::DecodeArgs a = {};
     a.q = q;
@@ -591,7 +596,7 @@ static int decode_impl(const void *q, const void *k, const void *v, void *out, c
 
     if (dtype == GQA_BF16) {
         const int hpb = gqa::decode_bf16_heads_per_block(Dk, G);
-        a.n_hblk = (G + hpb - 1) / hpb;
+        a.n_hblk = (int)cdiv(G, hpb);
         if ((long long)B * Hkv * S > 0x7fffffffLL || a.n_hblk > 65535) return GQA_ERR_UNSUPPORTED;
         if (Dk <= 128 && S >= 3) {
             // flat decode (balanced over all sequences); S bounds the pieces per stream

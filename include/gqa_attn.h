@@ -52,7 +52,14 @@
 extern "C" {
 #endif
 
+/* Element type.  Callers pass it as an int; in C++ the enum has int as its
+ * fixed underlying type, so an out-of-range value is a value the library
+ * can reject (GQA_ERR_INVALID_ARG) rather than undefined behaviour. */
+#ifdef __cplusplus
+typedef enum gqa_dtype_e : int { GQA_BF16 = 0, GQA_F32 = 1 } gqa_dtype;
+#else
 typedef enum { GQA_BF16 = 0, GQA_F32 = 1 } gqa_dtype;
+#endif
 
 enum {
     GQA_OK = 0,
