@@ -31,7 +31,9 @@ __all__ = [
     "decode_splits", "decode_workspace_size", "decode_noalloc", "decode_noalloc_scratch_bytes", "decode_topk", "decode_topk_splits", "check_topk_distinct", "decode_fp8", "attention_shard", "merge", "strerror",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_attn.so")
+# The library to load: the in-tree build, or another build of it (e.g. the
+# NaN-fill debug build) named by GQA_ATTN_LIB.
+LIB_PATH = os.environ.get("GQA_ATTN_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa_attn.so")
 GQA_BF16, GQA_F32 = 0, 1
 GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP = 0, -1, -2, -3, -4
 

@@ -19,6 +19,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgqa_attn.so")
+# debug build of the same library: LDS buffers and the split-KV workspace are
+# filled with NaN before use (GQA_DEBUG_NANFILL), so a read of anything no
+# copy or kernel wrote shows up in the results; select it with GQA_ATTN_LIB
+NANFILL_LIB = os.path.join(PKG, "libgqa_attn_nanfill.so")
 PROBE_LIB = os.path.join(PKG, "libgqa_probes.so")  # measurement aids for bench.py (not the attention ABI)
 OBJDIR = os.path.join(PKG, "_build")
 ARCH = os.environ.get("GQA_OFFLOAD_ARCH", "gfx950")
@@ -31,10 +35,11 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    sub = "probe_" if os.path.basename(os.path.dirname(src)) == "probes" else ""
+def _compile(src: str, variant: str = "") -> str:
+    sub = "probe_" if os.path.basename(os.path.dirname(src)) == "probes" else variant
     obj = os.path.join(OBJDIR, sub + os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    extra = ["-DGQA_DEBUG_NANFILL=1"] if variant == "nanfill_" else []
+    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -54,12 +59,15 @@ def build(verbose: bool = False) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     probe_srcs = sorted(glob.glob(os.path.join(PKG, "probes", "*.hip")))
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs) + len(probe_srcs))) as ex:
-        objs = list(ex.map(_compile, srcs + probe_srcs))
-    _link(objs[: len(srcs)], LIB)
-    _link(objs[len(srcs):], PROBE_LIB)
+    jobs = [(s, "") for s in srcs + probe_srcs] + [(s, "nanfill_") for s in srcs]
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    n, m = len(srcs), len(probe_srcs)
+    _link(objs[:n], LIB)
+    _link(objs[n:n + m], PROBE_LIB)
+    _link(objs[n + m:], NANFILL_LIB)
     if verbose:
-        print(f"built {LIB} and {PROBE_LIB}")
+        print(f"built {LIB}, {PROBE_LIB} and {NANFILL_LIB}")
     return LIB
 
 

@@ -47,6 +47,23 @@ int check_common(int B, int Hq, int Hkv, int Dk, int Dv, float scale, int dtype)
     return GQA_OK;
 }
 
+// Debug builds (GQA_DEBUG_NANFILL=1): poison the split-KV workspace with
+// NaN bit patterns before the partial kernels run, so a slot no kernel
+// writes reaches the combine as NaN.  Nothing in normal builds.
+#ifndef GQA_DEBUG_NANFILL
+#define GQA_DEBUG_NANFILL 0
+#endif
+void debug_fill_workspace(void *ws, size_t bytes, hipStream_t st)
+{
+#if GQA_DEBUG_NANFILL
+    (void)hipMemsetAsync(ws, 0xff, bytes, st);
+#else
+    (void)ws;
+    (void)bytes;
+    (void)st;
+#endif
+}
+
 int launch_status(int rc)
 {
     if (rc != 0) return GQA_ERR_UNSUPPORTED;
@@ -409,6 +426,7 @@ GQA_API int gqa_attn_decode_topk(const void *q, const void *kv, void *out, const
     a.idx = indices;
     a.topk = topk;
     hipStream_t st = (hipStream_t)stream;
+    debug_fill_workspace(workspace, need, st);
     (void)hipGetLastError();
     if (gqa::launch_mla_decode_topk(a, st) != 0) return GQA_ERR_UNSUPPORTED;
     gqa::CombineArgs c;
@@ -492,6 +510,7 @@ GQA_API int gqa_attn_decode_fp8(const void *q, const void *k, const void *v, con
     a.vs_st = vs_st;
     a.window = window;
     hipStream_t st = (hipStream_t)stream;
+    debug_fill_workspace(workspace, need, st);
     (void)hipGetLastError();
     if (gqa::launch_decode_fp8(a, Dk, Dv, st) != 0) return GQA_ERR_UNSUPPORTED;
     gqa::CombineArgs c;
@@ -604,6 +623,7 @@ static int decode_impl(const void *q, const void *k, const void *v, void *out, c
         }
         a.c = folded_scale(scale);
         if (dry_run) return GQA_OK;
+        debug_fill_workspace(workspace, need, st);
         (void)hipGetLastError();
         rc = gqa::launch_decode_bf16(a, Dk, Dv, st);
     } else {
@@ -611,6 +631,7 @@ static int decode_impl(const void *q, const void *k, const void *v, void *out, c
         a.n_hblk = 1;
         a.c = scale;  // the fp32 path works in natural-log units
         if (dry_run) return GQA_OK;
+        debug_fill_workspace(workspace, need, st);
         (void)hipGetLastError();
         rc = gqa::launch_decode_f32(a, Dk, st);
     }

@@ -100,6 +100,7 @@ __global__ __launch_bounds__(64 * NW, (DK <= 128 ? 2 : 1)) void decode_bf16_kern
     static_assert(STAGES >= 2 && (STAGES - 2) * NI < 64, "ring depth");
 
     __shared__ __attribute__((aligned(1024))) DecSmem<DK, DV, STAGES> sm;
+    debug_nanfill(sm);
 
     // chunk-major order: every sequence's first chunk is dispatched before
     // any second chunk, so full chunks start first and the short / empty
@@ -330,6 +331,7 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
 
     using Smem = typename std::conditional<F8, DecSmemF8<DK, DV, STAGES>, DecSmem<DK, DV, STAGES>>::type;
     __shared__ __attribute__((aligned(1024))) Smem sm;
+    debug_nanfill(sm);
 
     const int lane = threadIdx.x;
     const int col = lane & 31, hi = lane >> 5;

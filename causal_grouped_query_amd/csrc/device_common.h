@@ -239,6 +239,26 @@ __device__ __forceinline__ void hold_reg(const T &x)
     asm volatile("" ::"v"(x));
 }
 
+// Debug builds (GQA_DEBUG_NANFILL=1) fill a kernel's LDS buffers with NaN
+// bit patterns (0xffff in every bf16 half, 0xffffffff as fp32) before first
+// use, so any read of a slot no copy or store wrote turns the result into
+// NaN.  Called by every thread at kernel entry; ends with a barrier.  A
+// no-op in normal builds.
+#ifndef GQA_DEBUG_NANFILL
+#define GQA_DEBUG_NANFILL 0
+#endif
+template <typename T>
+__device__ __forceinline__ void debug_nanfill(T &lds_obj)
+{
+#if GQA_DEBUG_NANFILL
+    unsigned *w = (unsigned *)&lds_obj;
+    for (unsigned i = threadIdx.x; i < sizeof(T) / 4; i += blockDim.x) w[i] = 0xffffffffu;
+    __syncthreads();
+#else
+    (void)lds_obj;
+#endif
+}
+
 // Workgroup barrier for LDS hand-off: this wave's LDS reads and writes are
 // complete (lgkmcnt(0)) before it arrives.  Unlike __syncthreads it does not
 // drain outstanding vector-memory operations, so copies for later tiles stay

@@ -8,6 +8,7 @@
 // read from LDS, the wave reduces max and sum with shuffles, and each lane
 // accumulates the output dims d = lane and lane + 64.  Grouped heads read
 // their KV head by address (g(a) = a / (Hq/Hkv)); nothing is copied.
+#include "device_common.h"
 #include "launch.h"
 
 namespace gqa {
@@ -80,6 +81,8 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(F32FwdArgs p)
 {
     __shared__ float sq[D];
     __shared__ float sk[kKB * (D + 1)];
+    debug_nanfill(sq);
+    debug_nanfill(sk);
     const int i = blockIdx.x, a = blockIdx.y, b = blockIdx.z;
     const int g = a / p.G;
     const int lane = threadIdx.x;
@@ -101,6 +104,8 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs p)
 {
     __shared__ float sq[D];
     __shared__ float sk[kKB * (D + 1)];
+    debug_nanfill(sq);
+    debug_nanfill(sk);
     const int split = blockIdx.x, a = blockIdx.y, b = blockIdx.z;
     const int g = a / p.G;
     const int lane = threadIdx.x;

@@ -122,6 +122,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
     using Tile = PlaneTile<kBN>;
 
     __shared__ __attribute__((aligned(1024))) FwdSmem<D> sm;
+    debug_nanfill(sm);
 
     // ---- workgroup -> (unit, query tile), heaviest first ----
     // Dense: all units carry the same work, so consecutive query tiles of a

@@ -117,6 +117,9 @@ __global__ __launch_bounds__(kNT, 1) void mla_decode_kernel(DecodeArgs p)
     __shared__ __attribute__((aligned(16))) int sidx[SPARSE ? kMaxChunk : 4];  // staged index slice
     // sparse: open-addressing set of the slice's positions (entry indices)
     __shared__ unsigned htab[SPARSE ? 2 * kMaxChunk : 1];
+    debug_nanfill(sm);
+    debug_nanfill(sidx);
+    debug_nanfill(htab);
 
     // chunk-major order, as in the other decode kernel
     const int nbk = p.B * p.Hkv;
