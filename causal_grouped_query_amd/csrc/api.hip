@@ -103,7 +103,8 @@ int default_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int dtype)
         if (s > 64) s = 64;
         return (int)(s < 3 ? 3 : s);
     }
-    // fp32 path: one workgroup per (split, batch, KV head); ~2.5 workgroups
+    // fp32 path: one workgroup per (split, batch, KV head, 32 heads of its
+    // group); ~2.5 workgroups
     // per resident slot if every sequence were full length, chunks of at
     // least 256 keys
     long long s = (3200 + streams - 1) / streams;
@@ -114,8 +115,7 @@ int default_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int dtype)
     return (int)s;
 }
 
-// workspace: room for fp32 partial outputs [B, Hq, S, Dv] (the bf16 and fp8
-// paths store bf16 partials in its first half), then fp32 partial
+// workspace: fp32 partial outputs [B, Hq, S, Dv], then fp32 partial
 // log2-sum-exp [B, Hq, S]
 size_t ws_bytes(int B, int Hq, int Dv, int S)
 {
@@ -628,7 +628,7 @@ static int decode_impl(const void *q, const void *k, const void *v, void *out, c
         rc = gqa::launch_decode_bf16(a, Dk, Dv, st);
     } else {
         if (Hq > 65535 || B > 65535) return GQA_ERR_UNSUPPORTED;
-        a.n_hblk = 1;
+        a.n_hblk = (int)cdiv(G, 32);  // 32 query heads of the group per workgroup
         a.c = scale;  // the fp32 path works in natural-log units
         if (dry_run) return GQA_OK;
         debug_fill_workspace(workspace, need, st);

@@ -776,7 +776,10 @@ int decode_bf16_flat_workgroups(int Dk)
     // .. 3200 workgroups the ragged GQA decode is fastest at 2048 (226 us)
     // and clearly slower at 1280 (258 us) and above 2048 (244 .. 251 us).
     (void)Dk;
-    return 8 * 256;
+#ifndef GQA_DEC_WG_PER_CU
+#define GQA_DEC_WG_PER_CU 8
+#endif
+    return GQA_DEC_WG_PER_CU * 256;
 }
 
 // FP8 flat decode: one resident round of workgroups.  At 16.5 KiB of LDS

@@ -109,6 +109,7 @@ struct F32FwdArgs {
     float *out;
     int B, Hq, Hkv, Tq, Tk, G, causal;
     float scale;
+    int Gt, P, n_hblk;  // set by the launcher: heads x positions per workgroup, head blocks
 };
 int launch_fwd_f32(const F32FwdArgs &a, int D, hipStream_t stream);
 int launch_decode_f32(const DecodeArgs &a, int D, hipStream_t stream);

@@ -83,6 +83,7 @@ FWD_CASES = [
     (1, 4, 2, 64, 64, 64, True),       # exact tile multiples
     (2, 64, 1, 33, 1100, 128, True),   # MQA suffix, G=64
     (1, 2, 1, 5, 7, 64, True),         # smaller than one tile
+    (1, 40, 1, 50, 70, 64, True),      # G=40: a full and a ragged block of query heads
 ]
 
 
@@ -174,6 +175,7 @@ DEC_CASES = [
     (2, 4, 4, 300, 64, [64, 299]),
     (2, 16, 1, 260, 128, [200, 65]),
     (1, 6, 2, 100, 64, [100]),
+    (2, 40, 1, 300, 64, [300, 17]),    # G=40: two head blocks
 ]
 
 
