@@ -105,7 +105,7 @@ def traffic_for(kernel: str, launches_per_unit: int = 1):
     return t["bytes_per_launch"]
 
 
-PROFILE_WORKLOADS = ("prefill", "decode", "mqa", "mla", "topk", "swa", "fp8", "probes")
+PROFILE_WORKLOADS = ("prefill", "decode", "mqa", "mla", "topk", "topk64", "swa", "fp8", "shard", "merge", "probes")
 
 
 def _profile_call(torch, gqa, W, dev, name):
@@ -151,23 +151,63 @@ def _profile_call(torch, gqa, W, dev, name):
         return (lambda: gqa.decode_fp8(q, kc, vc, ks, vs, lens, scale=w.scale, num_splits=S, out=out,
                                        workspace=ws)), {"workload": w.name,
                                                         "kv_bytes_per_call": fp8_decode_bytes(w, lens_l)}
-    if name == "topk":
-        w = W.MLA_TOPK
-        q, kc, _, lens = W.decode_inputs(w, nan_tail=False)
-        sels = [W.topk_indices(dataclasses.replace(w, seed=w.seed + 10 * i), lens).to(dev) for i in range(8)]
-        sel_rows = [min(w.extra["topk"], n) for n in lens.tolist()]
-        q, kc, lens_d = q.to(dev), kc.to(dev), lens.to(dev)
-        out = torch.empty((w.B, w.Hq, 1, w.Dv), dtype=torch.bfloat16, device=dev)
-        S = gqa.decode_topk_splits(w.B, w.Hq, w.extra["topk"], w.Dk, w.Dv, gqa.GQA_BF16)
-        ws = torch.empty(gqa.decode_workspace_size(w.B, w.Hq, w.Dv, S), dtype=torch.uint8, device=dev)
-        turn = [0]
-
-        def fn():
-            idx = sels[turn[0] % len(sels)]
-            turn[0] += 1
-            gqa.decode_topk(q, kc, lens_d, idx, scale=w.scale, num_splits=S, out=out, workspace=ws)
+    if name in ("topk", "topk64"):
+        w = W.MLA_TOPK if name == "topk" else W.MLA_TOPK_B64
+        fn, S, sel_rows = _topk_call(torch, gqa, W, dev, w)
         return fn, {"workload": w.name, "kv_bytes_per_call": topk_bytes(w, sel_rows), "splits": S}
+    if name in ("shard", "merge"):
+        # one device's key shard under sequence parallelism (the heaviest: every
+        # key visible to every query), and the merge of all shards' partials
+        w = W.CP_SHARD
+        nsh, q_pos0 = w.extra["shards"], w.extra["q_pos0"]
+        q = W.fwd_inputs(w)[0].to(dev)
+        outs = torch.empty((nsh, w.B, w.Hq, w.Tq, w.Dv), dtype=torch.float32, device=dev)
+        lses = torch.empty((nsh, w.B, w.Hq, w.Tq), dtype=torch.float32, device=dev)
+        kv0 = None
+        for r in range(nsh):
+            _, k, v = W.fwd_inputs(dataclasses.replace(w, seed=w.seed + 10 * r))
+            k, v = k.to(dev), v.to(dev)
+            gqa.attention_shard(q, k, v, q_pos0, r * w.Tk, scale=w.scale, out=outs[r], lse=lses[r])
+            kv0 = kv0 or (k, v)
+        if name == "shard":
+            k0, v0 = kv0
+            return (lambda: gqa.attention_shard(q, k0, v0, q_pos0, 0, scale=w.scale, out=outs[0], lse=lses[0])), {
+                "workload": w.name, "flop_per_call": 2.0 * (w.Dk + w.Dv) * w.Tq * w.Tk * w.Hq * w.B}
+        merged = torch.empty((w.B, w.Hq, w.Tq, w.Dv), dtype=torch.bfloat16, device=dev)
+        mb = float(outs.numel() * 4 + lses.numel() * 4 + merged.numel() * 2)
+        return (lambda: gqa.merge(outs, lses, out=merged)), {
+            "workload": "context_parallel_merge_8_shards_262144_rows_d128", "kv_bytes_per_call": mb}
     raise ValueError(name)
+
+
+def _topk_call(torch, gqa, W, dev, w):
+    """A top-k decode call over eight selections in turn (one selection's rows
+    would be served from the Infinity Cache after the first call).  Batch 16
+    draws its inputs as the parity tests do; the batch-64 cache (2.4 GB) is
+    drawn on the device, for timing only."""
+    if w.B <= 16:
+        q, kc, _, lens = W.decode_inputs(w, nan_tail=False)
+        q, kc = q.to(dev), kc.to(dev)
+    else:
+        lens = W.decode_lengths(w)
+        g = torch.Generator(device=dev).manual_seed(w.seed)
+        q = torch.randn((w.B, w.Hq, 1, w.Dk), generator=g, device=dev).to(torch.bfloat16)
+        kc = torch.empty((w.B, 1, w.Tk, w.Dk), dtype=torch.bfloat16, device=dev)
+        for b in range(w.B):  # one sequence at a time: no 4.8 GB fp32 temporary
+            kc[b].copy_(torch.randn((1, w.Tk, w.Dk), generator=g, device=dev))
+    sels = [W.topk_indices(dataclasses.replace(w, seed=w.seed + 10 * i), lens).to(dev) for i in range(8)]
+    sel_rows = [min(w.extra["topk"], n) for n in lens.tolist()]
+    lens_d = lens.to(dev)
+    out = torch.empty((w.B, w.Hq, 1, w.Dv), dtype=torch.bfloat16, device=dev)
+    S = gqa.decode_topk_splits(w.B, w.Hq, w.extra["topk"], w.Dk, w.Dv, gqa.GQA_BF16)
+    ws = torch.empty(gqa.decode_workspace_size(w.B, w.Hq, w.Dv, S), dtype=torch.uint8, device=dev)
+    turn = [0]
+
+    def fn():
+        idx = sels[turn[0] % len(sels)]
+        turn[0] += 1
+        gqa.decode_topk(q, kc, lens_d, idx, scale=w.scale, num_splits=S, out=out, workspace=ws)
+    return fn, S, sel_rows
 
 
 def profile_one(torch, gqa, W, dev, name, steps, warmup) -> int:
@@ -555,31 +595,17 @@ def extra_workloads(torch, gqa, W, dev):
                    "kv_bytes_per_launch": b, "tokens_per_s": round(float(sum(lens.tolist())) / sec, 1)}
     del q, kc, vc, ks, vs, out, ws
 
-    w = W.MLA_TOPK
-    q, kc, _, lens = W.decode_inputs(w, nan_tail=False)
-    q, kc, lens_d = q.to(dev), kc.to(dev), lens.to(dev)
-    # eight selections in turn (302 MB of rows in all): one selection (38 MB)
-    # would be served from the Infinity Cache after the first call
-    sels = [W.topk_indices(dataclasses.replace(w, seed=w.seed + 10 * i), lens).to(dev) for i in range(8)]
-    out = torch.empty((w.B, w.Hq, 1, w.Dv), dtype=torch.bfloat16, device=dev)
-    S = gqa.decode_topk_splits(w.B, w.Hq, w.extra["topk"], w.Dk, w.Dv, gqa.GQA_BF16)
-    ws = torch.empty(gqa.decode_workspace_size(w.B, w.Hq, w.Dv, S), dtype=torch.uint8, device=dev)
-    turn = [0]
-
-    def topk():
-        idx = sels[turn[0] % len(sels)]
-        turn[0] += 1
-        gqa.decode_topk(q, kc, lens_d, idx, scale=w.scale, num_splits=S, out=out, workspace=ws)
-
-    sec = _time(torch, topk, reps=16, warm=8)
-    sel_rows = [min(w.extra["topk"], n) for n in lens.tolist()]
-    b = topk_bytes(w, sel_rows)
-    f = decode_flops(w, sel_rows)
-    res[w.name] = {"us": round(sec * 1e6, 1), "GB/s": round(b / sec / 1e9, 1),
-                   "frac_hbm_peak": round(b / sec / 1e9 / PEAK_HBM_GBPS, 4),
-                   "TFLOP/s": round(f / sec / 1e12, 2), "splits": S, "topk": w.extra["topk"],
-                   "kv_bytes_per_launch": b}
-    del q, kc, out, ws, sels
+    for w in (W.MLA_TOPK, W.MLA_TOPK_B64):
+        topk, S, sel_rows = _topk_call(torch, gqa, W, dev, w)
+        sec = _time(torch, topk, reps=16, warm=8)
+        b = topk_bytes(w, sel_rows)
+        f = decode_flops(w, sel_rows)
+        res[w.name] = {"us": round(sec * 1e6, 1), "GB/s": round(b / sec / 1e9, 1),
+                       "frac_hbm_peak": round(b / sec / 1e9 / PEAK_HBM_GBPS, 4),
+                       "TFLOP/s": round(f / sec / 1e12, 2), "splits": S, "topk": w.extra["topk"],
+                       "kv_bytes_per_launch": b}
+        del topk
+        torch.cuda.empty_cache()
 
     w = W.CP_SHARD
     nsh, q_pos0 = w.extra["shards"], w.extra["q_pos0"]

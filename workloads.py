@@ -108,6 +108,13 @@ MLA_TOPK = Workload("mla_dsa_topk2048_decode_b16_hq128_tk32768_dk576_dv512", "ml
                     extra={"topk": 2048})
 
 
+# The same top-k decode at batch 64 (a serving batch: one workgroup per
+# sequence and head block already fills the device).
+MLA_TOPK_B64 = Workload("mla_dsa_topk2048_decode_b64_hq128_tk32768_dk576_dv512", "mla_topk_decode", 64, 128, 1,
+                        1, 32768, 576, 512, "bf16", 9, 1.0 / math.sqrt(192), len_lo=4096, len_hi=32768,
+                        extra={"topk": 2048})
+
+
 # The GQA decode shape over an FP8 E4M3 cache with one scale per row.
 GQA_DECODE_FP8 = Workload("gqa_decode_fp8kv_b64_hq32_hkv8_tmax8192_d128", "fp8_decode", 64, 32, 8, 1, 8192, 128, 128,
                           "bf16", 7, 1.0 / math.sqrt(128), len_lo=1024, len_hi=8192)
