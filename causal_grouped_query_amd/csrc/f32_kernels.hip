@@ -190,18 +190,21 @@ __global__ __launch_bounds__(64 * kNW) void decode_f32_kernel(DecodeArgs p)
 
 } // namespace
 
-// query rows of one workgroup: Gt heads of a group x P positions
-static void f32_row_blocks(int G, int &Gt, int &P, int &n_hblk)
+// query rows of one workgroup: Gt heads of a group x P positions; P halves
+// (down to 1) while the grid would have fewer than 512 workgroups, so a
+// small problem still spreads over the device
+static void f32_row_blocks(int G, int &Gt, int &P, int &n_hblk, long long positions = 1)
 {
     Gt = G < kRows ? G : kRows;
     P = kRows / Gt;
     n_hblk = (G + Gt - 1) / Gt;
+    while (P > 1 && positions * n_hblk / P < 512) P /= 2;
 }
 
 int launch_fwd_f32(const F32FwdArgs &a_in, int D, hipStream_t stream)
 {
     F32FwdArgs a = a_in;
-    f32_row_blocks(a.G, a.Gt, a.P, a.n_hblk);
+    f32_row_blocks(a.G, a.Gt, a.P, a.n_hblk, (long long)a.B * a.Hkv * a.Tq);
     const long long ny = (long long)a.Hkv * a.n_hblk;
     if (ny > 65535 || a.B > 65535) return -1;
     dim3 grid((unsigned)((a.Tq + a.P - 1) / a.P), (unsigned)ny, a.B), block(64 * kNW);
