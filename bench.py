@@ -561,7 +561,8 @@ def extra_workloads(torch, gqa, W, dev):
     f = decode_flops(w, lens.tolist())
     res[w.name] = {"us": round(sec * 1e6, 1), "GB/s": round(b / sec / 1e9, 1),
                    "frac_hbm_peak": round(b / sec / 1e9 / PEAK_HBM_GBPS, 4),
-                   "TFLOP/s": round(f / sec / 1e12, 1), "splits": S}
+                   "TFLOP/s": round(f / sec / 1e12, 1), "frac_mfma_peak": round(f / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
+                   "splits": S}
     del q, kc, out, ws
 
     # the GQA decode shape with a 4096-key sliding window (each query reads
@@ -602,7 +603,8 @@ def extra_workloads(torch, gqa, W, dev):
         f = decode_flops(w, sel_rows)
         res[w.name] = {"us": round(sec * 1e6, 1), "GB/s": round(b / sec / 1e9, 1),
                        "frac_hbm_peak": round(b / sec / 1e9 / PEAK_HBM_GBPS, 4),
-                       "TFLOP/s": round(f / sec / 1e12, 2), "splits": S, "topk": w.extra["topk"],
+                       "TFLOP/s": round(f / sec / 1e12, 2),
+                       "frac_mfma_peak": round(f / sec / 1e12 / PEAK_BF16_TFLOPS, 4), "splits": S, "topk": w.extra["topk"],
                        "kv_bytes_per_launch": b}
         del topk
         torch.cuda.empty_cache()
