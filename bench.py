@@ -252,8 +252,9 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(see DESIGN.md for how the work would shard).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path (KV-head groups would "
+              "split across GPUs without communication; key shards would exchange (o, lse) partials and "
+              "merge them with gqa_attn_merge).", file=sys.stderr)
         return 2
 
     import torch
