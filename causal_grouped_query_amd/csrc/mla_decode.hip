@@ -53,6 +53,7 @@ constexpr int kKS = kDK / 32;   // 18 contraction steps of 32 dims
 constexpr int kDB = kDV / 16;   // 32 output blocks of 16 dims
 constexpr int kMaxChunk = 4096;  // index-list entries one sparse workgroup stages
 static_assert(kTK * kCPR % 64 == 0, "tile is whole wave copies");
+constexpr int kCopiesMax = (kTK * kCPR / 64 + kNW - 1) / kNW;  // wave copies per tile, at most
 
 struct MlaSmem {
     uint16_t k[kStages][kTK * kDK];
@@ -167,17 +168,63 @@ __global__ __launch_bounds__(kNT, 1) void mla_decode_kernel(DecodeArgs p)
     // (36 copies: waves 0-3 do 5, waves 4-7 do 4; the count per wave is fixed)
     const int my_copies = (NCOPY - w + kNW - 1) / kNW;
     using Tile = PlaneTile<kTK, true>;
+    // Copy j fills LDS slots 64 j + lane of the plane layout: tile row
+    // 16 (j & 1) + lrow, chunk 4 (j >> 1) + lchunk, with the lane's row and
+    // chunk inside a 16-row half-plane fixed (rows r and r + 16 share the
+    // swizzle).  A copy is then a workgroup-uniform base plus a per-lane
+    // unsigned 32-bit byte offset: for a full dense tile one fixed offset
+    // serves every copy; otherwise the offset is the fetched row times the
+    // row pitch plus the lane's chunk.  Caches whose offsets could pass
+    // 2^32 take per-lane 64-bit addresses instead.  The copy loops stay
+    // rolled: unrolled, their per-copy values stay live beside the 200
+    // registers of Q^T and O^T and the tile loop spills.
+    const int lrow = lane >> 2;
+    auto lane_chunk16 = [&]() { return (unsigned)(((lane & 3) ^ pswz16(lrow)) * 16); };
+    const unsigned pitch = (unsigned)p.k_st * 2u;  // bytes between key rows
+    // dense: offset of the lane's slot from its copy's base; sparse: its chunk
+    const unsigned lane_off = SPARSE ? lane_chunk16() : (unsigned)lrow * pitch + lane_chunk16();
+    const bool off32 = (long long)(SPARSE ? p.Tmax : kTK) * p.k_st * 2 + kDK * 2 < (1LL << 32);
+    const unsigned ring_lds = lds_u32(&sm) + (unsigned)(w * 64 * 16);
     auto issue_tile = [&](int k0, int slot) {
-        for (int j = w; j < NCOPY; j += kNW) {
-            int row, chunk;
-            Tile::slot_source(j * 64 + lane, row, chunk);
-            int pos;
-            if (SPARSE) {
-                pos = min(max(sidx[k0 - kbeg + row], 0), len - 1);  // in range for any entry
-            } else {
-                pos = min(k0 + row, kend - 1);
+        const unsigned dst = ring_lds + (unsigned)(slot * kTK * kDK * 2);
+        if (!SPARSE && off32 && k0 + kTK <= kend) {
+#pragma unroll 1
+            for (int jj = 0; jj < kCopiesMax; ++jj) {
+                const int j = w + kNW * jj;
+                if (j < NCOPY)
+                    g2lds16_at(kb + (size_t)(k0 + 16 * (j & 1)) * p.k_st + 32 * (j >> 1), lane_off,
+                               dst + (unsigned)(jj * kNW * 64 * 16));
             }
-            g2lds16(kb + (size_t)pos * p.k_st + chunk * 8, &sm.k[slot][j * 64 * 8]);
+        } else if (off32) {
+            // sparse: rows named by the staged list; dense: the tail tile,
+            // rows past kend re-read row kend - 1 (masked)
+            const uint16_t *base = SPARSE ? kb : kb + (size_t)k0 * p.k_st;
+#pragma unroll 1
+            for (int jj = 0; jj < kCopiesMax; ++jj) {
+                const int j = w + kNW * jj;
+                if (j >= NCOPY) continue;
+                const int row = 16 * (j & 1) + lrow;
+                unsigned off;
+                if (SPARSE) {
+                    const int pos = min(max(sidx[k0 - kbeg + row], 0), len - 1);  // in range for any entry
+                    off = (unsigned)pos * pitch + lane_off;
+                } else {
+                    off = lane_off + (unsigned)(min(row, kend - 1 - k0) - lrow) * pitch;
+                }
+                g2lds16_at(base + 32 * (j >> 1), off, dst + (unsigned)(jj * kNW * 64 * 16));
+            }
+        } else {
+            unsigned lc = lane_chunk16();
+            asm volatile("" : "+v"(lc));  // computed here: no 64-bit per-lane value lives across the loop
+#pragma unroll 1
+            for (int jj = 0; jj < kCopiesMax; ++jj) {
+                const int j = w + kNW * jj;
+                if (j >= NCOPY) continue;
+                const int row = 16 * (j & 1) + lrow;
+                const int pos = SPARSE ? min(max(sidx[k0 - kbeg + row], 0), len - 1) : min(k0 + row, kend - 1);
+                g2lds16_at((const char *)(kb + (size_t)pos * p.k_st + 32 * (j >> 1)) + lc,
+                           dst + (unsigned)(jj * kNW * 64 * 16));
+            }
         }
     };
 
