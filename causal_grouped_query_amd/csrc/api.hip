@@ -421,7 +421,7 @@ GQA_API int gqa_attn_decode_topk(const void *q, const void *kv, void *out, const
     a.k_st = a.v_st = kv_st;
     a.S = S;
     a.chunk = chunk;
-    a.n_hblk = (int)cdiv(Hq, 128);
+    a.n_hblk = (int)cdiv(Hq, gqa::mla_heads_per_block());
     a.c = folded_scale(scale);
     a.idx = indices;
     a.topk = topk;

@@ -764,7 +764,7 @@ int decode_bf16_key_tile() { return kTK; }
 // Query heads one workgroup covers for a head-dim pair and group size.
 int decode_bf16_heads_per_block(int Dk, int G)
 {
-    if (Dk == 576) return 128;
+    if (Dk == 576) return mla_heads_per_block();
     (void)G;
     return 32;
 }

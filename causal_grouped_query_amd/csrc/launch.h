@@ -97,6 +97,7 @@ int launch_mla_decode(const DecodeArgs &a, hipStream_t stream);
 // The same over the positions listed in a.idx; chunk <= mla_topk_max_chunk().
 int launch_mla_decode_topk(const DecodeArgs &a, hipStream_t stream);
 int mla_topk_max_chunk();
+int mla_heads_per_block();
 int decode_bf16_key_tile();
 // Flat (persistent, balanced) decode for Dk = Dv <= 128: workgroups to launch.
 int decode_bf16_flat_workgroups(int Dk);

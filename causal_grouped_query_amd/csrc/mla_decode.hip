@@ -7,7 +7,8 @@
 //
 // A workgroup owns 128 query heads of one sequence and one key chunk; the
 // key tile (32 keys x 576) is copied HBM -> LDS once with global_load_lds
-// into a 3-deep ring and read by all 8 waves.  Wave w owns 16 heads and works
+// into a ring (4 deep, 3 for the top-k flavour, whose staged index list
+// takes LDS) and read by all 8 waves.  Wave w owns 16 heads and works
 // with v_mfma_f32_16x16x32_bf16, so its whole state fits one wave's share of
 // the register file (2 waves per SIMD): Q^T over 576 dims (72 VGPRs) and O^T
 // over 512 dims (128 accumulators).  Per tile and wave:
@@ -41,10 +42,18 @@ namespace {
 constexpr int kTK = 32;      // keys per tile
 constexpr int kDK = 576;     // key width (latent 512 + rope 64)
 constexpr int kDV = 512;     // value width (the latent)
-constexpr int kNW = 8;       // waves per workgroup
+#ifndef GQA_MLA_NW
+#define GQA_MLA_NW 8
+#endif
+#ifndef GQA_MLA_STAGES
+#define GQA_MLA_STAGES 4  // key-tile ring depth of the dense kernel
+#endif
+constexpr int kNW = GQA_MLA_NW;  // waves per workgroup
 constexpr int kNT = 64 * kNW;
 constexpr int kHW = 16;      // heads per wave
-constexpr int kStages = 3;
+constexpr int kStagesDense = GQA_MLA_STAGES;
+constexpr int kStagesSparse = 3;  // the staged index list takes the rest of the LDS
+constexpr int kBlocksPerCu = 8 / kNW;  // two waves per SIMD
 #ifndef GQA_MLA_PF
 #define GQA_MLA_PF 6  // operand reads issued ahead of the MFMAs (0: compiler's choice)
 #endif
@@ -55,8 +64,9 @@ constexpr int kMaxChunk = 4096;  // index-list entries one sparse workgroup stag
 static_assert(kTK * kCPR % 64 == 0, "tile is whole wave copies");
 constexpr int kCopiesMax = (kTK * kCPR / 64 + kNW - 1) / kNW;  // wave copies per tile, at most
 
+template <int STAGES>
 struct MlaSmem {
-    uint16_t k[kStages][kTK * kDK];
+    uint16_t k[STAGES][kTK * kDK];
 };
 
 // The index mask of the DSA page is a scatter: a position listed twice is
@@ -111,10 +121,11 @@ __device__ __forceinline__ void dedup_slice(int *sidx, unsigned *htab, int n, in
 }
 
 template <bool SPARSE>
-__global__ __launch_bounds__(kNT, 1) void mla_decode_kernel(DecodeArgs p)
+__global__ __launch_bounds__(kNT, kBlocksPerCu) void mla_decode_kernel(DecodeArgs p)
 {
     constexpr int NCOPY = kTK * kCPR / 64;  // 36 wave-copies per tile, spread over 8 waves
-    __shared__ __attribute__((aligned(1024))) MlaSmem sm;
+    constexpr int kStages = SPARSE ? kStagesSparse : kStagesDense;
+    __shared__ __attribute__((aligned(1024))) MlaSmem<kStages> sm;
     __shared__ __attribute__((aligned(16))) int sidx[SPARSE ? kMaxChunk : 4];  // staged index slice
     // sparse: open-addressing set of the slice's positions (entry indices)
     __shared__ unsigned htab[SPARSE ? 2 * kMaxChunk : 1];
@@ -275,10 +286,10 @@ __global__ __launch_bounds__(kNT, 1) void mla_decode_kernel(DecodeArgs p)
         const int slot = it % kStages;
         // tile `it` must have landed; the next tile's copies may still fly
         if (it + kStages - 2 < ntiles) {
-            if (my_copies == 5)
-                wait_vmem_le<5>();
+            if (my_copies == kCopiesMax)
+                wait_vmem_le<kCopiesMax * (kStages - 2)>();
             else
-                wait_vmem_le<4>();
+                wait_vmem_le<(kCopiesMax - 1) * (kStages - 2)>();
         } else {
             wait_vmem();
         }
@@ -392,6 +403,7 @@ int launch_mla_decode(const DecodeArgs &a, hipStream_t stream)
 }
 
 int mla_topk_max_chunk() { return kMaxChunk; }
+int mla_heads_per_block() { return kHW * kNW; }
 
 int launch_mla_decode_topk(const DecodeArgs &a, hipStream_t stream)
 {

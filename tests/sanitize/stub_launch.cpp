@@ -39,6 +39,7 @@ int launch_decode_fp8(const DecodeArgs &a, int Dk, int Dv, hipStream_t s) { retu
 int launch_mla_decode(const DecodeArgs &a, hipStream_t s) { return launch_decode_bf16(a, 576, 512, s); }
 int launch_mla_decode_topk(const DecodeArgs &a, hipStream_t s) { return launch_decode_bf16(a, 576, 512, s); }
 int mla_topk_max_chunk() { return 4096; }
+int mla_heads_per_block() { return 128; }
 int decode_bf16_key_tile() { return 32; }
 int decode_bf16_flat_workgroups(int) { return 2048; }
 int decode_fp8_flat_workgroups(int) { return 2048; }
