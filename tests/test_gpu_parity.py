@@ -281,6 +281,31 @@ def test_mla_absorbed_decode_matches_oracle(Hq, splits):
     _check(out, ref, "bf16", f"mla Hq={Hq} S={splits}")
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("rising", [True, False])
+def test_mla_decode_reference_moves(splits, rising):
+    """Absorbed MLA whose scores climb (or fall) by ~60 in log2 units along
+    the sequence: every key is pulled toward the query direction by a ramp,
+    so a head's running reference max has to move many times mid-chunk (the
+    rescale path), or never after the first tile."""
+    B, Hq, Tmax = 2, 128, 900
+    lens = [900, 517]
+    q = _rand((B, Hq, 1, 576), 91, "bf16")
+    k = _rand((B, 1, Tmax, 576), 92, "bf16").float()
+    qd = q.float()[:, 0, 0, :]  # head 0's direction, shared by all heads of the draw
+    qd = qd / qd.norm(dim=-1, keepdim=True)
+    ramp = torch.linspace(0.0, 25.0, Tmax) if rising else torch.linspace(25.0, 0.0, Tmax)
+    k = (k + ramp[None, None, :, None] * qd[:, None, None, :]).to(torch.bfloat16)
+    for b, n in enumerate(lens):
+        k[b, :, n:] = float("nan")
+    kd = k.cuda()
+    scale = 1.0 / math.sqrt(192)
+    out = gqa.decode(q.cuda(), kd, kd[..., :512], torch.tensor(lens, dtype=torch.int32).cuda(), scale=scale,
+                     num_splits=splits)
+    ref = O.attention(q, k, k[..., :512], scale, True, kv_lens=lens)
+    _check(out, ref, "bf16", f"mla ramp rising={rising} S={splits}")
+
+
 def test_mla_decode_empty_and_short_sequences():
     """Absorbed MLA with an empty sequence (zero output) and sequences shorter
     than one 32-key tile, several splits (most of them empty)."""

@@ -91,6 +91,27 @@ def test_topk_decode_empty_selections_and_sequences():
     _check(out, ref, "topk empty / single")
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+def test_topk_reference_moves_out_of_order(splits):
+    """Scores that climb by ~60 in log2 units along the cache, visited in the
+    random order of a selection list: a head's reference max moves whenever a
+    later entry names a much larger score (the rescale path, in any order)."""
+    B, Hq, T, topk = 2, 128, 900, 640
+    lens = np.array([900, 700], dtype=np.int32)
+    q = _rand((B, Hq, 1, 576), 240)
+    kv = _rand((B, 1, T, 576), 241).float()
+    qd = q.float()[:, 0, 0, :]
+    qd = qd / qd.norm(dim=-1, keepdim=True)
+    kv = (kv + torch.linspace(0.0, 25.0, T)[None, None, :, None] * qd[:, None, None, :]).to(torch.bfloat16)
+    for b, n in enumerate(lens):
+        kv[b, :, n:, :] = float("nan")
+    rng = np.random.default_rng(242)
+    idx = np.stack([rng.permutation(int(n))[:topk] for n in lens]).astype(np.int32)
+    out = _run(q, kv, lens, idx, splits)
+    ref = O.decode_topk(q, kv, lens, idx, SCALE, 512)
+    _check(out, ref, f"topk ramp S={splits}")
+
+
 def test_topk_all_positions_equals_dense_mla_decode():
     """Selecting every position in order with the same slicing gives the
     dense MLA decode bit for bit (same tiles, same arithmetic)."""
