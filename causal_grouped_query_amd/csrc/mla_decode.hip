@@ -185,20 +185,22 @@ __global__ __launch_bounds__(kNT, kBlocksPerCu) void mla_decode_kernel(DecodeArg
     // swizzle).  A copy is then a workgroup-uniform base plus a per-lane
     // unsigned 32-bit byte offset: for a full dense tile one fixed offset
     // serves every copy; otherwise the offset is the fetched row times the
-    // row pitch plus the lane's chunk.  Caches whose offsets could pass
-    // 2^32 take per-lane 64-bit addresses instead.  The copy loops stay
-    // rolled: unrolled, their per-copy values stay live beside the 200
-    // registers of Q^T and O^T and the tile loop spills.
+    // row pitch plus the lane's chunk.  Dense offsets stay inside one tile,
+    // under 2^31 since the host bounds the row pitch to 2^25 elements; a
+    // top-k cache whose offsets from its first row could pass 2^32 takes
+    // per-lane 64-bit addresses instead.  The copy loops stay rolled:
+    // unrolled, their per-copy values stay live beside the 200 registers of
+    // Q^T and O^T and the tile loop spills.
     const int lrow = lane >> 2;
     auto lane_chunk16 = [&]() { return (unsigned)(((lane & 3) ^ pswz16(lrow)) * 16); };
     const unsigned pitch = (unsigned)p.k_st * 2u;  // bytes between key rows
     // dense: offset of the lane's slot from its copy's base; sparse: its chunk
     const unsigned lane_off = SPARSE ? lane_chunk16() : (unsigned)lrow * pitch + lane_chunk16();
-    const bool off32 = (long long)(SPARSE ? p.Tmax : kTK) * p.k_st * 2 + kDK * 2 < (1LL << 32);
+    const bool off32 = !SPARSE || (long long)p.Tmax * p.k_st * 2 + kDK * 2 < (1LL << 32);
     const unsigned ring_lds = lds_u32(&sm) + (unsigned)(w * 64 * 16);
     auto issue_tile = [&](int k0, int slot) {
         const unsigned dst = ring_lds + (unsigned)(slot * kTK * kDK * 2);
-        if (!SPARSE && off32 && k0 + kTK <= kend) {
+        if (!SPARSE && k0 + kTK <= kend) {
 #pragma unroll 1
             for (int jj = 0; jj < kCopiesMax; ++jj) {
                 const int j = w + kNW * jj;
@@ -224,7 +226,7 @@ __global__ __launch_bounds__(kNT, kBlocksPerCu) void mla_decode_kernel(DecodeArg
                 }
                 g2lds16_at(base + 32 * (j >> 1), off, dst + (unsigned)(jj * kNW * 64 * 16));
             }
-        } else {
+        } else if constexpr (SPARSE) {
             unsigned lc = lane_chunk16();
             asm volatile("" : "+v"(lc));  // computed here: no 64-bit per-lane value lives across the loop
 #pragma unroll 1
@@ -232,7 +234,7 @@ __global__ __launch_bounds__(kNT, kBlocksPerCu) void mla_decode_kernel(DecodeArg
                 const int j = w + kNW * jj;
                 if (j >= NCOPY) continue;
                 const int row = 16 * (j & 1) + lrow;
-                const int pos = SPARSE ? min(max(sidx[k0 - kbeg + row], 0), len - 1) : min(k0 + row, kend - 1);
+                const int pos = min(max(sidx[k0 - kbeg + row], 0), len - 1);
                 g2lds16_at((const char *)(kb + (size_t)pos * p.k_st + 32 * (j >> 1)) + lc,
                            dst + (unsigned)(jj * kNW * 64 * 16));
             }

@@ -5,6 +5,8 @@ Long caches stress the 32-bit in-tile offsets and the balanced decode's
 tile arithmetic (one stream of 32768 tiles), long prefills the grid and
 causal-tile arithmetic, many packed sequences the device-side tile search,
 and long top-k lists the index slicing (slices of at most 4096 entries).
+A top-k cache whose row offsets pass 2^32 bytes (4.4 GB) takes the MLA
+kernel's 64-bit copy addresses.
 """
 import numpy as np
 import pytest
@@ -117,3 +119,28 @@ def test_topk_long_selection(topk, splits):
                           scale=1.0 / np.sqrt(192.0), num_splits=splits)
     ref = O.decode_topk(q, kv, lens, idx, 1.0 / np.sqrt(192.0), 512)
     _check(out, ref, f"top-{topk} S={splits}")
+
+
+def test_topk_cache_past_4gib():
+    """Top-k decode on a 3.8M-row latent cache (4.4 GB): selected rows past
+    2^32 bytes from the cache start take the 64-bit per-lane copy path.  Only
+    the rows the kernel can read are written (the selected ones, the first
+    and the last); the reference runs on those rows alone."""
+    T, topk = 3_800_000, 256
+    q = _rand((1, 128, 1, 576), 470)
+    rng = np.random.default_rng(471)
+    far = rng.choice(np.arange(3_730_000, T - 1), 160, replace=False)
+    near = rng.choice(np.arange(1, 100_000), 80, replace=False)
+    sel = np.concatenate([far, near, [0, T - 1]]).astype(np.int32)
+    idx = np.concatenate([rng.permutation(sel), np.full(topk - sel.size, -1, np.int32)]).astype(np.int32)
+    rows = _rand((sel.size, 576), 472)
+    kvd = torch.empty((1, 1, T, 576), dtype=torch.bfloat16, device="cuda")
+    kvd[0, 0, torch.from_numpy(sel).long().cuda()] = rows.cuda()
+    out = gqa.decode_topk(q.cuda(), kvd, torch.tensor([T], dtype=torch.int32).cuda(),
+                          torch.from_numpy(idx[None]).cuda(), scale=1.0 / np.sqrt(192.0), num_splits=2)
+    compact = rows.reshape(1, 1, sel.size, 576)
+    pos_of = {int(p): i for i, p in enumerate(sel)}
+    cidx = np.array([[pos_of.get(int(p), -1) for p in idx]], dtype=np.int32)
+    ref = O.decode_topk(q, compact, np.array([sel.size], dtype=np.int32), cidx, 1.0 / np.sqrt(192.0), 512)
+    _check(out, ref, "top-k over a 4.4 GB cache")
+    del kvd
