@@ -139,7 +139,7 @@ bool fwd_geometry(gqa::FwdArgs &a, int B, int Hq, int Hkv, int Tq)
     const int waves = gqa::fwd_bf16_waves_per_block();
     const int rpw = gqa::fwd_bf16_rows_per_wave();
     int gt = 1;
-    while (gt * 2 <= waves && G % (gt * 2) == 0) gt *= 2;
+    while (gt * 2 <= waves && G % (gt * 2) == 0 && waves % (gt * 2) == 0) gt *= 2;
     a.Gt = gt;
     a.Pt = rpw * (waves / gt);
     a.n_hblk = G / gt;
