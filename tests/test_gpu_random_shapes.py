@@ -73,6 +73,34 @@ def test_random_forward(i):
     _check(out, ref, dtype, what)
 
 
+@pytest.mark.parametrize("i", range(8))
+def test_random_forward_many_tiles(i):
+    """Longer sequences (several query tiles and key tiles per workgroup,
+    several head blocks), checked on sampled rows: tile and head-block
+    edges of the first and last heads plus 400 random rows."""
+    rng = np.random.default_rng(20000 + i)
+    Hkv = int(rng.choice([1, 2, 4]))
+    Hq = Hkv * int(rng.choice([1, 2, 3, 4, 6, 8, 12, 16, 32]))
+    B = int(rng.integers(1, 3))
+    D = int(rng.choice([64, 128]))
+    causal = bool(rng.integers(0, 4))
+    Tq = int(rng.integers(300, 2500))
+    Tk = Tq + int(rng.integers(0, 1500)) if causal else int(rng.integers(200, 3000))
+    dtype = "f32" if i % 4 == 0 else "bf16"
+    what = f"fwd rows B={B} Hq={Hq} Hkv={Hkv} Tq={Tq} Tk={Tk} D={D} causal={causal} {dtype}"
+    print(what, flush=True)
+    g = torch.Generator("cpu").manual_seed(21000 + i)
+    q, k, v = _rand((B, Hq, Tq, D), g, dtype), _rand((B, Hkv, Tk, D), g, dtype), _rand((B, Hkv, Tk, D), g, dtype)
+    scale = 1.0 / math.sqrt(D)
+    out = gqa.attention(q.cuda(), k.cuda(), v.cuda(), scale=scale, causal=causal)
+    n = B * Hq * Tq
+    edges = [(b * Hq + a) * Tq + p for b in range(B) for a in (0, Hq - 1) for p in (0, 63, 64, 255, 256, Tq - 1)
+             if p < Tq]
+    rows = np.unique(np.concatenate([rng.integers(0, n, 400), [0, n - 1], edges]))
+    ref = O.attention(q, k, v, scale, causal, rows=rows.tolist())
+    _check(out.reshape(n, D)[torch.from_numpy(rows).cuda()], ref, dtype, what)
+
+
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_decode(i):
     rng = np.random.default_rng(7000 + i)
