@@ -54,6 +54,7 @@ constexpr int kHW = 16;      // heads per wave
 constexpr int kStagesDense = GQA_MLA_STAGES;
 constexpr int kStagesSparse = 3;  // the staged index list takes the rest of the LDS
 constexpr int kBlocksPerCu = 8 / kNW;  // two waves per SIMD
+static_assert(kNW == 4 || kNW == 8, "four or eight waves of 16 heads");
 #ifndef GQA_MLA_PF
 #define GQA_MLA_PF 6  // operand reads issued ahead of the MFMAs (0: compiler's choice)
 #endif
