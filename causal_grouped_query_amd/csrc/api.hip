@@ -90,13 +90,17 @@ int default_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int dtype)
     const long long streams = (long long)B * Hkv * cdiv(G, 32);
     if (dtype == GQA_BF16) {
         // flat decode: S bounds the pieces any stream may be cut into.  The
-        // kernel runs min(resident workgroups, ~T (S-2) / (n_max + S - 4))
-        // workgroups for T key tiles in all and n_max in the longest stream;
-        // with every sequence full, T = streams * n_max, so S - 2 of twice
-        // the resident workgroups per stream keeps all of them busy even when
-        // the lengths are ragged.
+        // kernel cuts its T key tiles into at most ~T (S-2) / (n_max + S - 4)
+        // pieces (n_max tiles in the longest stream), and the pieces after
+        // its first round hold no fewer than (n_max - 2) / (S - 1) tiles.
+        // With every sequence full, T = streams * n_max, so S - 2 of twice
+        // the pieces per stream keeps the grid full even when the lengths
+        // are ragged, and four times that lets the last pieces shrink to
+        // about a quarter of an even share (measured on the ragged GQA
+        // decode, 512 streams: 34, whose smallest piece is that of 32, beats
+        // 10, 16, 24, 48 and 64).
         const long long wgs = gqa::decode_bf16_flat_workgroups(Dk);
-        long long s = 2 + (2 * wgs + streams - 1) / streams;
+        long long s = 2 + 4 * ((2 * wgs + streams - 1) / streams);
         const long long cap = 2 + cdiv(Tmax, 32);
         if (s < 8) s = 8;
         if (s > cap) s = cap;
@@ -116,12 +120,14 @@ int default_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int dtype)
 }
 
 // workspace: fp32 partial outputs [B, Hq, S, Dv], then fp32 partial
-// log2-sum-exp [B, Hq, S]
+// log2-sum-exp [B, Hq, S], then (at the next 256-byte boundary) 256 bytes
+// for the flat decode's piece counter
+constexpr size_t kQueueBytes = 256;
 size_t ws_bytes(int B, int Hq, int Dv, int S)
 {
     const size_t rows = (size_t)B * Hq * S;
     size_t bytes = rows * Dv * sizeof(float) + rows * sizeof(float);
-    return (bytes + 255) & ~(size_t)255;
+    return ((bytes + 255) & ~(size_t)255) + kQueueBytes;
 }
 
 // Workgroup geometry of the bf16 forward kernel: one wave owns one query
@@ -534,7 +540,8 @@ GQA_API size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_spl
 // Workspace layouts of the decode: the caller-sized one (fp32 partial
 // outputs [B, Hq, S, Dv], then the fp32 partial LSE [B, Hq, S]) and the
 // compact one of the allocation-free entry point (the same partials, then
-// the LSE at the next 256-byte boundary).
+// the LSE at the next 256-byte boundary); both end in the 256-byte piece
+// counter region.
 static size_t compact_ws_lse_offset(int B, int Hq, int Dv, int S, int dtype)
 {
     const size_t rows = (size_t)B * Hq * S;
@@ -543,7 +550,8 @@ static size_t compact_ws_lse_offset(int B, int Hq, int Dv, int S, int dtype)
 }
 static size_t compact_ws_bytes(int B, int Hq, int Dv, int S, int dtype)
 {
-    return compact_ws_lse_offset(B, Hq, Dv, S, dtype) + (size_t)B * Hq * S * sizeof(float);
+    const size_t bytes = compact_ws_lse_offset(B, Hq, Dv, S, dtype) + (size_t)B * Hq * S * sizeof(float);
+    return ((bytes + 255) & ~(size_t)255) + kQueueBytes;
 }
 
 static int decode_impl(const void *q, const void *k, const void *v, void *out, const int *seq_lens, int B,
@@ -620,6 +628,8 @@ static int decode_impl(const void *q, const void *k, const void *v, void *out, c
         if (Dk <= 128 && S >= 3) {
             // flat decode (balanced over all sequences); S bounds the pieces per stream
             a.n_wg = gqa::decode_bf16_flat_workgroups(Dk);
+            a.n_first = gqa::decode_bf16_flat_first_round(Dk);
+            a.queue = (unsigned *)((char *)workspace + need - kQueueBytes);
         }
         a.c = folded_scale(scale);
         if (dry_run) return GQA_OK;

@@ -33,7 +33,10 @@ __global__ __launch_bounds__(kCT) void combine_kernel(CombineArgs p)
 {
     using PT = float;
     using PT4 = f32x4;
-    const size_t row = blockIdx.x;  // b * Hq + head
+    // row b * Hq + head, last row first: the flat decode cuts the streams at
+    // the end of its tile order into the most pieces, so the rows that need
+    // more than one batch of partial loads start first
+    const size_t row = (size_t)gridDim.x - 1 - blockIdx.x;
     const float *lse = p.part_lse + row * p.S;
     const PT *po = (const PT *)p.part_o + row * (size_t)p.S * p.Dv;
     const int ns = p.S;
@@ -65,14 +68,22 @@ __global__ __launch_bounds__(kCT) void combine_kernel(CombineArgs p)
     PT4 v[kCB];
     load_batch(v, 0, 0, min(64, ns));  // in flight together with the lse load
     float L = ll;
-    for (int s0 = 64; s0 < ns; s0 += 64) L = fmaxf(L, s0 + lane < ns ? lse[s0 + lane] : -INFINITY);
+    // slots past the last non-empty one weigh nothing: no batch is loaded
+    // for them (a split count above what a row uses costs no round trip)
+    int used = 0;
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+        const float x = s0 == 0 ? ll : (s0 + lane < ns ? lse[s0 + lane] : -INFINITY);
+        L = fmaxf(L, x);
+        const unsigned long long nz = __ballot(!(x == -INFINITY));
+        if (nz) used = s0 + 64 - __builtin_clzll(nz);
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) L = fmaxf(L, __shfl_xor(L, o));
     if (L != -INFINITY) {
-        for (int s0 = 0; s0 < ns; s0 += 64) {
+        for (int s0 = 0; s0 < used; s0 += 64) {
             if (s0 > 0) ll = s0 + lane < ns ? lse[s0 + lane] : -INFINITY;
             const float wl = __builtin_amdgcn_exp2f(ll - L);  // 0 for lse = -inf
-            const int n = min(64, ns - s0);
+            const int n = min(64, used - s0);
             for (int sb = 0; sb < n; sb += kCB) {
                 if (s0 > 0 || sb > 0) load_batch(v, s0, sb, n);
                 add_batch(v, sb, n, wl);

@@ -49,6 +49,17 @@ namespace gqa {
 namespace {
 
 constexpr int kTK = 32;  // keys per tile
+#ifndef GQA_DEC_LAST_PCT
+#define GQA_DEC_LAST_PCT 10
+#endif
+constexpr long long kLastPct = GQA_DEC_LAST_PCT;  // share of the key tiles left to the pieces after the first round
+#ifndef GQA_DEC_QUEUE_MIN_TILES
+#define GQA_DEC_QUEUE_MIN_TILES 48
+#endif
+// the piece queue is used when the first round holds at least this many key
+// tiles per workgroup (shorter decodes lose more to a ticket per piece than
+// their tail costs: at 32 the ragged decode of 32 sequences was 3 us slower)
+constexpr long long kQueueMinTiles = GQA_DEC_QUEUE_MIN_TILES;
 #ifndef GQA_DEC_STAGES
 #define GQA_DEC_STAGES 2  // K/V ring depth for the 128-dim kernel
 #endif
@@ -375,13 +386,37 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
     long long ne = T * S2 / ((nmax > 2 ? nmax - 2 : 0) + S2);
     ne = ne < 1 ? 1 : (ne > p.n_wg ? p.n_wg : ne);
     const long long N = ne;
-    const long long wi = blockIdx.x;
-    if (wi >= N) return;
-    const long long lo = wi * T / N, hi_t = (wi + 1) * T / N;
-    if (lo >= hi_t) return;
-    auto wg_of = [&](long long t) {  // workgroup whose range holds tile t
-        long long x = t * N / T;
-        while (x + 1 < N && (x + 1) * T / N <= t) ++x;
+    if ((long long)blockIdx.x >= N) return;
+    // Piece sizes.  Every piece holds at least floor(T / N) >= m tiles,
+    // m = floor((nmax - 2) / (S - 1)) + 1, and a stream of n tiles meets at
+    // most floor((n - 2) / m) + 2 <= S pieces.  Equal pieces, one per
+    // workgroup, unless the work is long enough for the queue: then the
+    // first round (nl pieces, one per resident workgroup) takes the large
+    // share and the pieces after it only ~kLastPct % of the tiles (never
+    // below m tiles each), handed out through a device-wide counter
+    // (below), so that compute units, and whole XCDs, that stream faster
+    // take more of the small pieces and all of them finish closer together.
+    // (The dispatcher alone cannot do this: it deals workgroups to the XCDs
+    // round-robin, so every XCD gets the same share of the pieces.)
+    const long long nl = p.n_first;
+    const bool queue = p.queue && nl > 0 && N > nl && T >= nl * kQueueMinTiles;
+    long long n1 = N, T1 = T;  // equal pieces: one region
+    if (queue) {
+        const long long m = (nmax > 2 ? (nmax - 2) / (p.S - 1) : 0) + 1;
+        const long long n2 = N - nl;
+        long long ts = (T * kLastPct + 99) / 100;
+        if (ts < n2 * m) ts = n2 * m;
+        if (ts * N <= T * n2) {  // small pieces no larger than equal ones
+            n1 = nl;
+            T1 = T - ts;
+        }
+    }
+    auto bnd = [&](long long w) {  // first tile of piece w (w <= N)
+        return w <= n1 ? w * T1 / n1 : T1 + (w - n1) * (T - T1) / (N - n1);
+    };
+    auto wg_of = [&](long long t) {  // piece whose range holds tile t
+        long long x = t < T1 ? t * n1 / T1 : n1 + (t - T1) * (N - n1) / (T - T1);
+        while (x + 1 < N && bnd(x + 1) <= t) ++x;
         return x;
     };
 
@@ -557,195 +592,218 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
     const int v8_h = vi & 1, v8_g1 = vg & 1;
     const float c = p.c;
 
-    const int ntl = (int)(hi_t - lo);  // tiles of this workgroup
-    Cur dc = locate(lo);               // copy cursor (runs STAGES-1 tiles ahead)
-    Cur cc = dc;                       // compute cursor
+    // The queue: workgroup i < nl takes first-round piece i and ends; the
+    // dispatcher then starts the later workgroups of each XCD as its slots
+    // free, and each of them takes piece nl + t for every ticket t it draws
+    // from the counter until the tickets run out.  Workgroup 0 zeroes the
+    // counter as it starts, before any slot frees, and itself draws after
+    // its first piece until the tickets run out, so every piece is computed
+    // whenever the others start.  A draw that still read the previous
+    // call's value takes a piece past the end (none) or one that is drawn
+    // again after the reset: the two compute the same values into the same
+    // slots.
+    if (queue && blockIdx.x == 0 && lane == 0)
+        __hip_atomic_store(p.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool draws = queue && (blockIdx.x == 0 || (long long)blockIdx.x >= nl);
+    auto draw = [&]() -> long long {
+        unsigned t = 0;
+        if (lane == 0) t = __hip_atomic_fetch_add(p.queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return nl + (long long)__builtin_amdgcn_readfirstlane(t);
+    };
+    const long long first = (queue && (long long)blockIdx.x >= nl) ? draw() : (long long)blockIdx.x;
+    for (long long wi = first; wi < N; wi = draws ? draw() : N) {
+        const long long lo = bnd(wi), hi_t = bnd(wi + 1);
+        if (lo >= hi_t) continue;
+        const int ntl = (int)(hi_t - lo);  // tiles of this piece
+        Cur dc = locate(lo);               // copy cursor (runs STAGES-1 tiles ahead)
+        Cur cc = dc;                       // compute cursor
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (s < ntl) {
-            issue_tile(dc, s);
-            advance(dc);
-        }
-
-    u32x4 qreg[KS];
-    f32x16 o[DT];
-    float m_run = -INFINITY, l_run = 0.f;
-    bool head_ok = false;
-    int head = 0;
-    for (int it = 0; it < ntl; ++it) {
-        const int slot = it % STAGES;
-        if (it + STAGES - 2 < ntl)
-            wait_vmem_le<(STAGES - 2) * NI>();  // tile `it` landed, later ones may fly
-        else
-            wait_vmem();
-        lds_barrier();  // this wave's reads of the slot being refilled are complete
-        if (it + STAGES - 1 < ntl) {
-            issue_tile(dc, (it + STAGES - 1) % STAGES);
-            advance(dc);
-        }
-
-        const int kvh = cc.s / p.n_hblk, hblk = cc.s % p.n_hblk;
-        if (it == 0 || cc.u == 0) {
-            // a new stream piece: its queries, fresh accumulators
-            const int hh = hblk * 32 + col;
-            head_ok = hh < p.G;
-            head = kvh * p.G + (head_ok ? hh : 0);
-            const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)cc.b * p.Hq + head) * DK;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                u32x4 z = {0u, 0u, 0u, 0u};
-                qreg[ks] = head_ok ? *(const u32x4 *)(qrow + 16 * ks + 8 * hi) : z;
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < ntl) {
+                issue_tile(dc, s);
+                advance(dc);
             }
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) hold_reg(qreg[ks]);
-#pragma unroll
-            for (int i = 0; i < DT; ++i)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
-            m_run = -INFINITY;
-            l_run = 0.f;
-        }
-        const int kend = cc.len;
-        const int k0 = cc.u * kTK;
 
-        // element e of the score accumulator is key acc_key(0, e, hi): keys
-        // 8 hi + 0..7 and 16 + 8 hi + 0..7 of the tile
-        auto row_scales = [&](int base, float (&dst)[16]) {
+        u32x4 qreg[KS];
+        f32x16 o[DT];
+        float m_run = -INFINITY, l_run = 0.f;
+        bool head_ok = false;
+        int head = 0;
+        for (int it = 0; it < ntl; ++it) {
+            const int slot = it % STAGES;
+            if (it + STAGES - 2 < ntl)
+                wait_vmem_le<(STAGES - 2) * NI>();  // tile `it` landed, later ones may fly
+            else
+                wait_vmem();
+            lds_barrier();  // this wave's reads of the slot being refilled are complete
+            if (it + STAGES - 1 < ntl) {
+                issue_tile(dc, (it + STAGES - 1) % STAGES);
+                advance(dc);
+            }
+
+            const int kvh = cc.s / p.n_hblk, hblk = cc.s % p.n_hblk;
+            if (it == 0 || cc.u == 0) {
+                // a new stream piece: its queries, fresh accumulators
+                const int hh = hblk * 32 + col;
+                head_ok = hh < p.G;
+                head = kvh * p.G + (head_ok ? hh : 0);
+                const uint16_t *qrow = (const uint16_t *)p.q + ((size_t)cc.b * p.Hq + head) * DK;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    u32x4 z = {0u, 0u, 0u, 0u};
+                    qreg[ks] = head_ok ? *(const u32x4 *)(qrow + 16 * ks + 8 * hi) : z;
+                }
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) hold_reg(qreg[ks]);
+#pragma unroll
+                for (int i = 0; i < DT; ++i)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) o[i][e] = 0.f;
+                m_run = -INFINITY;
+                l_run = 0.f;
+            }
+            const int kend = cc.len;
+            const int k0 = cc.u * kTK;
+
+            // element e of the score accumulator is key acc_key(0, e, hi): keys
+            // 8 hi + 0..7 and 16 + 8 hi + 0..7 of the tile
+            auto row_scales = [&](int base, float (&dst)[16]) {
+                if constexpr (F8) {
+                    const float *sc = &sm.sc[slot][base];
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) dst[e] = sc[acc_key(0, e, hi)];
+                }
+            };
+
+            f32x16 s;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) s[e] = 0.f;
             if constexpr (F8) {
-                const float *sc = &sm.sc[slot][base];
+                // K operand: lane (col, hi) takes dims 16 ks + 8 hi .. + 7 of key
+                // row krow: 8 codes of chunk ks, stored at position ks ^ sw(krow)
+                const char *kq_ = (const char *)sm.kq[slot];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) dst[e] = sc[acc_key(0, e, hi)];
-            }
-        };
-
-        f32x16 s;
+                for (int ks = 0; ks < KS; ++ks) {
+                    const u32x2 c8 = *(const u32x2 *)(kq_ + k8_base + ((ks ^ k8_sw) << 4));
+                    s = mfma32x32x16(e4m3x8_to_bf16(c8), qreg[ks], s);
+                }
+            } else {
+                const char *ks_ = (const char *)sm.k[slot];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = 0.f;
-        if constexpr (F8) {
-            // K operand: lane (col, hi) takes dims 16 ks + 8 hi .. + 7 of key
-            // row krow: 8 codes of chunk ks, stored at position ks ^ sw(krow)
-            const char *kq_ = (const char *)sm.kq[slot];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const u32x2 c8 = *(const u32x2 *)(kq_ + k8_base + ((ks ^ k8_sw) << 4));
-                s = mfma32x32x16(e4m3x8_to_bf16(c8), qreg[ks], s);
-            }
-        } else {
-            const char *ks_ = (const char *)sm.k[slot];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int off_ = ((ks & 1) ? kbase_odd : kbase_even) + (ks >> 1) * Tile::PLANE_BYTES;
-                s = mfma32x32x16(*(const u32x4 *)(ks_ + off_), qreg[ks], s);
-            }
-        }
-        if constexpr (F8) {
-            float ksc[16];  // the keys' row scales
-            row_scales(0, ksc);
-#pragma unroll
-            for (int e = 0; e < 16; ++e) s[e] *= ksc[e];
-        }
-        if (k0 + kTK > kend) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                if (k0 + acc_key(0, e, hi) >= kend) s[e] = -INFINITY;
-        }
-        float mx = s[0];
-#pragma unroll
-        for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
-        mx = halves_max(mx);
-        const float mt = mx * c;
-        if (__any(mt > m_run + 8.0f)) {
-            const float m_new = (mt > m_run + 8.0f) ? mt : m_run;
-            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int i = 0; i < DT; ++i)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
-        }
-        const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
-        float vsc[16];  // F8: the values' row scales
-        if constexpr (F8) row_scales(kTK, vsc);
-        u32x4 pb[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float pv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e)
-                pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h + e], c, -m_use));
-            if constexpr (F8) {
-                // value scales ride on the weights; the normaliser takes the
-                // unscaled ones
-#pragma unroll
-                for (int e = 0; e < 8; ++e) l_run += pv[e];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) pv[e] *= vsc[8 * h + e];
-            }
-            pb[h].x = pack_bf16x2(pv[0], pv[1]);
-            pb[h].y = pack_bf16x2(pv[2], pv[3]);
-            pb[h].z = pack_bf16x2(pv[4], pv[5]);
-            pb[h].w = pack_bf16x2(pv[6], pv[7]);
-            if constexpr (!F8) l_run = sum_bf16x8(pb[h], l_run);
-        }
-        if constexpr (F8) {
-            // V^T operand of step st, dims 32 dt ..: in 16-lane group g, lane
-            // 2 r + h points at key row 16 st + 8 (g >> 1) + r, dims
-            // 32 dt + 16 (g & 1) + 8 h .. + 7 (chunk 2 dt + (g & 1), half h);
-            // lane i then holds dim 32 dt + 16 (g & 1) + i of keys
-            // 16 st + 8 (g >> 1) + 0..7, the keys of its P^T slice
-            const char *vq_ = (const char *)sm.vq[slot];
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                const int row = 16 * st + v8_row;
-                const int sw = (row >> 1) & (CPRV - 1);
-                const char *rp = vq_ + row * DV + 8 * v8_h;
-#pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const u32x2 c8 = lds_read_tr8(rp + (((2 * dt + v8_g1) ^ sw) << 4));
-                    o[dt] = mfma32x32x16(e4m3x8_to_bf16(c8), pb[st], o[dt]);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int off_ = ((ks & 1) ? kbase_odd : kbase_even) + (ks >> 1) * Tile::PLANE_BYTES;
+                    s = mfma32x32x16(*(const u32x4 *)(ks_ + off_), qreg[ks], s);
                 }
             }
-        } else {
-            const char *vs_ = (const char *)sm.v[slot];
+            if constexpr (F8) {
+                float ksc[16];  // the keys' row scales
+                row_scales(0, ksc);
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
+                for (int e = 0; e < 16; ++e) s[e] *= ksc[e];
+            }
+            if (k0 + kTK > kend) {
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt) {
-                    const int o_ = dt * Tile::PLANE_BYTES + 16 * st * 64;
-                    const u32x2 lo2 = lds_read_tr16(vs_ + vb_h0 + o_);
-                    const u32x2 hv = lds_read_tr16(vs_ + vb_h1 + o_);
-                    u32x4 va = {lo2.x, lo2.y, hv.x, hv.y};
-                    o[dt] = mfma32x32x16(va, pb[st], o[dt]);
+                for (int e = 0; e < 16; ++e)
+                    if (k0 + acc_key(0, e, hi) >= kend) s[e] = -INFINITY;
+            }
+            float mx = s[0];
+#pragma unroll
+            for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+            mx = halves_max(mx);
+            const float mt = mx * c;
+            if (__any(mt > m_run + 8.0f)) {
+                const float m_new = (mt > m_run + 8.0f) ? mt : m_run;
+                const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int i = 0; i < DT; ++i)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) o[i][e] *= alpha;
+            }
+            const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+            float vsc[16];  // F8: the values' row scales
+            if constexpr (F8) row_scales(kTK, vsc);
+            u32x4 pb[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float pv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pv[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * h + e], c, -m_use));
+                if constexpr (F8) {
+                    // value scales ride on the weights; the normaliser takes the
+                    // unscaled ones
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) l_run += pv[e];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pv[e] *= vsc[8 * h + e];
+                }
+                pb[h].x = pack_bf16x2(pv[0], pv[1]);
+                pb[h].y = pack_bf16x2(pv[2], pv[3]);
+                pb[h].z = pack_bf16x2(pv[4], pv[5]);
+                pb[h].w = pack_bf16x2(pv[6], pv[7]);
+                if constexpr (!F8) l_run = sum_bf16x8(pb[h], l_run);
+            }
+            if constexpr (F8) {
+                // V^T operand of step st, dims 32 dt ..: in 16-lane group g, lane
+                // 2 r + h points at key row 16 st + 8 (g >> 1) + r, dims
+                // 32 dt + 16 (g & 1) + 8 h .. + 7 (chunk 2 dt + (g & 1), half h);
+                // lane i then holds dim 32 dt + 16 (g & 1) + i of keys
+                // 16 st + 8 (g >> 1) + 0..7, the keys of its P^T slice
+                const char *vq_ = (const char *)sm.vq[slot];
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+                    const int row = 16 * st + v8_row;
+                    const int sw = (row >> 1) & (CPRV - 1);
+                    const char *rp = vq_ + row * DV + 8 * v8_h;
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const u32x2 c8 = lds_read_tr8(rp + (((2 * dt + v8_g1) ^ sw) << 4));
+                        o[dt] = mfma32x32x16(e4m3x8_to_bf16(c8), pb[st], o[dt]);
+                    }
+                }
+            } else {
+                const char *vs_ = (const char *)sm.v[slot];
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+#pragma unroll
+                    for (int dt = 0; dt < DT; ++dt) {
+                        const int o_ = dt * Tile::PLANE_BYTES + 16 * st * 64;
+                        const u32x2 lo2 = lds_read_tr16(vs_ + vb_h0 + o_);
+                        const u32x2 hv = lds_read_tr16(vs_ + vb_h1 + o_);
+                        u32x4 va = {lo2.x, lo2.y, hv.x, hv.y};
+                        o[dt] = mfma32x32x16(va, pb[st], o[dt]);
+                    }
                 }
             }
-        }
 
-        if (cc.u == cc.n - 1 || it == ntl - 1) {
-            // end of this workgroup's piece of the stream: write its partial
-            const long long pw = cc.base + (long long)cc.s * cc.n;  // the stream's first tile
-            const long long first = wg_of(pw);
-            const int j = (int)(wi - first);
-            if (head_ok) {
-                const float l_tot = halves_sum(l_run);
-                const size_t prow = ((size_t)cc.b * p.Hq + head) * p.S + j;
-                const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+            if (cc.u == cc.n - 1 || it == ntl - 1) {
+                // end of this workgroup's piece of the stream: write its partial
+                const long long pw = cc.base + (long long)cc.s * cc.n;  // the stream's first tile
+                const long long first = wg_of(pw);
+                const int j = (int)(wi - first);
+                if (head_ok) {
+                    const float l_tot = halves_sum(l_run);
+                    const size_t prow = ((size_t)cc.b * p.Hq + head) * p.S + j;
+                    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
-                for (int dt = 0; dt < DT; ++dt)
+                    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-                    for (int jj = 0; jj < 4; ++jj)
-                        store_partial4(p.part_o, prow * DV + 32 * dt + 8 * jj + 4 * hi, o[dt][4 * jj] * inv,
-                                       o[dt][4 * jj + 1] * inv, o[dt][4 * jj + 2] * inv, o[dt][4 * jj + 3] * inv);
-                if (hi == 0) p.part_lse[prow] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
+                        for (int jj = 0; jj < 4; ++jj)
+                            store_partial4(p.part_o, prow * DV + 32 * dt + 8 * jj + 4 * hi, o[dt][4 * jj] * inv,
+                                           o[dt][4 * jj + 1] * inv, o[dt][4 * jj + 2] * inv, o[dt][4 * jj + 3] * inv);
+                    if (hi == 0) p.part_lse[prow] = l_tot > 0.f ? m_run + __log2f(l_tot) : -INFINITY;
+                }
+                if (j == 0 && head_ok && hi == 0) {
+                    // slots past the stream's last piece are empty for the combine
+                    const int count = (int)(wg_of(pw + cc.n - 1) - wi + 1);
+                    const size_t prow0 = ((size_t)cc.b * p.Hq + head) * p.S;
+                    for (int q = count; q < p.S; ++q) p.part_lse[prow0 + q] = -INFINITY;
+                }
             }
-            if (j == 0 && head_ok && hi == 0) {
-                // slots past the stream's last piece are empty for the combine
-                const int count = (int)(wg_of(pw + cc.n - 1) - wi + 1);
-                const size_t prow0 = ((size_t)cc.b * p.Hq + head) * p.S;
-                for (int q = count; q < p.S; ++q) p.part_lse[prow0 + q] = -INFINITY;
-            }
+            advance(cc);
         }
-        advance(cc);
     }
 }
 
@@ -780,6 +838,17 @@ int decode_bf16_flat_workgroups(int Dk)
 #define GQA_DEC_WG_PER_CU 8
 #endif
     return GQA_DEC_WG_PER_CU * 256;
+}
+
+int decode_bf16_flat_first_round(int Dk)
+{
+    // Per-workgroup clocks show four of these one-wave workgroups resident
+    // per compute unit at a time (1024 on the chip).
+    (void)Dk;
+#ifndef GQA_DEC_FIRST_PER_CU
+#define GQA_DEC_FIRST_PER_CU 4
+#endif
+    return GQA_DEC_FIRST_PER_CU * 256;
 }
 
 // FP8 flat decode: one resident round of workgroups.  At 16.5 KiB of LDS

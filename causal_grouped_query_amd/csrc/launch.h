@@ -74,6 +74,10 @@ struct DecodeArgs {
     int n_hblk;          // head blocks per KV head
     float c;             // scale * log2(e)
     int n_wg;            // > 0: balanced (flat) schedule with this many workgroups
+    int n_first;         // flat schedule: workgroups resident at once (the first
+                         // round); with `queue` set, long decodes hand the pieces
+                         // past the first round out through the counter
+    unsigned *queue;     // piece counter in the workspace (reset by workgroup 0)
     // top-k sparse decode (absorbed MLA): idx [B, topk] int32 cache positions;
     // the key axis of the split is the index list, entries outside
     // [0, lens[b]) select nothing
@@ -99,8 +103,10 @@ int launch_mla_decode_topk(const DecodeArgs &a, hipStream_t stream);
 int mla_topk_max_chunk();
 int mla_heads_per_block();
 int decode_bf16_key_tile();
-// Flat (persistent, balanced) decode for Dk = Dv <= 128: workgroups to launch.
+// Flat (balanced) decode for Dk = Dv <= 128: workgroups to launch, and how
+// many of them are resident at once (the first round).
 int decode_bf16_flat_workgroups(int Dk);
+int decode_bf16_flat_first_round(int Dk);
 int decode_fp8_flat_workgroups(int Dk);
 int decode_bf16_heads_per_block(int Dk, int G);
 

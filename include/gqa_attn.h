@@ -195,7 +195,9 @@ int gqa_attn_decode_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int Dv, gqa
 /*
  * Bytes of device workspace gqa_attn_decode needs for num_splits splits
  * (num_splits >= 1): fp32 partial outputs [B, Hq, S, Dv] followed by fp32
- * partial log-sum-exp values [B, Hq, S].  Returns 0 for invalid arguments.
+ * partial log-sum-exp values [B, Hq, S], rounded up to 256 bytes, and a
+ * 256-byte region for the balanced schedule's piece counter (the kernel
+ * zeroes it itself).  Returns 0 for invalid arguments.
  */
 size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_splits);
 
@@ -226,8 +228,10 @@ size_t gqa_attn_decode_workspace_size(int B, int Hq, int Dv, int num_splits);
  *   num_splits  number of key-axis splits, 1 .. 1024, or 0 for the value of
  *            gqa_attn_decode_splits().  For bf16 with Dk = Dv <= 128 and
  *            num_splits >= 3 the work is balanced over all sequences instead
- *            (the key tiles of all sequences are shared out evenly over the
- *            workgroups) and num_splits bounds how many pieces one
+ *            (the key tiles of all sequences are shared out over the
+ *            workgroups; on long decodes the last ~10 % in smaller pieces
+ *            that workgroups take at run time through a counter in the
+ *            workspace) and num_splits bounds how many pieces one
  *            sequence's keys may be cut into; otherwise each sequence's keys
  *            are cut into num_splits equal chunks.  The result is the same
  *            attention either way (exact log-sum-exp merge).
@@ -359,15 +363,18 @@ int gqa_attn_decode_window(const void *q, const void *k, const void *v, void *ou
  * A shape needs gqa_attn_decode_noalloc_scratch_bytes(B, Hq, Dv, S, dtype)
  * bytes of it for S splits (num_splits, or gqa_attn_decode_splits() when 0):
  * B*Hq*S fp32 partial outputs of Dv values plus B*Hq*S fp32 log-sum-exp
- * values.  A shape that needs more returns GQA_ERR_WORKSPACE with nothing
- * enqueued (e.g. B = 64, Hq = 32, Dv = 128, S = 10 needs 10.6 MB; the
- * absorbed-MLA B = 16, Hq = 128, Dv = 512, S = 16 needs 67.2 MB).
+ * values (at the next 256-byte boundary), rounded up to 256 bytes, plus 256
+ * bytes for the piece counter.  A shape that needs more returns
+ * GQA_ERR_WORKSPACE with nothing enqueued (e.g. B = 64, Hq = 32, Dv = 128,
+ * S = 32 needs 33.8 MB; the absorbed-MLA B = 16, Hq = 128, Dv = 512,
+ * S = 16 needs 67.2 MB).
  *
  * Calls on one GPU share its array: calls that overlap in time on that GPU
  * (different streams, or other processes' threads sharing this library
  * instance) race and corrupt each other's partials; order them on one
  * stream.  The array keeps the last call's contents; nothing in it needs to
- * start zeroed (every slot a call's combine reads is written by that call).
+ * start zeroed (every slot a call's combine reads is written by that call,
+ * and the piece counter is zeroed by the call's own partial kernel).
  */
 #define GQA_DECODE_NOALLOC_MAX_SCRATCH (96u << 20)
 size_t gqa_attn_decode_noalloc_scratch_bytes(int B, int Hq, int Dv, int num_splits, gqa_dtype dtype);

@@ -99,7 +99,8 @@ int main()
                           nullptr) == GQA_OK,
           "decode ok");
     CHECK(g_stub.launches == before + 2, "decode: partial kernel + combine");
-    CHECK(g_stub.dec.S == S && g_stub.dec.n_wg == 2048, "decode flat schedule");
+    CHECK(g_stub.dec.S == S && g_stub.dec.n_wg == 2048 && g_stub.dec.n_first == 1024, "decode flat schedule");
+    CHECK((char *)g_stub.dec.queue == W + ws - 256, "decode piece counter at the workspace end");
     CHECK((char *)g_stub.dec.part_o == W && (char *)g_stub.dec.part_lse == W + (size_t)B * Hq * S * D * 4,
           "decode workspace layout");
     CHECK(g_stub.comb.part_o == g_stub.dec.part_o && g_stub.comb.S == S && g_stub.comb.out_bf16 == 1, "combine args");
@@ -154,7 +155,8 @@ int main()
                                    64LL * 576, 64LL * 576, 576, 0.07f, 16, GQA_BF16, nullptr), GQA_ERR_WORKSPACE);
     REJECT(gqa_attn_decode_noalloc(nullptr, P, P, P, IP, B, Hq, Hkv, T, D, D, sb, sh, st, sb, sh, st, 0.088f, 0,
                                    GQA_BF16, nullptr), GQA_ERR_INVALID_ARG);
-    CHECK(gqa_attn_decode_noalloc_scratch_bytes(B, Hq, D, S, GQA_BF16) == lse_off + (size_t)B * Hq * S * 4,
+    CHECK(gqa_attn_decode_noalloc_scratch_bytes(B, Hq, D, S, GQA_BF16) ==
+              ((lse_off + (size_t)B * Hq * S * 4 + 255) & ~(size_t)255) + 256,
           "noalloc scratch size");
 
     if (failures) fprintf(stderr, "%d check(s) failed\n", failures);

@@ -42,6 +42,7 @@ int mla_topk_max_chunk() { return 4096; }
 int mla_heads_per_block() { return 128; }
 int decode_bf16_key_tile() { return 32; }
 int decode_bf16_flat_workgroups(int) { return 2048; }
+int decode_bf16_flat_first_round(int) { return 1024; }
 int decode_fp8_flat_workgroups(int) { return 2048; }
 int decode_bf16_heads_per_block(int Dk, int) { return Dk == 576 ? 128 : 32; }
 int launch_fwd_f32(const F32FwdArgs &, int, hipStream_t)

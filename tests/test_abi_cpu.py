@@ -127,7 +127,7 @@ def test_workspace_size_and_splits():
     assert gqa.decode_workspace_size(2, 4, 128, 0) == 0
     assert gqa.decode_workspace_size(2, 4, 128, 1025) == 0
     n = gqa.decode_workspace_size(64, 32, 128, 16)
-    assert n >= 64 * 32 * 16 * 129 * 4 and n % 256 == 0
+    assert n == 64 * 32 * 16 * 129 * 4 + 256  # partials, lse, the piece counter's 256 bytes
     # the split choice depends only on the shape
     s = gqa.decode_splits(64, 32, 8, 8192, 128, 128, BF16)
     assert 1 <= s <= 1024 and s == gqa.decode_splits(64, 32, 8, 8192, 128, 128, BF16)
@@ -265,13 +265,17 @@ def test_decode_noalloc_rejects_on_host():
 
 
 def test_decode_noalloc_scratch_sizes():
-    # fp32 partials, then the fp32 lse at the next 256-byte boundary
+    # fp32 partials, then the fp32 lse at the next 256-byte boundary, rounded
+    # up to 256 bytes, then 256 bytes for the piece counter
     rows = 64 * 32 * 10
-    assert gqa.decode_noalloc_scratch_bytes(64, 32, 128, 10, BF16) == rows * 128 * 4 + rows * 4
+    assert gqa.decode_noalloc_scratch_bytes(64, 32, 128, 10, BF16) == rows * 128 * 4 + rows * 4 + 256
     rows = 16 * 128 * 16
-    assert gqa.decode_noalloc_scratch_bytes(16, 128, 512, 16, BF16) == rows * 512 * 4 + rows * 4
+    assert gqa.decode_noalloc_scratch_bytes(16, 128, 512, 16, BF16) == rows * 512 * 4 + rows * 4 + 256
     assert gqa.decode_noalloc_scratch_bytes(16, 128, 512, 16, BF16) <= 96 << 20  # the absorbed-MLA workload fits
-    assert gqa.decode_noalloc_scratch_bytes(1, 1, 3, 1, F32) == 256 + 4
+    # the GQA decode at its default split count fits too
+    s = gqa.decode_splits(64, 32, 8, 8192, 128, 128, BF16)
+    assert gqa.decode_noalloc_scratch_bytes(64, 32, 128, s, BF16) <= 96 << 20
+    assert gqa.decode_noalloc_scratch_bytes(1, 1, 3, 1, F32) == 512 + 256
     assert gqa.decode_noalloc_scratch_bytes(0, 32, 128, 10, BF16) == 0
     assert gqa.decode_noalloc_scratch_bytes(1, 32, 128, 10, 9) == 0
 
