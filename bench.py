@@ -146,7 +146,7 @@ def _profile_call(torch, gqa, W, dev, name):
         lens_l = lens.tolist()
         q, kc, vc, ks, vs, lens = (t.to(dev) for t in (q, kc, vc, ks, vs, lens))
         out = torch.empty((w.B, w.Hq, 1, w.Dv), dtype=torch.bfloat16, device=dev)
-        S = gqa.decode_splits(w.B, w.Hq, w.Hkv, w.Tk, w.Dk, w.Dv, gqa.GQA_BF16)
+        S = gqa.decode_fp8_splits(w.B, w.Hq, w.Hkv, w.Tk, w.Dk, w.Dv)
         ws = torch.empty(gqa.decode_workspace_size(w.B, w.Hq, w.Dv, S), dtype=torch.uint8, device=dev)
         return (lambda: gqa.decode_fp8(q, kc, vc, ks, vs, lens, scale=w.scale, num_splits=S, out=out,
                                        workspace=ws)), {"workload": w.name,
@@ -587,7 +587,7 @@ def extra_workloads(torch, gqa, W, dev):
     q, kc, vc, ks, vs, lens = W.fp8_decode_inputs(w, nan_tail=False)
     q, kc, vc, ks, vs, lens_d = (t.to(dev) for t in (q, kc, vc, ks, vs, lens))
     out = torch.empty((w.B, w.Hq, 1, w.Dv), dtype=torch.bfloat16, device=dev)
-    S = gqa.decode_splits(w.B, w.Hq, w.Hkv, w.Tk, w.Dk, w.Dv, gqa.GQA_BF16)
+    S = gqa.decode_fp8_splits(w.B, w.Hq, w.Hkv, w.Tk, w.Dk, w.Dv)
     ws = torch.empty(gqa.decode_workspace_size(w.B, w.Hq, w.Dv, S), dtype=torch.uint8, device=dev)
     sec = _time(torch, lambda: gqa.decode_fp8(q, kc, vc, ks, vs, lens_d, scale=w.scale, num_splits=S, out=out,
                                               workspace=ws))

@@ -28,7 +28,7 @@ import os
 __all__ = [
     "LIB_PATH", "GQA_BF16", "GQA_F32", "GQAError", "lib", "attention", "attention_varlen", "check_cu_seqlens",
     "decode",
-    "decode_splits", "decode_workspace_size", "decode_noalloc", "decode_noalloc_scratch_bytes", "decode_topk", "decode_topk_splits", "check_topk_distinct", "decode_fp8", "attention_shard", "merge", "strerror",
+    "decode_splits", "decode_workspace_size", "decode_noalloc", "decode_noalloc_scratch_bytes", "decode_topk", "decode_topk_splits", "check_topk_distinct", "decode_fp8", "decode_fp8_splits", "attention_shard", "merge", "strerror",
 ]
 
 # The library to load: the in-tree build, or another build of it (e.g. the
@@ -39,7 +39,7 @@ GQA_OK, GQA_ERR_INVALID_ARG, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP
 
 EXPORTS = ("gqa_attn_fwd", "gqa_attn_fwd_varlen", "gqa_attn_decode", "gqa_attn_decode_splits",
            "gqa_attn_decode_workspace_size", "gqa_attn_decode_topk", "gqa_attn_decode_topk_splits",
-           "gqa_attn_decode_fp8", "gqa_attn_fwd_shard", "gqa_attn_merge", "gqa_attn_decode_window",
+           "gqa_attn_decode_fp8", "gqa_attn_decode_fp8_splits", "gqa_attn_fwd_shard", "gqa_attn_merge", "gqa_attn_decode_window",
            "gqa_attn_decode_noalloc", "gqa_attn_decode_noalloc_scratch_bytes", "gqa_attn_strerror")
 
 _lib = None
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
         L.gqa_attn_decode_topk.restype = I
         L.gqa_attn_decode_topk.argtypes = [P, P, P, P, P, I, I, I, I, I, I, LL, LL, F, I, P, SZ, I, P]
         L.gqa_attn_decode_fp8.restype = I
+        L.gqa_attn_decode_fp8_splits.restype = I
+        L.gqa_attn_decode_fp8_splits.argtypes = [I, I, I, I, I, I]
         L.gqa_attn_decode_fp8.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I] + [LL] * 12 + [F, I, I, P, SZ, P]
         L.gqa_attn_decode_window.restype = I
         L.gqa_attn_decode_window.argtypes = [P, P, P, P, P, I, I, I, I, I, I, LL, LL, LL, LL, LL, LL, F, I, I, P,
@@ -340,6 +342,15 @@ def decode_noalloc_scratch_bytes(B: int, Hq: int, Dv: int, num_splits: int, dtyp
     return int(lib().gqa_attn_decode_noalloc_scratch_bytes(B, Hq, Dv, num_splits, dtype_code))
 
 
+def decode_fp8_splits(B: int, Hq: int, Hkv: int, Tmax: int, Dk: int, Dv: int) -> int:
+    """Split count decode_fp8 uses with num_splits = 0 (never above
+    decode_splits(..., GQA_BF16), so a workspace sized for that fits)."""
+    s = lib().gqa_attn_decode_fp8_splits(B, Hq, Hkv, Tmax, Dk, Dv)
+    if s < 0:
+        raise GQAError(s, "gqa_attn_decode_fp8_splits")
+    return s
+
+
 def decode_topk_splits(B: int, Hq: int, topk: int, Dk: int, Dv: int, dtype_code: int) -> int:
     s = lib().gqa_attn_decode_topk_splits(B, Hq, topk, Dk, Dv, dtype_code)
     if s < 0:
@@ -437,7 +448,7 @@ def decode_fp8(q, k_codes, v_codes, k_scale, v_scale, seq_lens, scale: float | N
         raise ValueError("inconsistent q / code / scale / seq_lens shapes")
     if scale is None:
         scale = 1.0 / math.sqrt(Dk)
-    S = num_splits if num_splits else decode_splits(B, Hq, Hkv, Tmax, Dk, Dv, GQA_BF16)
+    S = num_splits if num_splits else decode_fp8_splits(B, Hq, Hkv, Tmax, Dk, Dv)
     need = decode_workspace_size(B, Hq, Dv, S)
     if need == 0:
         raise GQAError(GQA_ERR_INVALID_ARG, "gqa_attn_decode_workspace_size")

@@ -119,6 +119,24 @@ int default_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int dtype)
     return (int)s;
 }
 
+// FP8 flat decode: one resident round of workgroups and equal pieces (no
+// piece queue), so S only needs to keep the grid full when the lengths are
+// ragged: S - 2 of twice the workgroups per stream (with every sequence
+// full, T = streams * n_max).  Never above the bf16 default, so a workspace
+// sized for that fits.
+int fp8_default_splits(int B, int Hq, int Hkv, int Tmax, int Dk)
+{
+    const long long streams = (long long)B * Hkv * cdiv(Hq / Hkv, 32);
+    const long long wgs = gqa::decode_fp8_flat_workgroups(Dk);
+    long long s = 2 + (2 * wgs + streams - 1) / streams;
+    const long long cap = 2 + cdiv(Tmax, 32);
+    if (s < 8) s = 8;
+    if (s > cap) s = cap;
+    if (s > 64) s = 64;
+    const int bf16 = default_splits(B, Hq, Hkv, Tmax, Dk, GQA_BF16);
+    return (int)(s < 3 ? 3 : (s > bf16 ? bf16 : s));
+}
+
 // workspace: fp32 partial outputs [B, Hq, S, Dv], then fp32 partial
 // log2-sum-exp [B, Hq, S], then (at the next 256-byte boundary) 256 bytes
 // for the flat decode's piece counter
@@ -353,6 +371,15 @@ GQA_API int gqa_attn_decode_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int
     return default_splits(B, Hq, Hkv, Tmax, Dk, dtype);
 }
 
+GQA_API int gqa_attn_decode_fp8_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int Dv)
+{
+    int rc = check_common(B, Hq, Hkv, Dk, Dv, 1.f, GQA_BF16);
+    if (rc != GQA_OK) return rc;
+    if (Tmax <= 0) return GQA_ERR_INVALID_ARG;
+    if (Dk != Dv || (Dk != 64 && Dk != 128)) return GQA_ERR_UNSUPPORTED;
+    return fp8_default_splits(B, Hq, Hkv, Tmax, Dk);
+}
+
 // Top-k sparse decode: splits when the caller leaves the choice to the
 // library.  A workgroup covers 128 heads of one sequence and one slice of the
 // index list; aim at one workgroup per CU (256) with slices of at least 64
@@ -476,7 +503,7 @@ GQA_API int gqa_attn_decode_fp8(const void *q, const void *k, const void *v, con
     // a 32-row tile is addressed with 32-bit byte offsets
     if (k_st > (1LL << 25) || v_st > (1LL << 25)) return GQA_ERR_UNSUPPORTED;
 
-    const int S = num_splits ? num_splits : default_splits(B, Hq, Hkv, Tmax, Dk, GQA_BF16);
+    const int S = num_splits ? num_splits : fp8_default_splits(B, Hq, Hkv, Tmax, Dk);
     const size_t need = ws_bytes(B, Hq, Dv, S);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return GQA_ERR_WORKSPACE;
 

@@ -268,10 +268,10 @@ int gqa_attn_decode(const void *q, const void *k, const void *v, void *out, cons
  *            gqa_attn_decode_workspace_size(B, Hq, Dv, splits) bytes)
  *   window   0, or w >= 1: a sliding window as for gqa_attn_decode_window
  *            (the last min(seq_lens[b], w) rows only)
- *   num_splits  0 (the value of gqa_attn_decode_splits(..., GQA_BF16)) or
- *            3 .. 1024: the bound on the pieces one sequence's keys are cut
- *            into by the balanced schedule; 1 and 2 return
- *            GQA_ERR_INVALID_ARG.
+ *   num_splits  0 (the value of gqa_attn_decode_fp8_splits(), which is never
+ *            above gqa_attn_decode_splits(..., GQA_BF16)) or 3 .. 1024: the
+ *            bound on the pieces one sequence's keys are cut into by the
+ *            balanced schedule; 1 and 2 return GQA_ERR_INVALID_ARG.
  * Rows at t >= seq_lens[b] are never read (codes and scales there may hold
  * anything).  Codes of rows that are read must not be NaN.
  * Supported: Dk = Dv = 64 or 128 (else GQA_ERR_UNSUPPORTED), row strides up
@@ -284,6 +284,16 @@ int gqa_attn_decode_fp8(const void *q, const void *k, const void *v, const float
                         long long ks_sh, long long ks_st, long long vs_sb, long long vs_sh,
                         long long vs_st, float scale, int window, int num_splits, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/*
+ * Split count gqa_attn_decode_fp8 uses when called with num_splits = 0
+ * (shape only, host-only): 3 .. 64 and never above gqa_attn_decode_splits(B,
+ * Hq, Hkv, Tmax, Dk, Dv, GQA_BF16), so a workspace sized for that value
+ * fits; or a negative GQA_ERR_* code.  The FP8 decode runs one resident
+ * round of workgroups with equal pieces, so it needs fewer split slots
+ * than the bf16 decode's balanced schedule.
+ */
+int gqa_attn_decode_fp8_splits(int B, int Hq, int Hkv, int Tmax, int Dk, int Dv);
 
 /*
  * Split count gqa_attn_decode_topk uses when called with num_splits = 0

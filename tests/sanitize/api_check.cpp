@@ -126,6 +126,10 @@ int main()
     CHECK(gqa_attn_decode_fp8(P, P, P, SP, SP, P, IP, B, Hq, Hkv, T, D, D, sb, sh, st, sb, sh, st, Hkv * T, T, 1,
                               Hkv * T, T, 1, 0.088f, 0, 0, W, ws, nullptr) == GQA_OK && g_stub.dec.fp8 == 1,
           "fp8 ok");
+    CHECK(g_stub.dec.S == gqa_attn_decode_fp8_splits(B, Hq, Hkv, T, D, D) && g_stub.dec.S <= S &&
+              g_stub.dec.queue == nullptr,
+          "fp8 default splits, no piece queue");
+    REJECT(gqa_attn_decode_fp8_splits(B, Hq, Hkv, T, 576, 512), GQA_ERR_UNSUPPORTED);
     REJECT(gqa_attn_decode_fp8(P, P, P, SP, SP, P, IP, B, Hq, Hkv, T, D, D, sb, sh, st, sb, sh, st, Hkv * T, T, 1,
                                Hkv * T, T, 1, 0.088f, 0, 2, W, ws, nullptr), GQA_ERR_INVALID_ARG);
 

@@ -140,6 +140,23 @@ def test_workspace_size_and_splits():
         assert gqa.decode_workspace_size(B, Hq, Dv, gqa.decode_splits(*shape)) > 0
 
 
+def test_fp8_split_count():
+    # one resident round, equal pieces: 2 + ceil(4096 / streams) within 8 .. 64,
+    # and never above the bf16 default, so a workspace sized for that fits
+    assert gqa.decode_fp8_splits(64, 32, 8, 8192, 128, 128) == 10
+    for B, Hkv, T in [(1, 8, 8192), (8, 8, 8192), (16, 8, 8192), (64, 8, 8192), (128, 8, 8192), (64, 8, 100),
+                      (4096, 8, 8192), (3, 1, 64)]:
+        s8 = gqa.decode_fp8_splits(B, 32, Hkv, T, 128, 128)
+        sb = gqa.decode_splits(B, 32, Hkv, T, 128, 128, BF16)
+        assert 3 <= s8 <= 64 and s8 <= sb, (B, Hkv, T, s8, sb)
+    with pytest.raises(gqa.GQAError):
+        gqa.decode_fp8_splits(64, 32, 8, 8192, 576, 512)
+    with pytest.raises(gqa.GQAError):
+        gqa.decode_fp8_splits(64, 30, 8, 8192, 128, 128)
+    with pytest.raises(gqa.GQAError):
+        gqa.decode_fp8_splits(64, 32, 8, 0, 128, 128)
+
+
 def test_python_binding_rejects_cpu_tensors():
     import torch
     q = torch.zeros(1, 2, 4, 64)
