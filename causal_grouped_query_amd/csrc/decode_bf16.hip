@@ -605,13 +605,15 @@ __global__ __launch_bounds__(64, 2) void decode_bf16_flat_kernel(DecodeArgs p)
     if (queue && blockIdx.x == 0 && lane == 0)
         __hip_atomic_store(p.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool draws = queue && (blockIdx.x == 0 || (long long)blockIdx.x >= nl);
+    // (the ticket is unsigned: readfirstlane returns an int, and a stale
+    // count of 2^31 or more must not become a negative piece index)
     auto draw = [&]() -> long long {
         unsigned t = 0;
         if (lane == 0) t = __hip_atomic_fetch_add(p.queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        return nl + (long long)__builtin_amdgcn_readfirstlane(t);
+        return nl + (long long)(unsigned)__builtin_amdgcn_readfirstlane((int)t);
     };
-    const long long first = (queue && (long long)blockIdx.x >= nl) ? draw() : (long long)blockIdx.x;
-    for (long long wi = first; wi < N; wi = draws ? draw() : N) {
+    const long long wi0 = (queue && (long long)blockIdx.x >= nl) ? draw() : (long long)blockIdx.x;
+    for (long long wi = wi0; wi < N; wi = draws ? draw() : N) {
         const long long lo = bnd(wi), hi_t = bnd(wi + 1);
         if (lo >= hi_t) continue;
         const int ntl = (int)(hi_t - lo);  // tiles of this piece
@@ -842,13 +844,14 @@ int decode_bf16_flat_workgroups(int Dk)
 
 int decode_bf16_flat_first_round(int Dk)
 {
-    // Per-workgroup clocks show four of these one-wave workgroups resident
-    // per compute unit at a time (1024 on the chip).
-    (void)Dk;
+    // D = 128: per-workgroup clocks show four of these one-wave workgroups
+    // (32 KiB of LDS each) resident per compute unit at a time, 1024 on the
+    // chip.  D = 64 (24 KiB) fits more than four per CU, so the whole grid
+    // is its first round (equal pieces, no queue).
 #ifndef GQA_DEC_FIRST_PER_CU
 #define GQA_DEC_FIRST_PER_CU 4
 #endif
-    return GQA_DEC_FIRST_PER_CU * 256;
+    return Dk == 128 ? GQA_DEC_FIRST_PER_CU * 256 : decode_bf16_flat_workgroups(Dk);
 }
 
 // FP8 flat decode: one resident round of workgroups.  At 16.5 KiB of LDS

@@ -11,13 +11,24 @@ Checked against the fp64 oracle:
     counter left by one call is the next call's stale value);
   * the full-size ragged GQA decode at split counts that change the piece
     sizes of the small last pieces, every output row compared with the
-    equal-chunk schedule (S = 2, no queue) and sampled rows with the oracle.
+    equal-chunk schedule (S = 2, no queue) and sampled rows with the oracle;
+  * seeded random long decodes: group sizes 1 to 48 (two head blocks),
+    1 to 8 KV heads, head dims 128 (queued) and 64 (equal pieces), sliding
+    windows, split counts 3 to 64, empty and one-key sequences, NaN past
+    every sequence's end; sampled rows against the oracle (GQA_QUEUE_CASES
+    cases, default 4, plus seed 7020: head dim 64 with more workgroups
+    resident than the first round, which once let a draw before the
+    counter's reset read a stale count of 2^31 or more as a negative piece
+    index).
 
 Each case first checks, with the kernel's own piece-count rule, that the
 queue is used (more pieces than the first round of 1024 workgroups, and at
 least 48 tiles per first-round workgroup).  Tolerance as for every bf16
 path: max |err| <= 2e-2, mean |err| <= 2e-3.
 """
+import math
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -33,10 +44,16 @@ MAX_PIECES = 2048    # pieces of the balanced schedule at most
 MIN_TILES = 48       # key tiles per first-round workgroup for the queue
 
 
-def _queued(lens, Hkv, Tmax, S, G=4):
+def _queued(lens, Hkv, Tmax, S, G=4, window=0, D=128):
     """Whether the balanced decode uses its queue (host replica of the
-    kernel's rule: T key tiles, n_max in the longest stream, N pieces)."""
-    tiles = [(min(max(int(n), 0), Tmax) + 31) // 32 for n in lens]
+    kernel's rule: T key tiles, n_max in the longest stream, N pieces; head
+    dim 64 fits more than 1024 workgroups at once and takes equal pieces)."""
+    if D != 128:
+        return False
+    eff = [min(max(int(n), 0), Tmax) for n in lens]
+    if window > 0:
+        eff = [min(n, window) for n in eff]
+    tiles = [(n + 31) // 32 for n in eff]
     H = Hkv * ((G + 31) // 32)
     T = sum(tiles) * H
     nmax = max(tiles)
@@ -123,3 +140,50 @@ def test_queue_full_size_split_counts():
         got = out.reshape(-1, w.Dv)[torch.tensor(rows, device="cuda")]
         _check(got, ref, f"full-size GQA decode S={S} (queue {queued}), sampled rows")
     assert _queued(lens.tolist(), w.Hkv, w.Tk, 32) and not _queued(lens.tolist(), w.Hkv, w.Tk, 3)
+
+
+def _random_long_decode(seed):
+    rng = np.random.default_rng(seed)
+    D = int(rng.choice([64, 128]))
+    G = int(rng.choice([1, 2, 3, 4, 8, 16, 48]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    Tmax = int(rng.choice([2048, 4096, 8192, 12000]))
+    window = int(rng.choice([0, 0, 0, 700, 3000]))
+    S = int(rng.integers(3, 65))
+    lo = int(rng.choice([1, Tmax // 4, Tmax // 2]))
+    eff = (lo + Tmax) / 2 if window == 0 else min(window, (lo + Tmax) / 2)
+    tiles_per_seq = Hkv * ((G + 31) // 32) * max(eff / 32, 1)
+    B = int(math.ceil(1.5 * FIRST_ROUND * MIN_TILES / tiles_per_seq))
+    if B * Hkv * Tmax * D * 4 > (3 << 30):  # keep the host cache small: long sequences instead
+        window, lo, Tmax = 0, 4096, 8192
+        B = int(math.ceil(1.5 * FIRST_ROUND * MIN_TILES / (Hkv * ((G + 31) // 32) * 192)))
+    lens = rng.integers(lo, Tmax + 1, size=B)
+    lens[rng.integers(0, B)] = 0
+    lens[rng.integers(0, B)] = 1
+    lens[0] = Tmax
+    return dict(B=B, Hq=G * Hkv, Hkv=Hkv, Tmax=Tmax, D=D, window=window, S=S, lens=[int(x) for x in lens])
+
+
+@pytest.mark.parametrize("seed", sorted({*range(7000, 7000 + int(os.environ.get("GQA_QUEUE_CASES", "4"))), 7020}))
+def test_queue_random_long_decodes(seed):
+    c = _random_long_decode(seed)
+    B, Hq, Hkv, Tmax, D, window, S, lens = (c[k] for k in ("B", "Hq", "Hkv", "Tmax", "D", "window", "S", "lens"))
+    G = Hq // Hkv
+    print(f"seed {seed}: B={B} Hq={Hq} Hkv={Hkv} Tmax={Tmax} D={D} window={window} S={S}", flush=True)
+    assert _queued(lens, Hkv, Tmax, S, G=G, window=window, D=D) == (D == 128)
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn(B, Hq, 1, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, Hkv, Tmax, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, Tmax, D, generator=g).to(torch.bfloat16)
+    for b, n in enumerate(lens):
+        k[b, :, n:] = float("nan")
+        v[b, :, n:] = float("nan")
+    lens_t = torch.tensor(lens, dtype=torch.int32)
+    out = gqa.decode(q.cuda(), k.cuda(), v.cuda(), lens_t.cuda(), num_splits=S, window=window)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed + 1)
+    rows = sorted({0, B * Hq - 1, *(b * Hq for b in range(B) if lens[b] <= 1),
+                   *rng.integers(0, B * Hq, 48).tolist()})
+    ref = O.attention(q, k, v, 1.0 / np.sqrt(D), True, kv_lens=lens, rows=rows, window=window)
+    got = out.reshape(-1, D)[torch.tensor(rows, device="cuda")]
+    _check(got, ref, f"random long decode seed {seed}")
