@@ -165,6 +165,12 @@ struct PlaneTile {
 // instructions have no register results; they only read their address
 // operands at issue.  M0 carries the LDS base (1 wait state before the copy).
 //
+// NT = true marks the copy non-temporal (the `nt` cache policy): for data a
+// kernel reads once per call, such as a decode's KV stream, so that those
+// lines do not push other data (the dirty output lines of a preceding
+// kernel, say) out of the caches.  Data that other workgroups read again,
+// like the forward kernel's K/V tiles, keeps the default policy.
+//
 // Every one of these statements writes M0 and names it in its clobber list.
 // M0 is a reserved register of the AMDGPU backend (the compiler sets it
 // right before each of its own uses and never keeps a value in it); clang
@@ -177,54 +183,84 @@ __device__ __forceinline__ unsigned lds_u32(const void *lds_ptr)
     return __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)(GQA_LDS const void *)lds_ptr);
 }
 
+template <bool NT = false>
 __device__ __forceinline__ void g2lds16(const void *gptr, void *lds_wave_base)
 {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
-                 "s"(lds_u32(lds_wave_base))
-                 : "memory", "m0");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(gptr),
+                     "s"(lds_u32(lds_wave_base))
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+                     "s"(lds_u32(lds_wave_base))
+                     : "memory", "m0");
 }
 
 // 4 bytes per lane (global_load_lds_dword): lane l's word lands at
 // lds_wave_base + 4*l.
+template <bool NT = false>
 __device__ __forceinline__ void g2lds4(const void *gptr, void *lds_wave_base)
 {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr),
-                 "s"(lds_u32(lds_wave_base))
-                 : "memory", "m0");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off nt" ::"v"(gptr),
+                     "s"(lds_u32(lds_wave_base))
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(gptr),
+                     "s"(lds_u32(lds_wave_base))
+                     : "memory", "m0");
 }
 
 // Same copy from a workgroup-uniform base plus a per-lane unsigned byte
 // offset (scalar-base form: no per-lane 64-bit address arithmetic).
+template <bool NT = false>
 __device__ __forceinline__ void g2lds16(const void *uniform_base, unsigned byte_off, void *lds_wave_base)
 {
     const unsigned long long a = (unsigned long long)uniform_base;
     const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
     const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
     const unsigned long long base = ((unsigned long long)hi << 32) | lo;
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(byte_off), "s"(base),
-                 "s"(lds_u32(lds_wave_base))
-                 : "memory", "m0");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(byte_off), "s"(base),
+                     "s"(lds_u32(lds_wave_base))
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(byte_off), "s"(base),
+                     "s"(lds_u32(lds_wave_base))
+                     : "memory", "m0");
 }
 
 // Same copy with the LDS destination given as a workgroup-uniform LDS byte
 // address (no generic-pointer round trip, whose null check costs scalar
 // instructions per copy).
+template <bool NT = false>
 __device__ __forceinline__ void g2lds16_at(const void *uniform_base, unsigned byte_off, unsigned lds_addr)
 {
     const unsigned long long a = (unsigned long long)uniform_base;
     const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
     const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
     const unsigned long long base = ((unsigned long long)hi << 32) | lo;
-    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(byte_off), "s"(base),
-                 "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-                 : "memory", "m0");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(byte_off), "s"(base),
+                     "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(byte_off), "s"(base),
+                     "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                     : "memory", "m0");
 }
 
+template <bool NT = false>
 __device__ __forceinline__ void g2lds16_at(const void *gptr, unsigned lds_addr)
 {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
-                 "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-                 : "memory", "m0");
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(gptr),
+                     "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr),
+                     "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+                     : "memory", "m0");
 }
 
 #pragma clang diagnostic pop

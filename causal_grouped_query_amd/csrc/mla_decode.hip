@@ -50,6 +50,13 @@ constexpr int kDV = 512;     // value width (the latent)
 #endif
 constexpr int kNW = GQA_MLA_NW;  // waves per workgroup
 constexpr int kNT = 64 * kNW;
+#ifndef GQA_MLA_NT
+#define GQA_MLA_NT 0
+#endif
+// Non-temporal copies (device_common.h), off: unlike the GQA decode's
+// stream they made these kernels slower (absorbed MLA ~+4 us, top-k at
+// batch 16 / 64 +2.4 / +4.5 us on one box)
+constexpr bool kCopyNT = GQA_MLA_NT;
 constexpr int kHW = 16;      // heads per wave
 constexpr int kStagesDense = GQA_MLA_STAGES;
 constexpr int kStagesSparse = 3;  // the staged index list takes the rest of the LDS
@@ -169,7 +176,7 @@ __global__ __launch_bounds__(kNT, kBlocksPerCu) void mla_decode_kernel(DecodeArg
         if (len == 0) ntiles = 0;
         const int *il = p.idx + (size_t)b * p.topk;
         for (int e0 = w * 64; e0 < ntiles * kTK; e0 += kNT)
-            g2lds4(il + min(kbeg + e0 + lane, p.topk - 1), &sidx[e0]);
+            g2lds4<kCopyNT>(il + min(kbeg + e0 + lane, p.topk - 1), &sidx[e0]);
         for (int i = tid; i < 2 * kMaxChunk; i += kNT) htab[i] = 0xffffffffu;
         wait_vmem();
         lds_barrier();  // the slice and the empty table are visible to every wave
@@ -206,7 +213,7 @@ __global__ __launch_bounds__(kNT, kBlocksPerCu) void mla_decode_kernel(DecodeArg
             for (int jj = 0; jj < kCopiesMax; ++jj) {
                 const int j = w + kNW * jj;
                 if (j < NCOPY)
-                    g2lds16_at(kb + (size_t)(k0 + 16 * (j & 1)) * p.k_st + 32 * (j >> 1), lane_off,
+                    g2lds16_at<kCopyNT>(kb + (size_t)(k0 + 16 * (j & 1)) * p.k_st + 32 * (j >> 1), lane_off,
                                dst + (unsigned)(jj * kNW * 64 * 16));
             }
         } else if (off32) {
@@ -225,7 +232,7 @@ __global__ __launch_bounds__(kNT, kBlocksPerCu) void mla_decode_kernel(DecodeArg
                 } else {
                     off = lane_off + (unsigned)(min(row, kend - 1 - k0) - lrow) * pitch;
                 }
-                g2lds16_at(base + 32 * (j >> 1), off, dst + (unsigned)(jj * kNW * 64 * 16));
+                g2lds16_at<kCopyNT>(base + 32 * (j >> 1), off, dst + (unsigned)(jj * kNW * 64 * 16));
             }
         } else if constexpr (SPARSE) {
             unsigned lc = lane_chunk16();
@@ -236,7 +243,7 @@ __global__ __launch_bounds__(kNT, kBlocksPerCu) void mla_decode_kernel(DecodeArg
                 if (j >= NCOPY) continue;
                 const int row = 16 * (j & 1) + lrow;
                 const int pos = min(max(sidx[k0 - kbeg + row], 0), len - 1);
-                g2lds16_at((const char *)(kb + (size_t)pos * p.k_st + 32 * (j >> 1)) + lc,
+                g2lds16_at<kCopyNT>((const char *)(kb + (size_t)pos * p.k_st + 32 * (j >> 1)) + lc,
                            dst + (unsigned)(jj * kNW * 64 * 16));
             }
         }
