@@ -54,8 +54,9 @@ constexpr int kNT = 64 * kNW;
 #define GQA_MLA_NT 0
 #endif
 // Non-temporal copies (device_common.h), off: unlike the GQA decode's
-// stream they made these kernels slower (absorbed MLA ~+4 us, top-k at
-// batch 16 / 64 +2.4 / +4.5 us on one box)
+// stream they gained nothing here (absorbed MLA 187.0 vs 186.6 us) and
+// slowed the top-k decode (batch 16 / 64: 47.1 vs 44.1, 75.4 vs 73.0 us;
+// decode + combine, one box)
 constexpr bool kCopyNT = GQA_MLA_NT;
 constexpr int kHW = 16;      // heads per wave
 constexpr int kStagesDense = GQA_MLA_STAGES;
