@@ -324,6 +324,34 @@ def test_mla_decode_empty_and_short_sequences():
     _check(out[1:], ref, "bf16", "mla short / empty")
 
 
+def _forward_loops(B, Hq, Hkv, T, rows_per_wave=32, waves=8, resident=256):
+    """Host replica of the launcher's rule for the looping forward (dense,
+    D = 128): one resident round of workgroups walks the items when every
+    XCD's share is whole units with an even number of items per workgroup."""
+    G = Hq // Hkv
+    gt = 1
+    while gt * 2 <= waves and G % (gt * 2) == 0 and waves % (gt * 2) == 0:
+        gt *= 2
+    pt = rows_per_wave * (waves // gt)
+    n_qt = -(-T // pt)
+    items = B * Hkv * (G // gt) * n_qt
+    per, nwx = items // 8, resident // 8
+    return (items > resident and items % 8 == 0 and per % n_qt == 0 and n_qt % 2 == 0
+            and per % nwx == 0 and (per // nwx) % 2 == 0)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("B,T", [(8, 512), (4, 1024)])
+def test_forward_looping_round(B, T, causal):
+    """Shapes on which one resident round of workgroups loops over two items
+    each (snake order within each XCD's range), compared in full."""
+    Hq, Hkv, D = 32, 8, 128
+    assert _forward_loops(B, Hq, Hkv, T)
+    q, k, v = _rand((B, Hq, T, D), 60 + T, "bf16"), _rand((B, Hkv, T, D), 61 + T, "bf16"), _rand((B, Hkv, T, D), 62 + T, "bf16")
+    out = gqa.attention(q.cuda(), k.cuda(), v.cuda(), causal=causal)
+    _check(out, O.attention(q, k, v, 1.0 / math.sqrt(D), causal), "bf16", f"looping forward B={B} T={T} causal={causal}")
+
+
 # ------------------------------------------------------------------ headline workloads, full size
 
 def _sample_rows(B, Hq, Tq, n, seed, extra_pos=()):
