@@ -342,10 +342,14 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCu) void fwd_bf16_kernel(FwdArg
                 for (int t = 0; t < kNT; ++t)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) sc[cb][t][e] = 0.f;
+            // head-dim steps outermost: consecutive MFMAs share their Q^T
+            // operand and alternate between the 32-key blocks' accumulators
+            // (each accumulator still sums its steps in order, so the scores
+            // are the same bits as with the key blocks outermost)
 #pragma unroll
-            for (int t = 0; t < kNT; ++t) {
+            for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
+                for (int t = 0; t < kNT; ++t) {
                     const int off_ = ((ks & 1) ? kb_odd : kb_even) + (ks >> 1) * Tile::PLANE_BYTES + t * 32 * 64;
                     const u32x4 a = *(const u32x4 *)(ks_ + off_);
 #pragma unroll
