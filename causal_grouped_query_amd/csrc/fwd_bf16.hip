@@ -65,7 +65,7 @@ namespace {
 #define GQA_FWD_STAGES 4  // K/V ring depth
 #endif
 #ifndef GQA_FWD_PREFETCH
-#define GQA_FWD_PREFETCH 6  // LDS operand reads kept in flight ahead of the MFMAs (0: compiler's choice)
+#define GQA_FWD_PREFETCH 4  // LDS operand reads kept in flight ahead of the MFMAs (0: compiler's choice)
 #endif
 // sum of one lane's weights in a tile past which its reference max moves
 constexpr float kSumCap = 65536.0f;
